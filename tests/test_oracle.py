@@ -1,0 +1,380 @@
+"""Pins of the FP64 oracle to things other than itself (CPU only).
+
+Each test checks the oracle against a library routine, a closed form, an invariant of the
+softmax, or brute force on tiny inputs, chosen so that a plausible slip in the oracle (a
+dropped term, a wrong sign, base or index, a transposed operand) fails at least one of them.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_mla_attention_amd import inputs
+
+LN2 = math.log(2.0)
+
+
+# ---------------------------------------------------------------------------
+# number formats (pinned to torch's casts: a library routine)
+# ---------------------------------------------------------------------------
+
+def test_e4m3_decode_all_codes_match_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    ours = np.array([oracle.e4m3_value(c) for c in codes])
+    nan = np.isnan(ref)
+    assert np.array_equal(nan, np.isnan(ours))
+    assert set(np.flatnonzero(nan)) == {0x7F, 0xFF}
+    assert np.array_equal(ref[~nan], ours[~nan])
+    assert ours[0x7E] == 448.0 and ours[0x01] == 2.0 ** -9
+
+
+def test_e4m3_encode_matches_torch_rne_and_saturates():
+    codes = np.arange(0, 0x7F)
+    vals = np.array([oracle.e4m3_value(c) for c in codes])
+    mids = (vals[:-1] + vals[1:]) / 2  # exact ties: round half to even
+    rng = np.random.default_rng(0)
+    xs = np.concatenate([vals, mids, mids * (1 + 1e-6), mids * (1 - 1e-6),
+                         rng.uniform(0, 480, 4000), rng.uniform(0, 2.0 ** -6, 2000),
+                         [448.0, 449.0, 463.9, 464.0, 500.0, 1e6]])
+    xs = np.concatenate([xs, -xs]).astype(np.float32).astype(np.float64)
+    ours = np.array([oracle.e4m3_encode(x) for x in xs], dtype=np.uint8)
+    ref = torch.from_numpy(xs.astype(np.float32)).clamp(-448, 448).to(torch.float8_e4m3fn)
+    ref = ref.view(torch.uint8).numpy()
+    # torch keeps the sign of a negative value that rounds to zero, as does the oracle
+    assert np.array_equal(ours, ref), xs[ours != ref][:10]
+    for c in codes:  # every finite code is a fixed point
+        assert oracle.e4m3_encode(oracle.e4m3_value(c)) == c
+
+
+def test_bf16_decode_matches_torch():
+    rng = np.random.default_rng(1)
+    bits = rng.integers(0, 1 << 16, size=5000, dtype=np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    ours = np.array([oracle.bf16_value(b) for b in bits])
+    nan = np.isnan(ref)
+    assert np.array_equal(nan, np.isnan(ours))
+    assert np.array_equal(ref[~nan], ours[~nan])
+
+
+# ---------------------------------------------------------------------------
+# exact mode against dense float64 attention (brute force, a library routine)
+# ---------------------------------------------------------------------------
+
+def _e4m3_f64(b):
+    return torch.from_numpy(np.ascontiguousarray(b)).view(torch.float8_e4m3fn).to(torch.float64)
+
+
+def _dense_reference(p, lse_log2=False):
+    """Materialise each token's active rows and run torch's float64 SDPA on them.  A sink is an
+    extra key with k = 0, v = 0 and an additive score bias equal to the sink."""
+    T, H, _ = p["q"].shape
+    W = p["indices"].shape[1]
+    out = np.zeros((T, H, 512))
+    lse = np.full((T, H), -np.inf)
+    q = _e4m3_f64(p["q"])[..., :p["qk_dim"]]
+    for t in range(T):
+        n = int(np.clip(p["lens"][t], 0, W))
+        rows = []
+        for c in range(n):
+            i = int(p["indices"][t, c])
+            if i < 0:
+                continue
+            pool = p["kv_b"] if (p["kv_b"] is not None and c >= p["split_col"]) else p["kv_a"]
+            rows.append(pool[i])
+        if not rows:
+            continue
+        kv = _e4m3_f64(np.stack(rows))
+        k = kv[:, :p["qk_dim"]]
+        v = kv[:, :512]
+        bias = torch.zeros((H, k.shape[0]), dtype=torch.float64)
+        if p["sinks"] is not None:
+            k = torch.cat([k, torch.zeros((1, k.shape[1]), dtype=torch.float64)])
+            v = torch.cat([v, torch.zeros((1, 512), dtype=torch.float64)])
+            sink = torch.from_numpy(p["sinks"].astype(np.float64))[:, None]
+            bias = torch.cat([bias, sink], dim=1)
+        qt = q[t][None]  # [1, H, d]
+        o = torch.nn.functional.scaled_dot_product_attention(
+            qt, k[None].expand(1, -1, -1), v[None].expand(1, -1, -1), attn_mask=bias[None],
+            scale=p["bmm1"])
+        out[t] = (o[0] * p["bmm2"]).numpy()
+        scores = p["bmm1"] * (q[t] @ k.T) + bias
+        lse[t] = torch.logsumexp(scores, dim=1).numpy()
+    if lse_log2:
+        lse = lse / LN2
+    return out.reshape(T * H, 512), lse.reshape(T * H)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(T=1, H=16, W=32, row_bytes=576),
+    dict(T=2, H=16, W=24, row_bytes=576, lens=[24, 17]),
+    dict(T=2, H=16, W=20, row_bytes=512, sinks=True),
+    dict(T=2, H=16, W=30, row_bytes=512, two_pools=True, split_col=7, sinks=True, rows_b=300),
+    dict(T=1, H=16, W=16, row_bytes=576, kv_scale_to_amax=True),
+    dict(T=2, H=16, W=32, row_bytes=576, qk_dim=512),
+])
+def test_exact_matches_dense_attention(kw):
+    kw = dict(kw)
+    T, H, W = kw.pop("T"), kw.pop("H"), kw.pop("W")
+    p = inputs.random_problem(11 + W, T, H, W, pool_rows=256, **kw)
+    for log2 in (False, True):
+        out, lse = oracle.decode_exact(p, lse_log2=log2)
+        ref_out, ref_lse = _dense_reference(p, lse_log2=log2)
+        np.testing.assert_allclose(out, ref_out, rtol=1e-9, atol=1e-12)
+        np.testing.assert_allclose(lse, ref_lse, rtol=1e-12, atol=1e-12)
+
+
+def test_exact_units_subset_equals_full():
+    p = inputs.random_problem(5, 3, 16, 40, pool_rows=300, neg_frac=0.2, lens=[40, 33, 0])
+    full, lse = oracle.decode_exact(p)
+    units = [(2, 5), (0, 0), (1, 15), (0, 9)]
+    sub, sub_lse = oracle.decode_exact(p, units=units)
+    for k, (t, h) in enumerate(units):
+        assert np.array_equal(sub[k], full[t * 16 + h])
+        assert sub_lse[k] == lse[t * 16 + h] or (np.isinf(lse[t * 16 + h]) and np.isinf(sub_lse[k]))
+
+
+# ---------------------------------------------------------------------------
+# softmax invariants and closed forms
+# ---------------------------------------------------------------------------
+
+def test_permuting_columns_and_adding_unused_columns_changes_nothing():
+    p = inputs.random_problem(7, 2, 16, 48, pool_rows=400, neg_frac=0.25, lens=[48, 31],
+                              sinks=True)
+    out, lse = oracle.decode_exact(p)
+    rng = np.random.default_rng(3)
+    q = dict(p)
+    idx = p["indices"].copy()
+    for t in range(2):
+        n = int(p["lens"][t])
+        idx[t, :n] = idx[t, rng.permutation(n)]
+    q["indices"] = idx
+    out2, lse2 = oracle.decode_exact(q)
+    np.testing.assert_allclose(out2, out, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(lse2, lse, rtol=1e-13)
+    # widen W with -1 columns inside the count
+    r = dict(p)
+    wide = np.full((2, 64), -1, np.int32)
+    wide[:, :48] = p["indices"]
+    for t in range(2):
+        n = int(p["lens"][t])
+        wide[t, :n + 16] = np.concatenate([p["indices"][t, :n], np.full(16, -1, np.int32)])
+    r["indices"], r["lens"] = wide, p["lens"] + 16
+    out3, lse3 = oracle.decode_exact(r)
+    np.testing.assert_allclose(out3, out, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(lse3, lse, rtol=1e-13)
+
+
+def test_duplicating_every_column_adds_ln2_to_lse():
+    p = inputs.random_problem(8, 2, 16, 24, pool_rows=300, neg_frac=0.1)
+    out, lse = oracle.decode_exact(p)
+    d = dict(p)
+    d["indices"] = np.concatenate([p["indices"], p["indices"]], axis=1)
+    d["lens"] = p["lens"] * 2
+    d["split_col"] = 48
+    out2, lse2 = oracle.decode_exact(d)
+    np.testing.assert_allclose(out2, out, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(lse2, lse + LN2, rtol=1e-13)
+
+
+def test_single_active_column_returns_its_row():
+    p = inputs.random_problem(9, 1, 16, 8, pool_rows=64, lens=1, row_bytes=576)
+    out, lse = oracle.decode_exact(p)
+    row = _e4m3_f64(p["kv_a"][p["indices"][0, 0]]).numpy()
+    for h in range(16):
+        assert np.array_equal(out[h], p["bmm2"] * row[:512])
+    s = p["bmm1"] * (_e4m3_f64(p["q"][0]).numpy() @ row)
+    np.testing.assert_allclose(lse, s, rtol=1e-13, atol=1e-13)
+
+
+def test_equal_scores_give_the_mean_row_and_weights_sum_to_one():
+    p = inputs.random_problem(10, 1, 16, 20, pool_rows=100, sinks=True)
+    p["q"] = np.zeros_like(p["q"])  # every score 0
+    out, lse = oracle.decode_exact(p)
+    rows = _e4m3_f64(p["kv_a"][p["indices"][0]]).numpy()[:, :512]
+    sinks = p["sinks"].astype(np.float64)
+    for h in range(16):
+        z = 20.0 + math.exp(sinks[h])
+        np.testing.assert_allclose(out[h], p["bmm2"] * rows.sum(0) / z, rtol=1e-12, atol=1e-15)
+        np.testing.assert_allclose(lse[h], math.log(z), rtol=1e-14)
+    # all-ones V: out = bmm2 * (1 - sink weight) with the sink weight e^{sink - lse}
+    p2 = inputs.random_problem(12, 2, 16, 20, pool_rows=100, sinks=True, lens=[20, 9])
+    p2["kv_a"] = p2["kv_a"].copy()
+    p2["kv_a"][:, :512] = 0x38  # E4M3 1.0
+    out2, lse2 = oracle.decode_exact(p2)
+    sink_w = np.exp(np.tile(p2["sinks"].astype(np.float64), 2) - lse2)
+    np.testing.assert_allclose(out2, (p2["bmm2"] * (1 - sink_w))[:, None] * np.ones((1, 512)),
+                               rtol=1e-12)
+
+
+@pytest.mark.parametrize("case", ["lens0", "all_neg", "lens_negative"])
+def test_zero_count_rule_is_exact(case):
+    p = inputs.random_problem(13, 3, 16, 16, pool_rows=64, sinks=True)
+    if case == "lens0":
+        p["lens"] = np.array([16, 0, 16], np.int32)
+    elif case == "all_neg":
+        p["indices"] = p["indices"].copy()
+        p["indices"][1] = -1
+    else:
+        p["lens"] = np.array([16, -5, 16], np.int32)
+    out, lse = oracle.decode_exact(p)
+    assert np.array_equal(out[16:32], np.zeros((16, 512)))
+    assert not np.signbit(out[16:32]).any()
+    assert np.all(lse[16:32] == -np.inf)
+    assert np.all(np.isfinite(lse[:16])) and np.all(np.isfinite(lse[32:]))
+    om, lm = oracle.decode_mimic(p, splits=2, chunk=8, terms=2)
+    assert np.array_equal(om[16:32], np.zeros((16, 512))) and np.all(lm[16:32] == -np.inf)
+
+
+def test_out_of_range_and_nan_inputs_are_rejected():
+    p = inputs.random_problem(14, 1, 16, 8, pool_rows=32, poison=False)
+    bad = dict(p)
+    bad["indices"] = p["indices"].copy()
+    bad["indices"][0, 3] = 32
+    with pytest.raises(oracle.OracleError):
+        oracle.decode_exact(bad)
+    nan = dict(p)
+    nan["kv_a"] = p["kv_a"].copy()
+    nan["kv_a"][p["indices"][0, 2], 5] = 0x7F
+    with pytest.raises(oracle.OracleError):
+        oracle.decode_exact(nan)
+    # an index past lens, or a poisoned row that is never active, is never read
+    ok = dict(p)
+    ok["indices"] = p["indices"].copy()
+    ok["lens"] = np.array([5], np.int32)
+    ok["indices"][0, 6] = 10 ** 6
+    oracle.decode_exact(ok)
+
+
+# ---------------------------------------------------------------------------
+# mimic mode
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("splits,chunk", [(1, 64), (3, 8), (4, 5), (7, 128)])
+def test_mimic_without_quantization_is_exact(splits, chunk):
+    p = inputs.random_problem(15, 2, 16, 40, pool_rows=300, neg_frac=0.2, lens=[40, 23],
+                              sinks=True)
+    out, lse = oracle.decode_exact(p)
+    om, lm = oracle.decode_mimic(p, splits=splits, chunk=chunk, quantize=False)
+    np.testing.assert_allclose(om, out, rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(lm, lse, rtol=1e-12)
+
+
+def test_mimic_single_chunk_matches_recipe_with_torch_quantizer():
+    """One split, one chunk: P = 2^(s2 - max + log2 448) quantized by torch's E4M3 cast."""
+    p = inputs.random_problem(16, 1, 16, 32, pool_rows=200)
+    rows = _e4m3_f64(p["kv_a"][p["indices"][0]]).numpy()
+    q = _e4m3_f64(p["q"][0]).numpy()
+    s2 = p["bmm1"] * (q @ rows[:, :576].T) / LN2  # [H, n]
+    m = s2.max(axis=1, keepdims=True)
+    pv = np.exp2(s2 - m + math.log2(448.0))
+    for terms in (1, 2):
+        hi = torch.from_numpy(pv).clamp(-448, 448).to(torch.float8_e4m3fn).to(torch.float64)
+        phat = hi.numpy()
+        if terms == 2:
+            res = torch.from_numpy(16 * (pv - phat)).clamp(-448, 448).to(torch.float8_e4m3fn)
+            phat = phat + res.to(torch.float64).numpy() / 16
+        ref = p["bmm2"] * (phat @ rows[:, :512]) / pv.sum(1, keepdims=True)
+        ref_lse = (m[:, 0] - math.log2(448.0) + np.log2(pv.sum(1))) * LN2
+        om, lm = oracle.decode_mimic(p, splits=1, chunk=32, terms=terms)
+        np.testing.assert_allclose(om, ref, rtol=1e-10, atol=1e-13)
+        np.testing.assert_allclose(lm, ref_lse, rtol=1e-12)
+
+
+def test_mimic_equal_scores_quantize_exactly():
+    """Equal scores put every P at the anchor 448, which E4M3 holds exactly."""
+    p = inputs.random_problem(17, 1, 16, 40, pool_rows=100)
+    p["q"] = np.zeros_like(p["q"])
+    out, lse = oracle.decode_exact(p)
+    om, lm = oracle.decode_mimic(p, splits=1, chunk=64, terms=1)
+    np.testing.assert_allclose(om, out, rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(lm, lse, rtol=1e-13)
+
+
+def test_mimic_two_terms_is_much_closer_than_one():
+    p = inputs.random_problem(18, 2, 16, 128, pool_rows=600)
+    out, _ = oracle.decode_exact(p)
+    e1 = np.linalg.norm(oracle.decode_mimic(p, 2, 64, terms=1)[0] - out) / np.linalg.norm(out)
+    e2 = np.linalg.norm(oracle.decode_mimic(p, 2, 64, terms=2)[0] - out) / np.linalg.norm(out)
+    assert 2e-3 < e1 < 5e-2  # E4M3's 3 mantissa bits: percent-level per P
+    assert e2 < e1 / 16
+
+
+def test_mimic_lse_ignores_p_quantization():
+    """The running sums use the unquantized P, so the LSE matches exact mode closely."""
+    p = inputs.random_problem(19, 2, 16, 64, pool_rows=300, sinks=True, neg_frac=0.1)
+    _, lse = oracle.decode_exact(p)
+    _, lm = oracle.decode_mimic(p, 3, 16, terms=1)
+    np.testing.assert_allclose(lm, lse, rtol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# lse_merge
+# ---------------------------------------------------------------------------
+
+def _bf16_to_f64(bits):
+    return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+
+
+def test_merge_single_source_is_identity():
+    m = inputs.random_merge(20, 1, 3, 8, 64, empty_frac=0.3)
+    out, lse = oracle.lse_merge(m["partials"], m["lse"])
+    valid = np.isfinite(m["lse"][0])
+    np.testing.assert_array_equal(out[valid], _bf16_to_f64(m["partials"][0])[valid])
+    np.testing.assert_allclose(lse[valid], m["lse"][0][valid].astype(np.float64) * LN2, rtol=1e-15)
+    assert np.all(out[~valid] == 0) and np.all(lse[~valid] == -np.inf)
+
+
+def test_merge_closed_form_two_sources():
+    x = inputs.bf16_bits(np.array([[[[1.0, 2.0]]], [[[3.0, -4.0]]]], np.float32))
+    lse = np.array([[[2.0]], [[3.0]]], np.float32)  # base 2: weights 1/3 and 2/3
+    out, l = oracle.lse_merge(x, lse, lse_log2=True)
+    np.testing.assert_allclose(out[0, 0], [1 / 3 + 2.0, 2 / 3 - 8 / 3], rtol=1e-15)
+    np.testing.assert_allclose(l[0, 0], 3.0 + math.log2(1.5), rtol=1e-15)
+
+
+def test_merge_empty_encodings_and_nan_partials_do_not_propagate():
+    m = inputs.random_merge(21, 5, 4, 8, 32, empty_frac=0.4, nan_lse=True)
+    out, lse = oracle.lse_merge(m["partials"], m["lse"])
+    assert np.all(np.isfinite(out))
+    none = ~np.isfinite(m["lse"]).any(axis=0)
+    assert none[0, 0]
+    assert np.all(out[none] == 0) and np.all(lse[none] == -np.inf)
+    assert np.all(np.isfinite(lse[~none]))
+
+
+def test_merge_recovers_full_decode_from_two_column_ranges():
+    """Decoding columns [0,k) and [k,n) separately (base-2 LSE), rounding to BF16, and merging
+    gives the full decode within BF16 rounding; this also cross-checks exact mode against the
+    merge."""
+    p = inputs.random_problem(22, 2, 16, 64, pool_rows=400, neg_frac=0.1)
+    full, full_lse = oracle.decode_exact(p)
+    parts, lses = [], []
+    for lo, hi in ((0, 25), (25, 64)):
+        q = dict(p)
+        idx = np.full_like(p["indices"], -1)
+        idx[:, lo:hi] = p["indices"][:, lo:hi]
+        q["indices"] = idx
+        o, l = oracle.decode_exact(q, lse_log2=True)
+        parts.append(inputs.bf16_bits(o.reshape(2, 16, 512).astype(np.float32)))
+        lses.append(l.reshape(2, 16).astype(np.float32))
+    out, lse = oracle.lse_merge(np.stack(parts), np.stack(lses))
+    err = np.linalg.norm(out.reshape(-1, 512) - full) / np.linalg.norm(full)
+    assert err < 4e-3
+    np.testing.assert_allclose(lse.reshape(-1), full_lse, rtol=1e-6)
+
+
+def test_dominant_sink_does_not_overflow():
+    """A sink far above every score: the stabiliser m must include the sink, the output goes
+    to ~0 and the LSE to the sink (closed form ln(e^sink + sum e^s) ~ sink)."""
+    p = inputs.random_problem(23, 1, 16, 16, pool_rows=64, sinks=True)
+    p["sinks"] = np.full(16, 800.0, np.float32)
+    out, lse = oracle.decode_exact(p)
+    assert np.all(np.isfinite(lse)) and np.all(np.isfinite(out))
+    np.testing.assert_allclose(lse, 800.0, rtol=1e-12)
+    assert np.abs(out).max() < 1e-300
+    om, lm = oracle.decode_mimic(p, 2, 8, terms=1)
+    np.testing.assert_allclose(lm, 800.0, rtol=1e-12)
+    assert np.all(np.isfinite(om)) and np.abs(om).max() < 1e-300
