@@ -1,0 +1,149 @@
+/*
+ * smla.h -- sparse MLA decode and the split-KV LSE merge on AMD Instinct MI355X (gfx950).
+ *
+ * C ABI.  Every pointer argument named as device memory must be a device pointer that the
+ * caller allocated and owns; the library never allocates, frees or synchronizes.  Calls are
+ * asynchronous and ordered on the given HIP stream (0 = the null stream).  Arguments are
+ * checked on the host before anything is launched; on an error nothing is written.
+ *
+ * Method (cited by page title and section; the pages are API documentation pages of vLLM):
+ *   sparse_mla_cute page, "What this module computes": each query token t and head h attends
+ *     over its own set of FP8 (E4M3) KV rows, the active columns c of the token
+ *     (c < lens[t] and indices[t, c] >= 0):
+ *       s_c = bmm1 * q[t,h] . kv[c];  out[t,h] = bmm2 * sum_c e^{s_c-m} v_c / (sum_c e^{s_c-m}
+ *       + e^{sink_h - m}), m the maximum of the scores and the sink, V the first 512 bytes of
+ *       the same row; columns below split_col index pool A, the others pool B; a token with no
+ *       active column gets zeros.
+ *   attn_sparse page (Kimi K3.1 SparseDcpDecode), module docstring: 576-byte rows (512 latent
+ *     + 64 rope bytes) of a per-tensor-scaled FP8 cache; softmax in base 2 with P quantized to
+ *     E4M3 at 448 of the running row maximum (RN, satfinite), FP32 sums of the unquantized P,
+ *     FP32 accumulation, one BF16 rounding of the output; rows of count 0 give zeros and
+ *     LSE -inf; the split partials are merged in FP32 (merge method: weights exp2(max_c - max),
+ *     BF16(sum * k_scale / total), LSE = max + log2(total / 448), natural log in the
+ *     non-push output).
+ *   dcp page, DcpValue.merge: LSE-weighted merge of D split partials in FP32, weights
+ *     exp2(lse - top) / sum, empty sources weighted 0, one BF16 rounding.
+ */
+#ifndef SMLA_H
+#define SMLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+typedef int32_t smla_status;
+#define SMLA_OK 0
+#define SMLA_EINVAL 1        /* a null pointer, bad size, misalignment or bad flag */
+#define SMLA_EUNSUPPORTED 2  /* a shape this build has no kernel for (see each entry point) */
+#define SMLA_EWORKSPACE 3    /* the workspace is missing or smaller than required */
+#define SMLA_EHIP 4          /* a HIP runtime error (device query or kernel launch) */
+
+/* Flags. */
+#define SMLA_LSE_LOG2 0x1u   /* LSE outputs in base 2 (default: natural log) */
+#define SMLA_P_ONE_TERM 0x2u /* sparse_mla_decode: P as one E4M3 term, the attn_sparse page's
+                                recipe as printed.  Default: two E4M3 terms, P = hi + lo/16 with
+                                hi = E4M3(P) and lo = E4M3(16 (P - hi)), which keeps the E4M3
+                                quantization at the 448 anchor but reaches FP32-level accuracy
+                                (relative output error ~1e-3 instead of ~2e-2). */
+
+/* The launch decomposition of one sparse_mla_decode call.  A workgroup takes one token, a
+ * group of `tiles` 16-head tiles and one of `splits` contiguous ranges of the token's clamped
+ * count (range s = [min(n, s*per), +min(n - first, per)), per = ceil(n / splits), as the
+ * attn_sparse page's key split); the ranges run in chunks of `chunk` columns and are merged in
+ * FP32 when splits > 1. */
+typedef struct smla_plan {
+    int32_t splits; /* >= 1 */
+    int32_t tiles;  /* 16-head tiles per workgroup: 1, 2, 4 or 8, dividing H / 16 */
+    int32_t chunk;  /* columns per gathered chunk (128 in this build; output only) */
+    int32_t reserved;
+} smla_plan;
+
+/* The plan sparse_mla_decode uses for these sizes when it is given none: the split count and
+ * tiles per workgroup fill the device's compute units (queried once per device).  Returns
+ * SMLA_EINVAL for bad sizes, SMLA_EHIP if the device cannot be queried. */
+smla_status smla_decode_plan(int32_t T, int32_t H, int32_t W, int32_t row_bytes, uint32_t flags,
+                             smla_plan *plan);
+
+/* Workspace bytes sparse_mla_decode needs under `plan` (0 when plan->splits == 1): FP32
+ * partials [T, H, splits, 512] plus (max, sum) pairs [T, H, splits, 2].  0 for a bad plan. */
+size_t smla_decode_workspace_size(const smla_plan *plan, int32_t T, int32_t H);
+
+/*
+ * sparse_mla_decode -- sparse MLA decode of T tokens (formula above).
+ *
+ *   q            device, E4M3 bytes; head h of token t at q + t*q_stride_t + h*q_stride_h,
+ *                qk_dim bytes.  16-byte aligned; both strides multiples of 16.
+ *   kv_a, rows_a device, pool A: rows_a rows of row_bytes E4M3 bytes, 16-byte aligned.
+ *   kv_b, rows_b device, pool B (may be NULL: then every column uses pool A and split_col is
+ *                ignored).  Columns c >= split_col use pool B.
+ *   row_bytes    576 (512 latent + 64 rope) or 512.  V is bytes [0, 512) of a row.
+ *   qk_dim       576 or 512, <= row_bytes: the bytes of q and of each row in the score.
+ *   indices      device int32 [T, W] row-major: storage rows, negative = unused column.
+ *                Every active entry must be < the row count of its pool (precondition, not
+ *                checked); entries at columns >= lens[t] are never read.
+ *   lens         device int32 [T]: active counts, clamped to [0, W].
+ *   bmm1_scale   score scale in natural-log units (per-tensor form: sm_scale*q_scale*k_scale).
+ *   bmm2_scale   output scale (per-tensor form: k_scale).
+ *   sinks        device float32 [H] natural-log sink logits, or NULL for no sink.
+ *   out          device BF16 [T, H, 512] (16-byte aligned), written for every (t, h).
+ *   lse          device float32 [T, H] or NULL: ln(sum_c e^{s_c} + e^{sink}) (base 2 with
+ *                SMLA_LSE_LOG2); -inf for a token with no active column, whose output is +0.
+ *   flags        SMLA_LSE_LOG2 | SMLA_P_ONE_TERM.
+ *   plan         NULL for smla_decode_plan's, else an explicit decomposition (results are
+ *                bit-identical across `tiles` for a fixed `splits`).
+ *   workspace    device scratch of workspace_bytes >= smla_decode_workspace_size(plan, T, H),
+ *                16-byte aligned (may be NULL when that size is 0).  Its contents on entry do
+ *                not matter.  Calls that share a workspace must be stream-ordered.
+ *
+ * T == 0 is a no-op returning SMLA_OK after the size, flag and plan checks (the pointers are
+ * not examined: empty tensors may have null data).  Errors: SMLA_EINVAL (null required
+ * pointer, T < 0,
+ * H <= 0 or H % 16 != 0, W < 1, bad row_bytes/qk_dim, misaligned pointer or stride,
+ * split_col outside [0, W], unknown flag, non-finite scale, bad plan), SMLA_EWORKSPACE,
+ * SMLA_EHIP (launch failure).
+ */
+smla_status sparse_mla_decode(const void *q, int64_t q_stride_t, int64_t q_stride_h,
+                              const void *kv_a, int64_t rows_a,
+                              const void *kv_b, int64_t rows_b, int32_t split_col,
+                              int32_t row_bytes, int32_t qk_dim,
+                              const int32_t *indices, const int32_t *lens,
+                              int32_t T, int32_t H, int32_t W,
+                              float bmm1_scale, float bmm2_scale, const float *sinks,
+                              void *out, float *lse, uint32_t flags,
+                              const smla_plan *plan, void *workspace, size_t workspace_bytes,
+                              hipStream_t stream);
+
+/*
+ * lse_merge -- LSE-weighted merge of S split-KV partials (dcp page, DcpValue.merge).
+ *
+ *   partials  device BF16 [S, T, H, D] (16-byte aligned): source s's normalized output.
+ *   lse2      device float32 [S, T, H]: source s's LSE in base 2.  A source is empty unless
+ *             its LSE is finite (NaN and +-inf are empty); an empty source's partial is never
+ *             read.
+ *   out       device BF16 [T, H, D] (16-byte aligned):
+ *             sum_s (2^{lse_s - top} / sum_r 2^{lse_r - top}) x_s in FP32, one BF16 rounding;
+ *             +0 where every source is empty.
+ *   lse_out   device float32 [T, H] or NULL: (top + log2 sum_s 2^{lse_s - top}) in natural log
+ *             (base 2 with SMLA_LSE_LOG2); -inf where every source is empty.
+ *
+ * S in [1, 64], D a multiple of 8.  T == 0 is a no-op (pointers not examined).  Errors: SMLA_EINVAL (null pointer,
+ * bad size, misalignment, unknown flag), SMLA_EUNSUPPORTED (S > 64 or D % 8 != 0),
+ * SMLA_EHIP.
+ */
+smla_status lse_merge(const void *partials, const float *lse2, int32_t S, int32_t T, int32_t H,
+                      int32_t D, void *out, float *lse_out, uint32_t flags, hipStream_t stream);
+
+/* A static string describing a status code. */
+const char *smla_strerror(smla_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SMLA_H */

@@ -1,0 +1,143 @@
+"""Sparse MLA decode and split-KV LSE merge on AMD MI355X (gfx950).
+
+A thin ctypes binding of the C ABI in ``include/smla.h`` (library ``_build/libsmla.so``):
+argument marshalling only.  Every step of the computation runs in the library's HIP kernels;
+PyTorch supplies device memory and the current stream.  Importing this package does not load
+the library; the first call does, and raises if it is missing (build it with
+``python -m sparse_mla_attention_amd.build`` or ``__graft_entry__.build()``).  There is no CPU
+fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "_build", "libsmla.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "smla.h")
+
+SMLA_OK, SMLA_EINVAL, SMLA_EUNSUPPORTED, SMLA_EWORKSPACE, SMLA_EHIP = 0, 1, 2, 3, 4
+SMLA_LSE_LOG2 = 0x1
+SMLA_P_ONE_TERM = 0x2
+
+
+class SmlaError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {_load().smla_strerror(status).decode()} (status {status})")
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [("splits", ctypes.c_int32), ("tiles", ctypes.c_int32),
+                ("chunk", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+    def __repr__(self):
+        return f"Plan(splits={self.splits}, tiles={self.tiles}, chunk={self.chunk})"
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"the HIP library is not built ({LIB_PATH} is missing)")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, U32, F, SZ = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32,
+                               ctypes.c_float, ctypes.c_size_t)
+    L.smla_strerror.argtypes = [I32]
+    L.smla_strerror.restype = ctypes.c_char_p
+    L.smla_decode_plan.argtypes = [I32, I32, I32, I32, U32, ctypes.POINTER(Plan)]
+    L.smla_decode_plan.restype = I32
+    L.smla_decode_workspace_size.argtypes = [ctypes.POINTER(Plan), I32, I32]
+    L.smla_decode_workspace_size.restype = SZ
+    L.sparse_mla_decode.argtypes = [P, I64, I64, P, I64, P, I64, I32, I32, I32, P, P, I32, I32,
+                                    I32, F, F, P, P, P, U32, ctypes.POINTER(Plan), P, SZ, P]
+    L.sparse_mla_decode.restype = I32
+    L.lse_merge.argtypes = [P, P, I32, I32, I32, I32, P, P, U32, P]
+    L.lse_merge.restype = I32
+    _lib = L
+    return L
+
+
+def library():
+    """The loaded ctypes library (raises if it is not built)."""
+    return _load()
+
+
+def declared_functions() -> list[str]:
+    """Names of the functions include/smla.h declares (for the export check)."""
+    text = open(HEADER_PATH).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) -
+                  {"if", "while", "for", "sizeof", "return"})
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def plan_for(T: int, H: int, W: int, row_bytes: int = 576, flags: int = 0) -> Plan:
+    p = Plan()
+    st = _load().smla_decode_plan(T, H, W, row_bytes, flags, ctypes.byref(p))
+    if st != SMLA_OK:
+        raise SmlaError(st, "smla_decode_plan")
+    return p
+
+
+def workspace_size(plan: Plan, T: int, H: int) -> int:
+    return int(_load().smla_decode_workspace_size(ctypes.byref(plan), T, H))
+
+
+def make_plan(splits: int, tiles: int) -> Plan:
+    return Plan(splits, tiles, 128, 0)
+
+
+def sparse_mla_decode(q, kv_a, indices, lens, bmm1_scale, bmm2_scale, out, lse=None, *,
+                      kv_b=None, split_col=None, sinks=None, qk_dim=None, lse_log2=False,
+                      one_term=False, plan=None, workspace=None, stream=None):
+    """Call sparse_mla_decode on device tensors.
+
+    q: uint8 [T, H, qk_dim] (any strides with unit last stride, 16-byte multiples);
+    kv_a / kv_b: uint8 [rows, row_bytes]; indices int32 [T, W]; lens int32 [T];
+    out bf16 [T, H, 512]; lse float32 [T, H] or None; sinks float32 [H] or None.
+    workspace: a uint8 device tensor of at least workspace_size(plan, T, H) bytes when the plan
+    splits the columns (None otherwise)."""
+    T, H, qd = q.shape
+    W = indices.shape[1]
+    row_bytes = kv_a.shape[1]
+    qk_dim = qd if qk_dim is None else qk_dim
+    flags = (SMLA_LSE_LOG2 if lse_log2 else 0) | (SMLA_P_ONE_TERM if one_term else 0)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = _load().sparse_mla_decode(
+        _ptr(q), q.stride(0) * q.element_size(), q.stride(1) * q.element_size(),
+        _ptr(kv_a), kv_a.shape[0],
+        _ptr(kv_b), 0 if kv_b is None else kv_b.shape[0],
+        W if split_col is None else int(split_col),
+        row_bytes, qk_dim, _ptr(indices), _ptr(lens), T, H, W,
+        float(bmm1_scale), float(bmm2_scale), _ptr(sinks), _ptr(out), _ptr(lse), flags,
+        None if plan is None else ctypes.byref(plan), _ptr(workspace), ws_bytes,
+        _stream(stream))
+    if st != SMLA_OK:
+        raise SmlaError(st, "sparse_mla_decode")
+    return out, lse
+
+
+def lse_merge(partials, lse2, out, lse_out=None, *, lse_log2=False, stream=None):
+    """partials bf16 [S, T, H, D]; lse2 float32 [S, T, H] (base 2); out bf16 [T, H, D];
+    lse_out float32 [T, H] or None."""
+    S, T, H, D = partials.shape
+    st = _load().lse_merge(_ptr(partials), _ptr(lse2), S, T, H, D, _ptr(out), _ptr(lse_out),
+                           SMLA_LSE_LOG2 if lse_log2 else 0, _stream(stream))
+    if st != SMLA_OK:
+        raise SmlaError(st, "lse_merge")
+    return out, lse_out

@@ -1,0 +1,244 @@
+// C ABI of the library: argument validation, launch planning and dispatch (see include/smla.h).
+// Every check happens on the host before anything is launched; no entry point allocates,
+// frees or synchronizes.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include <atomic>
+
+#include "smla.h"
+#include "smla_internal.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+constexpr int kMaxSplits = 64;
+constexpr int kChunk = 128;
+std::atomic<int> g_cu_count[kMaxDevices];
+
+// Compute units of the current device, queried once per device.
+hipError_t current_cu_count(int *cus)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev >= 0 && dev < kMaxDevices) {
+        int cached = g_cu_count[dev].load(std::memory_order_relaxed);
+        if (cached > 0) {
+            *cus = cached;
+            return hipSuccess;
+        }
+    }
+    int n = 0;
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess)
+        return e;
+    if (n <= 0)
+        n = 1;
+    if (dev >= 0 && dev < kMaxDevices)
+        g_cu_count[dev].store(n, std::memory_order_relaxed);
+    *cus = n;
+    return hipSuccess;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
+
+// The largest tile count (16-head tiles per workgroup) this build has a kernel for that
+// divides the head tiles.
+int default_tiles(int32_t H)
+{
+    const int ht = H / 16;
+    for (int t = 4; t > 1; t /= 2)
+        if (ht % t == 0)
+            return t;
+    return 1;
+}
+
+// Key ranges per (token, head group): enough workgroups to cover every compute unit, with at
+// least half a chunk of columns per range on average and at most kMaxSplits ranges.
+int default_splits(int32_t T, int32_t groups, int32_t W, int cus)
+{
+    const int64_t units = (int64_t)T * groups;
+    int64_t want = units > 0 ? (cus + units - 1) / units : 1;
+    int64_t cap = (W + kChunk / 2 - 1) / (kChunk / 2);
+    if (cap < 1)
+        cap = 1;
+    if (want > cap)
+        want = cap;
+    if (want > kMaxSplits)
+        want = kMaxSplits;
+    return want < 1 ? 1 : (int)want;
+}
+
+bool plan_ok(const smla_plan *p, int32_t H)
+{
+    if (p->splits < 1 || p->splits > kMaxSplits)
+        return false;
+    if (p->tiles != 1 && p->tiles != 2 && p->tiles != 4)
+        return false;
+    return (H / 16) % p->tiles == 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *smla_strerror(smla_status status)
+{
+    switch (status) {
+    case SMLA_OK: return "ok";
+    case SMLA_EINVAL: return "invalid argument";
+    case SMLA_EUNSUPPORTED: return "unsupported shape";
+    case SMLA_EWORKSPACE: return "workspace missing or too small";
+    case SMLA_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+smla_status smla_decode_plan(int32_t T, int32_t H, int32_t W, int32_t row_bytes, uint32_t flags,
+                             smla_plan *plan)
+{
+    if (plan == nullptr || T < 0 || H <= 0 || H % 16 != 0 || W < 1)
+        return SMLA_EINVAL;
+    if (row_bytes != 512 && row_bytes != 576)
+        return SMLA_EINVAL;
+    if (flags & ~(SMLA_LSE_LOG2 | SMLA_P_ONE_TERM))
+        return SMLA_EINVAL;
+    int cus = 0;
+    if (current_cu_count(&cus) != hipSuccess)
+        return SMLA_EHIP;
+    plan->tiles = default_tiles(H);
+    plan->splits = default_splits(T, H / 16 / plan->tiles, W, cus);
+    plan->chunk = kChunk;
+    plan->reserved = 0;
+    return SMLA_OK;
+}
+
+size_t smla_decode_workspace_size(const smla_plan *plan, int32_t T, int32_t H)
+{
+    if (plan == nullptr || T < 0 || H <= 0 || H % 16 != 0 || !plan_ok(plan, H))
+        return 0;
+    if (plan->splits == 1)
+        return 0;
+    const size_t units = (size_t)T * (size_t)H * (size_t)plan->splits;
+    return units * 512 * sizeof(float) + units * 2 * sizeof(float);
+}
+
+smla_status sparse_mla_decode(const void *q, int64_t q_stride_t, int64_t q_stride_h,
+                              const void *kv_a, int64_t rows_a,
+                              const void *kv_b, int64_t rows_b, int32_t split_col,
+                              int32_t row_bytes, int32_t qk_dim,
+                              const int32_t *indices, const int32_t *lens,
+                              int32_t T, int32_t H, int32_t W,
+                              float bmm1_scale, float bmm2_scale, const float *sinks,
+                              void *out, float *lse, uint32_t flags,
+                              const smla_plan *plan, void *workspace, size_t workspace_bytes,
+                              hipStream_t stream)
+{
+    // ---- validation (host only) ----------------------------------------------------------
+    if (T < 0 || H <= 0 || H % 16 != 0 || W < 1)
+        return SMLA_EINVAL;
+    if (flags & ~(SMLA_LSE_LOG2 | SMLA_P_ONE_TERM))
+        return SMLA_EINVAL;
+    if (row_bytes != 512 && row_bytes != 576)
+        return SMLA_EINVAL;
+    if ((qk_dim != 512 && qk_dim != 576) || qk_dim > row_bytes)
+        return SMLA_EINVAL;
+    if (!isfinite(bmm1_scale) || !isfinite(bmm2_scale))
+        return SMLA_EINVAL;
+    if (plan != nullptr && !plan_ok(plan, H))
+        return SMLA_EINVAL;
+    if (T == 0)  // empty tensors may have null data pointers
+        return SMLA_OK;
+    if (q == nullptr || kv_a == nullptr || indices == nullptr || lens == nullptr || out == nullptr)
+        return SMLA_EINVAL;
+    if (rows_a < 1)
+        return SMLA_EINVAL;
+    if (kv_b != nullptr && (rows_b < 1 || split_col < 0 || split_col > W))
+        return SMLA_EINVAL;
+    if (!aligned16(q) || (q_stride_t & 15) || (q_stride_h & 15) || q_stride_t < 0 ||
+        q_stride_h < 0)
+        return SMLA_EINVAL;
+    if (!aligned16(kv_a) || (kv_b != nullptr && !aligned16(kv_b)) || !aligned16(out))
+        return SMLA_EINVAL;
+    if (!aligned4(indices) || !aligned4(lens) || (lse != nullptr && !aligned4(lse)) ||
+        (sinks != nullptr && !aligned4(sinks)))
+        return SMLA_EINVAL;
+    smla_plan chosen;
+    if (plan != nullptr) {
+        chosen = *plan;
+    } else {
+        smla_status st = smla_decode_plan(T, H, W, row_bytes, flags, &chosen);
+        if (st != SMLA_OK)
+            return st;
+    }
+    const size_t need = smla_decode_workspace_size(&chosen, T, H);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
+        return SMLA_EWORKSPACE;
+
+    // ---- launch ------------------------------------------------------------------------
+    smla::DecodeParams p;
+    p.q = static_cast<const uint8_t *>(q);
+    p.q_st = q_stride_t;
+    p.q_sh = q_stride_h;
+    p.kv_a = static_cast<const uint8_t *>(kv_a);
+    p.kv_b = static_cast<const uint8_t *>(kv_b);
+    p.split_col = kv_b != nullptr ? split_col : W;
+    p.indices = indices;
+    p.lens = lens;
+    p.T = T;
+    p.H = H;
+    p.W = W;
+    p.scale_log2 = (float)((double)bmm1_scale * 1.4426950408889634);
+    p.bmm2 = bmm2_scale;
+    p.sinks = sinks;
+    p.out = static_cast<uint16_t *>(out);
+    p.lse = lse;
+    p.lse_log2 = (flags & SMLA_LSE_LOG2) ? 1 : 0;
+    p.splits = chosen.splits;
+    p.groups = H / 16 / chosen.tiles;
+    p.ws_o = nullptr;
+    p.ws_ml = nullptr;
+    if (need > 0) {
+        const size_t units = (size_t)T * (size_t)H * (size_t)chosen.splits;
+        p.ws_o = static_cast<float *>(workspace);
+        p.ws_ml = p.ws_o + units * 512;
+    }
+    const hipError_t e = smla::launch_decode(p, chosen.tiles, row_bytes, qk_dim,
+                                             (flags & SMLA_P_ONE_TERM) == 0, stream);
+    return e == hipSuccess ? SMLA_OK : SMLA_EHIP;
+}
+
+smla_status lse_merge(const void *partials, const float *lse2, int32_t S, int32_t T, int32_t H,
+                      int32_t D, void *out, float *lse_out, uint32_t flags, hipStream_t stream)
+{
+    if (S < 1 || T < 0 || H < 1 || D < 1)
+        return SMLA_EINVAL;
+    if (flags & ~SMLA_LSE_LOG2)
+        return SMLA_EINVAL;
+    if (S > 64 || D % 8 != 0)
+        return SMLA_EUNSUPPORTED;
+    if (T == 0)  // empty tensors may have null data pointers
+        return SMLA_OK;
+    if (partials == nullptr || lse2 == nullptr || out == nullptr)
+        return SMLA_EINVAL;
+    if (!aligned16(partials) || !aligned16(out) || !aligned4(lse2) ||
+        (lse_out != nullptr && !aligned4(lse_out)))
+        return SMLA_EINVAL;
+    smla::LseMergeParams p;
+    p.partials = static_cast<const uint16_t *>(partials);
+    p.lse2 = lse2;
+    p.S = S;
+    p.T = T;
+    p.H = H;
+    p.D = D;
+    p.out = static_cast<uint16_t *>(out);
+    p.lse_out = lse_out;
+    p.lse_log2 = (flags & SMLA_LSE_LOG2) ? 1 : 0;
+    return smla::launch_lse_merge(p, stream) == hipSuccess ? SMLA_OK : SMLA_EHIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,46 @@
+// Internal declarations shared by the library's own source files (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace smla {
+
+// One sparse_mla_decode launch, fully resolved on the host.
+struct DecodeParams {
+    const uint8_t *q;
+    int64_t q_st, q_sh;         // q strides in bytes (token, head)
+    const uint8_t *kv_a;        // pool A
+    const uint8_t *kv_b;        // pool B or null
+    int32_t split_col;          // columns >= split_col use pool B (when kv_b is set)
+    const int32_t *indices;     // [T, W]
+    const int32_t *lens;        // [T]
+    int32_t T, H, W;
+    float scale_log2;           // bmm1 * log2(e)
+    float bmm2;
+    const float *sinks;         // [H] natural-log units, or null
+    uint16_t *out;              // BF16 [T, H, 512]
+    float *lse;                 // [T, H] or null
+    int32_t lse_log2;           // 1: base-2 LSE
+    float *ws_o;                // FP32 partials [T, H, splits, 512] (splits > 1)
+    float *ws_ml;               // (max, sum) [T, H, splits, 2] (splits > 1)
+    int32_t splits;             // key ranges per (token, head group)
+    int32_t groups;             // head groups per token = H / (16 * tiles)
+};
+
+// Launch the decode (and, for splits > 1, the split merge) on `stream`.
+hipError_t launch_decode(const DecodeParams &p, int tiles, int row_bytes, int qk_dim,
+                         bool two_term, hipStream_t stream);
+
+struct LseMergeParams {
+    const uint16_t *partials;   // BF16 [S, T, H, D]
+    const float *lse2;          // [S, T, H] base 2
+    int32_t S, T, H, D;
+    uint16_t *out;              // BF16 [T, H, D]
+    float *lse_out;             // [T, H] or null
+    int32_t lse_log2;
+};
+
+hipError_t launch_lse_merge(const LseMergeParams &p, hipStream_t stream);
+
+}  // namespace smla

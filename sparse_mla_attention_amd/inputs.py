@@ -130,7 +130,8 @@ def random_problem(seed: int, T: int, H: int, W: int, *, pool_rows: int = 4096,
     bmm1 = k_scale / np.sqrt(qk_dim)
     return dict(name=f"random{seed}", q=q, kv_a=kv_a, kv_b=kv_b, split_col=int(split_col),
                 qk_dim=int(qk_dim), indices=indices, lens=lens_arr, sinks=sk,
-                bmm1=float(bmm1), bmm2=float(k_scale), lse_log2=lse_log2)
+                bmm1=float(bmm1), bmm2=float(k_scale), lse_log2=lse_log2,
+                value_scale=float(value_scale))
 
 
 def config_tiny(poison: bool = True) -> dict:

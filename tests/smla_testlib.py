@@ -1,0 +1,111 @@
+"""Shared helpers of the GPU parity tests: move a seeded problem to the device, run the HIP
+path through the C ABI, decode its BF16 output, and measure errors against the oracle."""
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import torch
+
+import sparse_mla_attention_amd as smla
+
+LN2 = math.log(2.0)
+
+# Tolerances against the exact oracle, on unit-scale data (rel-L2 and max-abs of the output,
+# absolute LSE in natural-log units): the gate the method is held to.
+EXACT_REL_L2 = 1e-2
+EXACT_MAX_ABS = 3e-2
+LSE_ABS = 2e-3
+# The one-term E4M3-P path against mimic mode of the same plan: the two model the same
+# quantization points and differ only by FP32 summation order, the FP32 logits and exp2, and
+# the BF16 output rounding, which alone contributes ~1.7e-3 relative L2 (8 significant bits:
+# a half-ulp of 2^-9..2^-8 relative, uniformly distributed).
+MIMIC_REL_L2 = 3e-3
+MIMIC_MAX_ABS = 1e-2
+
+
+def log(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def dev(x, device="cuda"):
+    if x is None:
+        return None
+    return torch.from_numpy(np.ascontiguousarray(x)).to(device)
+
+
+def bf16_to_f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+class DeviceProblem:
+    """A problem dict (from inputs.py) resident on the device."""
+
+    def __init__(self, p: dict, device="cuda", q_pad_heads: int = 0):
+        self.p = p
+        T, H, qd = p["q"].shape
+        self.T, self.H = T, H
+        if q_pad_heads:
+            # q as a view into a larger buffer [T, H + pad, qd]: non-trivial head/token strides
+            buf = torch.full((T, H + q_pad_heads, qd), 0x7F, dtype=torch.uint8, device=device)
+            buf[:, :H] = dev(p["q"], device)
+            self.q = buf[:, :H]
+        else:
+            self.q = dev(p["q"], device)
+        self.kv_a = dev(p["kv_a"], device)
+        self.kv_b = dev(p["kv_b"], device)
+        self.indices = dev(p["indices"], device)
+        self.lens = dev(p["lens"], device)
+        self.sinks = dev(p["sinks"], device)
+        self.out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=device)
+        self.lse = torch.empty((T, H), dtype=torch.float32, device=device)
+
+    def run(self, plan=None, one_term=False, lse_log2=None, poison_out=True):
+        p = self.p
+        if lse_log2 is None:
+            lse_log2 = bool(p.get("lse_log2", False))
+        if poison_out:  # outputs start as NaN: every element must be written
+            self.out.view(torch.int16).fill_(0x7FC0)
+            self.lse.fill_(float("nan"))
+        use = plan if plan is not None else smla.plan_for(self.T, self.H, p["indices"].shape[1],
+                                                         self.kv_a.shape[1])
+        nbytes = smla.workspace_size(use, self.T, self.H)
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=self.q.device) if nbytes else None
+        if ws is not None:
+            ws.fill_(0xFF)  # NaN garbage: the kernels must not depend on its contents
+        smla.sparse_mla_decode(self.q, self.kv_a, self.indices, self.lens, p["bmm1"], p["bmm2"],
+                               self.out, self.lse, kv_b=self.kv_b, split_col=p["split_col"],
+                               sinks=self.sinks, qk_dim=p["qk_dim"], lse_log2=lse_log2,
+                               one_term=one_term, plan=use, workspace=ws)
+        torch.cuda.synchronize()
+        out = bf16_to_f64(self.out).reshape(self.T * self.H, 512)
+        lse = self.lse.cpu().numpy().astype(np.float64).reshape(-1)
+        return out, lse, use
+
+
+def rel_l2(a, b):
+    d = np.linalg.norm(b)
+    return float(np.linalg.norm(a - b) / d) if d > 0 else float(np.linalg.norm(a - b))
+
+
+def lse_err(a, b):
+    fin = np.isfinite(b)
+    assert np.array_equal(np.isfinite(a), fin), "LSE finiteness differs"
+    assert np.all(a[~fin] == b[~fin]), "non-finite LSE values differ"
+    return float(np.abs(a[fin] - b[fin]).max()) if fin.any() else 0.0
+
+
+def check_empty_rows_exact(out_t: torch.Tensor, lse_t: torch.Tensor, p: dict):
+    """Rows with no active column: BF16 +0.0 bits and LSE -inf bits, exactly."""
+    W = p["indices"].shape[1]
+    for t in range(p["q"].shape[0]):
+        n = int(np.clip(p["lens"][t], 0, W))
+        if (p["indices"][t, :n] >= 0).any():
+            continue
+        bits = out_t[t].view(torch.int16).cpu()
+        assert torch.count_nonzero(bits) == 0, f"token {t}: empty row not all +0.0"
+        lb = lse_t[t].cpu().view(torch.int32)
+        assert torch.all(lb == torch.tensor(np.float32(-np.inf)).view(torch.int32)), \
+            f"token {t}: empty row LSE not -inf"

@@ -1,0 +1,168 @@
+"""Parity of the HIP sparse_mla_decode (through the C ABI) with the FP64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_mla_attention_amd as smla
+from sparse_mla_attention_amd import inputs
+from smla_testlib import (EXACT_MAX_ABS, EXACT_REL_L2, LSE_ABS, MIMIC_MAX_ABS, MIMIC_REL_L2,
+                          DeviceProblem, check_empty_rows_exact, log, lse_err, rel_l2)
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_exact(p, out, lse, lse_log2, label):
+    ref, ref_lse = oracle.decode_exact(p, lse_log2=lse_log2)
+    if lse_log2:  # compare LSE in natural-log units
+        ref_lse, lse = ref_lse * np.log(2), lse * np.log(2)
+    r = rel_l2(out, ref)
+    m = float(np.abs(out - ref).max())
+    le = lse_err(lse, ref_lse)
+    log(f"{label}: rel_l2={r:.3e} max_abs={m:.3e} lse={le:.3e}")
+    assert np.all(np.isfinite(out)), "non-finite output"
+    # the max-abs bound is stated for unit-scale data; it scales with the V values
+    tol_abs = EXACT_MAX_ABS * max(1.0, p.get("value_scale", 1.0))
+    assert r <= EXACT_REL_L2 and m <= tol_abs and le <= LSE_ABS, (r, m, le)
+    return r, m, le
+
+
+def _check_mimic(p, out, lse, lse_log2, plan, label):
+    ref, ref_lse = oracle.decode_mimic(p, splits=plan.splits, chunk=plan.chunk, terms=1,
+                                       lse_log2=lse_log2)
+    if lse_log2:
+        ref_lse, lse = ref_lse * np.log(2), lse * np.log(2)
+    r = rel_l2(out, ref)
+    m = float(np.abs(out - ref).max())
+    le = lse_err(lse, ref_lse)
+    log(f"{label} vs mimic: rel_l2={r:.3e} max_abs={m:.3e} lse={le:.3e}")
+    tol_abs = MIMIC_MAX_ABS * max(1.0, p.get("value_scale", 1.0))
+    assert r <= MIMIC_REL_L2 and m <= tol_abs and le <= LSE_ABS, (r, m, le)
+
+
+CASES = {
+    # name: random_problem kwargs
+    "one_chunk": dict(seed=100, T=1, H=16, W=64),
+    "ragged_multi_chunk": dict(seed=101, T=3, H=32, W=300, lens=[300, 129, 77], neg_frac=0.1),
+    "empty_rows_interior": dict(seed=102, T=4, H=16, W=200, lens=[150, 0, -3, 200],
+                                neg_frac=0.05),
+    "all_neg_row": dict(seed=103, T=2, H=16, W=40, neg_frac=1.0, lens=[40, 0]),
+    "lens_past_W": dict(seed=104, T=2, H=16, W=50, lens=[50, 50]),
+    "qk512_rows512_sinks": dict(seed=105, T=3, H=16, W=260, row_bytes=512, sinks=True,
+                                neg_frac=0.1, lens=[260, 10, 133]),
+    "two_pools": dict(seed=106, T=3, H=16, W=250, row_bytes=512, two_pools=True, split_col=128,
+                      rows_b=5000, sinks=True, neg_frac=0.1, lens=[250, 100, 129]),
+    "qk512_rows576": dict(seed=107, T=2, H=32, W=140, qk_dim=512),
+    "H64_amax_scaled": dict(seed=108, T=2, H=64, W=390, kv_scale_to_amax=True, lens=[390, 5]),
+    "large_scores": dict(seed=109, T=2, H=16, W=300, value_scale=4.0),
+    "duplicates": dict(seed=110, T=2, H=16, W=200, duplicates=True, pool_rows=50),
+    "W1": dict(seed=111, T=3, H=16, W=1, lens=[1, 0, 1]),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+@pytest.mark.parametrize("one_term", [False, True])
+def test_decode_random_cases(name, one_term):
+    kw = dict(CASES[name])
+    seed, T, H, W = kw.pop("seed"), kw.pop("T"), kw.pop("H"), kw.pop("W")
+    if "lens" in kw and kw["lens"] is not None and not np.isscalar(kw["lens"]):
+        kw["lens"] = np.array(kw["lens"])
+    kw.setdefault("pool_rows", 3000)
+    p = inputs.random_problem(seed, T, H, W, **kw)
+    if name == "lens_past_W":
+        p["lens"] = np.array([50, 10 ** 6], np.int32)
+    log(f"case {name} one_term={one_term} T={T} H={H} W={W}")
+    d = DeviceProblem(p)
+    for lse_log2 in (False, True):
+        out, lse, plan = d.run(one_term=one_term, lse_log2=lse_log2)
+        check_empty_rows_exact(d.out, d.lse, p)
+        label = f"{name} {plan} log2={lse_log2}"
+        if one_term:
+            _check_mimic(p, out, lse, lse_log2, plan, label)
+            ref, ref_lse = oracle.decode_exact(p, lse_log2=False)
+            m = float(np.abs(out - ref).max())
+            assert m <= EXACT_MAX_ABS * max(1.0, p.get("value_scale", 1.0)), m
+        else:
+            _check_exact(p, out, lse, lse_log2, label)
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 7, 16])
+def test_decode_split_plans(splits):
+    """Every split count gives the same answer within tolerance (empty ranges included: with
+    16 splits of 40 columns most ranges are short, some empty)."""
+    p = inputs.random_problem(200 + splits, 3, 32, 300, pool_rows=3000,
+                              lens=np.array([300, 40, 0]), neg_frac=0.1, sinks=True)
+    d = DeviceProblem(p)
+    for one_term in (False, True):
+        plan = smla.make_plan(splits, 2)
+        out, lse, _ = d.run(plan=plan, one_term=one_term)
+        check_empty_rows_exact(d.out, d.lse, p)
+        if one_term:
+            _check_mimic(p, out, lse, False, plan, f"splits={splits} one-term")
+        else:
+            _check_exact(p, out, lse, False, f"splits={splits}")
+
+
+@pytest.mark.parametrize("one_term", [False, True])
+def test_tile_grouping_is_bit_identical(one_term):
+    """The attn_sparse page claims its wide-CTA variant matches the one-tile kernel bit for bit;
+    here a workgroup's tile count changes only which waves share a gathered chunk, so results
+    at a fixed split plan must be bit-identical across 1, 2 and 4 tiles per workgroup."""
+    p = inputs.random_problem(300, 3, 64, 333, pool_rows=4000, lens=np.array([333, 200, 1]),
+                              neg_frac=0.1, sinks=True)
+    d = DeviceProblem(p)
+    for splits in (1, 3):
+        ref_bits = ref_lse = None
+        for tiles in (1, 2, 4):
+            d.run(plan=smla.make_plan(splits, tiles), one_term=one_term)
+            bits = d.out.view(torch.int16).cpu().clone()
+            lb = d.lse.cpu().view(torch.int32).clone()
+            if ref_bits is None:
+                ref_bits, ref_lse = bits, lb
+            else:
+                assert torch.equal(bits, ref_bits), f"splits={splits} tiles={tiles}: out differs"
+                assert torch.equal(lb, ref_lse), f"splits={splits} tiles={tiles}: lse differs"
+
+
+def test_padded_q_strides():
+    """q as a view of a larger [T, H + 16, 576] buffer (the pages' padded q mailbox rows)."""
+    p = inputs.random_problem(400, 2, 32, 150, pool_rows=2000)
+    d = DeviceProblem(p, q_pad_heads=16)
+    out, lse, _ = d.run()
+    _check_exact(p, out, lse, False, "padded q")
+
+
+def test_repeated_calls_are_deterministic():
+    p = inputs.random_problem(401, 4, 32, 500, pool_rows=6000, neg_frac=0.1)
+    d = DeviceProblem(p)
+    plan = smla.make_plan(3, 2)
+    d.run(plan=plan)
+    a = d.out.view(torch.int16).cpu().clone()
+    for _ in range(3):
+        d.run(plan=plan)
+        assert torch.equal(d.out.view(torch.int16).cpu(), a)
+
+
+def test_t0_is_a_noop():
+    p = inputs.random_problem(402, 1, 16, 8, pool_rows=64)
+    d = DeviceProblem(p)
+    out = torch.zeros((0, 16, 512), dtype=torch.bfloat16, device="cuda")
+    q = d.q[:0]
+    smla.sparse_mla_decode(q, d.kv_a, d.indices[:0], d.lens[:0], 1.0, 1.0, out)
+    torch.cuda.synchronize()
+
+
+def test_invalid_arguments_are_rejected():
+    p = inputs.random_problem(403, 1, 16, 8, pool_rows=64)
+    d = DeviceProblem(p)
+    with pytest.raises(smla.SmlaError) as e:  # H not a multiple of 16
+        smla.sparse_mla_decode(d.q[:, :8], d.kv_a, d.indices, d.lens, 1.0, 1.0, d.out[:, :8])
+    assert e.value.status == smla.SMLA_EINVAL
+    plan = smla.make_plan(4, 1)
+    with pytest.raises(smla.SmlaError) as e:  # split plan without a workspace
+        smla.sparse_mla_decode(d.q, d.kv_a, d.indices, d.lens, 1.0, 1.0, d.out, plan=plan)
+    assert e.value.status == smla.SMLA_EWORKSPACE
+    with pytest.raises(smla.SmlaError) as e:  # bad tile count
+        smla.sparse_mla_decode(d.q, d.kv_a, d.indices, d.lens, 1.0, 1.0, d.out,
+                               plan=smla.make_plan(1, 3))
+    assert e.value.status == smla.SMLA_EINVAL
