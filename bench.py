@@ -63,6 +63,7 @@ def traffic_for(plan, one_term):
 
 
 def time_calls(fn, n, stream):
+    """Back-to-back launches from Python; ms per call (includes any host launch gaps)."""
     import torch
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
@@ -73,6 +74,35 @@ def time_calls(fn, n, stream):
     end.record(stream)
     torch.cuda.synchronize()
     return start.elapsed_time(end) / n  # ms per call
+
+
+def graph_time(fn, calls_per_graph, replays):
+    """Device time per call: `calls_per_graph` calls captured in one HIP graph, replayed
+    `replays` times; the median over replays of (elapsed / calls_per_graph), in ms."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for i in range(calls_per_graph):  # warm the code paths on the capture stream
+            fn(i, s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for i in range(calls_per_graph):
+            fn(i, s)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(replays):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b) / calls_per_graph)
+    times.sort()
+    return times[len(times) // 2]
 
 
 def latency_configs(smla, inputs, stream, reps=200):
@@ -92,20 +122,22 @@ def latency_configs(smla, inputs, stream, reps=200):
         nb = smla.workspace_size(plan, T, H)
         ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda") if nb else None
 
-        def call(i):
+        def call(i, s=stream):
             smla.sparse_mla_decode(d["q"], d["kv_a"], d["indices"], d["lens"], p["bmm1"],
                                    p["bmm2"], out, lse, kv_b=d["kv_b"], split_col=p["split_col"],
                                    sinks=d["sinks"], qk_dim=p["qk_dim"], lse_log2=p["lse_log2"],
-                                   plan=plan, workspace=ws, stream=stream)
+                                   plan=plan, workspace=ws, stream=s)
         for i in range(20):
             call(i)
-        ms = time_calls(call, reps, stream)
+        ms_eager = time_calls(call, reps, stream)
+        ms = graph_time(call, 100, 20)
         active = int(sum(((p["indices"][t, :int(np.clip(p["lens"][t], 0, W))] >= 0).sum())
                          for t in range(T)))
-        res[name] = {"us_per_call": round(ms * 1e3, 3), "T": T, "H": H,
-                     "gathered_bytes": active * p["kv_a"].shape[1],
+        res[name] = {"us_per_call": round(ms * 1e3, 3), "us_per_call_eager": round(ms_eager * 1e3, 3),
+                     "T": T, "H": H, "gathered_bytes": active * p["kv_a"].shape[1],
                      "plan": f"splits={plan.splits},tiles={plan.tiles}"}
-        print(f"[bench] latency {name}: {ms * 1e3:.2f} us/call", file=sys.stderr, flush=True)
+        print(f"[bench] latency {name}: {ms * 1e3:.2f} us/call (graph), {ms_eager * 1e3:.2f} "
+              f"(eager)", file=sys.stderr, flush=True)
     return res
 
 
@@ -174,16 +206,18 @@ def main():
     ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda") if nb else None
     sets = w["index_sets"]
 
-    def call(i):
+    def call(i, s=stream):
         smla.sparse_mla_decode(w["q"], w["kv_a"], sets[i % len(sets)], w["lens"], w["bmm1"],
                                w["bmm2"], out, lse, one_term=args.one_term, plan=plan,
-                               workspace=ws, stream=stream)
+                               workspace=ws, stream=s)
 
     for i in range(args.warmup):
         call(i)
     torch.cuda.synchronize()
     print(f"[bench] timing {args.steps} calls, {plan}", file=sys.stderr, flush=True)
+    # the timed steps: back-to-back calls on the stream, bracketed by synchronizations
     ms = time_calls(call, args.steps, stream)
+    ms_graph = graph_time(call, len(sets), max(4, args.steps // len(sets)))
 
     gathered = T * W * ROW_BYTES  # every column active: lens = W, no -1 entries
     gbs = gathered / (ms * 1e-3) / 1e9
@@ -203,7 +237,8 @@ def main():
         "config": {"workload": "large-batch sparse MLA decode: T=64 tokens, H=128 heads, 2048 "
                                "active 576-byte E4M3 rows per token from a 1,048,576-row pool",
                    "p_terms": 1 if args.one_term else 2, "plan": f"splits={plan.splits},"
-                   f"tiles={plan.tiles}", "us_per_call": round(ms * 1e3, 2)},
+                   f"tiles={plan.tiles}", "us_per_call": round(ms * 1e3, 2),
+                   "us_per_call_graph": round(ms_graph * 1e3, 2)},
         "roofline": roof,
     }
     if not args.no_latency:

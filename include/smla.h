@@ -59,7 +59,7 @@ typedef int32_t smla_status;
  * FP32 when splits > 1. */
 typedef struct smla_plan {
     int32_t splits; /* >= 1 */
-    int32_t tiles;  /* 16-head tiles per workgroup: 1, 2, 4 or 8, dividing H / 16 */
+    int32_t tiles;  /* 16-head tiles per workgroup (one wave each): 1, 2, 4 or 8, dividing H / 16 */
     int32_t chunk;  /* columns per gathered chunk (128 in this build; output only) */
     int32_t reserved;
 } smla_plan;

@@ -46,8 +46,9 @@ hipError_t current_cu_count(int *cus)
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
 
-// The largest tile count (16-head tiles per workgroup) this build has a kernel for that
-// divides the head tiles.
+// The largest tile count up to 4 (16-head tiles per workgroup) that divides the head tiles:
+// measured on MI355X, 4 tiles (4 waves, one per SIMD) beat 8 at the large-batch shape because
+// the chunk's LDS operand traffic, not the wave count, bounds a workgroup.
 int default_tiles(int32_t H)
 {
     const int ht = H / 16;
@@ -77,7 +78,7 @@ bool plan_ok(const smla_plan *p, int32_t H)
 {
     if (p->splits < 1 || p->splits > kMaxSplits)
         return false;
-    if (p->tiles != 1 && p->tiles != 2 && p->tiles != 4)
+    if (p->tiles != 1 && p->tiles != 2 && p->tiles != 4 && p->tiles != 8)
         return false;
     return (H / 16) % p->tiles == 0;
 }

@@ -14,24 +14,31 @@
 // are zero and their scores are forced to -inf.  Two chunk buffers alternate: the gather of
 // chunk c+1 is in flight while chunk c is computed.
 //
+// LDS layout of a chunk buffer: row-major, 128 rows x row_bytes, the 16-byte pieces of row r
+// stored in XOR-permuted order (piece p at position p ^ a(r)).  A gather instruction fills 64
+// consecutive 16-byte positions, i.e. about two whole rows, so its global reads coalesce into
+// whole cache lines; the permutation puts the 16 rows of a QK operand tile and the 8 rows of a
+// transposed V read on distinct LDS banks (a(r) = ((r >> 2) ^ ((r >> 4) << 1)) & 3 for
+// 576-byte rows, conflict-free; r & 7 for 512-byte rows, at most 2-way).
+//
 // Per wave and chunk (16 heads x 128 keys):
 //   S^T = K Q^T on v_mfma_scale_f32_16x16x128_f8f6f4 (scales 2^0): A = 16 key rows from LDS,
 //     B = the wave's Q fragments, kept in VGPRs for the whole kernel.  Lane (h, g) of the
-//     accumulator holds 4 keys of head h, so the softmax of head h lives in the 4 lanes h+16g.
+//     accumulator of tile u holds keys 16u + 4g + [0, 4) of head h, so the softmax of head h
+//     lives in the 4 lanes h + 16g.  Steps run block-major (consecutive MFMAs feed different
+//     tiles) with the next A operand read while the current MFMA runs.
 //   softmax: masked scores -> -inf, chunk max (in-lane, then 2 cross-lane steps), running max,
 //     alpha = 2^(m_old - m_new), P = 2^(s2 - m_new + log2 448) rounded to E4M3 by
 //     v_cvt_pk_fp8_f32 (RNE; P <= 448 by construction, where the conversion is exact RNE),
-//     FP32 sums of the unquantized P, accumulators rescaled only when some alpha != 1.
+//     FP32 sums of the unquantized P, accumulators rescaled by alpha.
 //   O^T += V^T P^T on the same MFMA: B = P straight from the softmax registers (no LDS round
-//     trip: the key order of the QK tiles is permuted so that each lane's 32 P bytes are the
-//     keys its V fragment holds), A = V^T read with ds_read_b64_tr_b8 (an 8x16 byte block of 8
-//     key rows is returned column-wise, 8 keys of one latent column per lane).
+//     trip: P register u of lane group g holds keys 16u + 4g + [0, 4), and the V^T operand is
+//     read with ds_read_b64_tr_b8 from exactly those rows: an 8 x 16 byte block of rows
+//     {32j + 4g + [0,4), 32j + 16 + 4g + [0,4)} returned column-wise, 8 keys of one latent
+//     column per lane), the V^T operand of tile v+D read while tile v's MFMAs run.
 //   Two-term P (default): P = hi + lo/16 with hi = E4M3(P), lo = E4M3(16 (P - hi)); the second
 //     product uses the MFMA's E8M0 B scale 2^-4, so it costs one more MFMA per tile and no
 //     conversion of V.
-//
-// LDS per workgroup: 2 x 128 rows x (row_bytes + 16) bytes (the 16-byte pad per row spreads
-// the 16-row MFMA operand reads over the banks) + 3 x 128 masked indices.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -46,7 +53,6 @@ typedef int v2i __attribute__((ext_vector_type(2)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 #define SMLA_LDS(T) __attribute__((address_space(3))) T
-#define SMLA_GLOBAL(T) __attribute__((address_space(1))) T
 
 constexpr int CHUNK = 128;                         // columns per gathered chunk
 constexpr float ANCHOR = 448.0f;                   // P anchor: E4M3's largest finite value
@@ -61,23 +67,29 @@ __device__ __attribute__((aligned(16))) uint8_t g_zero_row[576];
 
 template <int RB>
 struct Geom {
-    static constexpr int PITCH = RB + 16;     // LDS bytes per gathered row
-    static constexpr int SLOTS = PITCH / 16;  // 16-byte slots per LDS row; the last is the pad
-    static constexpr int BUF = CHUNK * PITCH; // one chunk buffer
+    static constexpr int PIECES = RB / 16;   // 16-byte pieces of a row
+    static constexpr int BUF = CHUNK * RB;   // one chunk buffer
+    // XOR applied to the piece index of row r (keeps the 128-byte K block of a piece)
+    __device__ static constexpr int perm(int r)
+    {
+        return RB == 576 ? (((r >> 2) ^ ((r >> 4) << 1)) & 3) : (r & 7);
+    }
 };
 
-__device__ inline v8i lds_read32(const uint8_t *p)
+__device__ inline v8i join(v4i x, v4i y)
 {
-    const v4i *v = reinterpret_cast<const v4i *>(p);
-    v4i x = v[0], y = v[1];
     return v8i{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+}
+
+__device__ inline v4i lds16(const uint8_t *base, int off)
+{
+    return *reinterpret_cast<const v4i *>(base + off);
 }
 
 __device__ inline v8i global_read32(const uint8_t *p)
 {
     const v4i *v = reinterpret_cast<const v4i *>(p);
-    v4i x = v[0], y = v[1];
-    return v8i{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+    return join(v[0], v[1]);
 }
 
 __device__ inline v4f mfma_fp8(v8i a, v8i b, v4f c)
@@ -128,21 +140,8 @@ __device__ inline uint32_t bf16_bits(float x)
     return u >> 16;
 }
 
-// The raw index of position pos of the token's columns, or -1 past the range.  Only positions
-// < end (<= clamped count <= W) are read.
-__device__ inline int load_index(const int32_t *idx_row, int pos, int end)
-{
-    return pos < end ? idx_row[pos] : -1;
-}
-
-// Any negative index is an unused column.
-__device__ inline int mask_index(int v)
-{
-    return v < 0 ? -1 : v;
-}
-
 template <int TILES, int RB, int QK, bool TWO>
-__global__ void __launch_bounds__(64 * TILES) decode_kernel(DecodeParams a)
+__global__ void __launch_bounds__(64 * TILES, 2) decode_kernel(DecodeParams a)
 {
     constexpr int NT = 64 * TILES;
     using G = Geom<RB>;
@@ -150,11 +149,14 @@ __global__ void __launch_bounds__(64 * TILES) decode_kernel(DecodeParams a)
     constexpr bool TAIL = (QK % 128) != 0;       // qk_dim 576: a last block of 64 bytes
     constexpr int NQ = QB + (TAIL ? 1 : 0);
     constexpr int IDX_PER_THREAD = (CHUNK + NT - 1) / NT;
-    constexpr int GATHER_ITERS = (CHUNK * G::SLOTS + NT - 1) / NT;
+    constexpr int GATHER_ITERS = CHUNK * G::PIECES / NT;  // exact for every tile count
+    static_assert(CHUNK * G::PIECES % NT == 0, "gather slots must tile the waves");
 
     __shared__ __attribute__((aligned(16))) uint8_t kvbuf[2][G::BUF];
-    constexpr int CIDX = CHUNK > NT ? CHUNK : NT;  // every thread owns a slot: no branches
-    __shared__ __attribute__((aligned(16))) int32_t cidx[3][CIDX];
+    // masked indices and gather source rows of three chunks in flight; slot CHUNK is a sink
+    // for threads without a column (no branches around the stores)
+    __shared__ __attribute__((aligned(16))) int32_t cidx[3][CHUNK + 4];
+    __shared__ const uint8_t *rowsrc[3][CHUNK + 1];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -175,55 +177,55 @@ __global__ void __launch_bounds__(64 * TILES) decode_kernel(DecodeParams a)
     const int end = first + mine;
     const int nchunks = (mine + CHUNK - 1) / CHUNK;
     const int32_t *idx_row = a.indices + (int64_t)t * a.W;
+    const uint8_t *zero_row = g_zero_row;
 
     // Q fragments, B operand of S^T = K Q^T: lane (h16, g) holds bytes 128 b + 32 g + [0, 32).
     v8i qf[NQ];
     {
-        const uint8_t *qp = a.q + (int64_t)t * a.q_st + (int64_t)head * a.q_sh + 32 * g;
+        const uint8_t *qp = a.q + (int64_t)t * a.q_st + (int64_t)head * a.q_sh;
 #pragma unroll
         for (int b = 0; b < QB; b++)
-            qf[b] = global_read32(qp + 128 * b);
+            qf[b] = global_read32(qp + 128 * b + 32 * g);
         if constexpr (TAIL) {
-            // bytes 512 + 32 g for g < 2; zero for g >= 2 (both operands zero there)
-            const uint8_t *tp = a.q + (int64_t)t * a.q_st + (int64_t)head * a.q_sh + 512 + 32 * (g & 1);
-            v8i x = global_read32(tp);
+            // bytes 512 + 32 g for g < 2; zero for g >= 2
+            const v8i x = global_read32(qp + 512 + 32 * (g & 1));
             qf[QB] = g < 2 ? x : v8i{0, 0, 0, 0, 0, 0, 0, 0};
         }
     }
 
-    // The gather of chunk c into buffer `buf`: 16-byte slots, one direct-to-LDS load each; a
-    // wave's 64 consecutive slots form one instruction with a wave-uniform LDS base.
-    const uint8_t *zero_row = g_zero_row;
+    // The masked index and the gather source row of position pos (only positions < end, which
+    // is at most the clamped count <= W, are ever read from the index row).
+    auto source_of = [&](int pos, int raw, int32_t *ci, const uint8_t **rs) {
+        const int v = (pos < end && raw >= 0) ? raw : -1;
+        const uint8_t *pool = (a.kv_b != nullptr && pos >= a.split_col) ? a.kv_b : a.kv_a;
+        *ci = v;
+        *rs = v >= 0 ? pool + (int64_t)v * RB : zero_row;
+    };
+
+    // The gather of chunk c into buffer `buf`: 128 * PIECES 16-byte positions, 64 consecutive
+    // ones per wave instruction; position s holds piece (s % PIECES) ^ perm(row) of row
+    // s / PIECES.
     auto gather = [&](int c, int buf) {
-        const int32_t *ci = cidx[c % 3];
-        const int base = first + c * CHUNK;
+        const uint8_t *const *rs = rowsrc[c % 3];
         const uint32_t dst = lds_addr(kvbuf[buf]);
 #pragma unroll 1
         for (int it = 0; it < GATHER_ITERS; it++) {
             const int s0 = it * NT + wave * 64;
-            const uint32_t ldst = __builtin_amdgcn_readfirstlane(dst + (uint32_t)s0 * 16u);
-            const int sl = s0 + lane;
-            const int r = sl / G::SLOTS;
-            const int piece = sl - r * G::SLOTS;
-            if (sl < CHUNK * G::SLOTS && piece != G::SLOTS - 1) {
-                const int idx = ci[r];
-                const uint8_t *src = zero_row + piece * 16;
-                if (idx >= 0) {
-                    const uint8_t *pool =
-                        (a.kv_b != nullptr && base + r >= a.split_col) ? a.kv_b : a.kv_a;
-                    src = pool + (int64_t)idx * RB + piece * 16;
-                }
-                dma16(src, ldst);
-            }
+            const int s = s0 + lane;
+            const int r = s / G::PIECES;
+            const int p = (s - r * G::PIECES) ^ G::perm(r);
+            dma16(rs[r] + 16 * p, __builtin_amdgcn_readfirstlane(dst + (uint32_t)s0 * 16u));
         }
     };
 
-    // prologue: masked indices of chunks 0 and 1, then the gather of chunk 0
+    // prologue: indices and sources of chunks 0 and 1, then the gather of chunk 0
 #pragma unroll
     for (int c = 0; c < 2; c++) {
         if (c < nchunks) {
-            for (int i = tid; i < CHUNK; i += NT)
-                cidx[c][i] = mask_index(load_index(idx_row, first + c * CHUNK + i, end));
+            for (int i = tid; i < CHUNK; i += NT) {
+                const int pos = first + c * CHUNK + i;
+                source_of(pos, pos < end ? idx_row[pos] : -1, &cidx[c][i], &rowsrc[c][i]);
+            }
         }
     }
     __syncthreads();
@@ -237,23 +239,42 @@ __global__ void __launch_bounds__(64 * TILES) decode_kernel(DecodeParams a)
     for (int v = 0; v < 32; v++)
         acc[v] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-    // QK A-operand row of tile u for this lane, and the key each accumulator entry holds:
-    // tile u = 2 j + e, lane row i: key 32 j + 8 (i / 4) + 4 e + i % 4.  Accumulator entry
-    // (u, r) of lane group g then holds key 32 j + 8 g + 4 e + r, so the 8 bytes of VGPRs
-    // (2j, 2j+1) of this lane's P are keys 32 j + 8 g + [0, 8): one ds_read_b64_tr_b8 block.
-    const int vrow = 8 * g + (h16 >> 1);  // V^T read: key row of this lane's 8-byte piece
-    const int vcol = 8 * (h16 & 1);       //            and its column offset in the tile
+    // Lane constants of the operand reads.  QK: the A row of tile u is 16u + h16; its first
+    // piece of block b is (8b + 2g) ^ perm, the second that ^ 1 (byte offset ^ 16).  perm of
+    // row 16u + h16 depends on u only through u & 1 for 576-byte rows, not at all for
+    // 512-byte rows.  PV: this lane provides half (h16 & 1) of row kv_row(j) = 32j + r0,
+    // r0 = 16 (rr >> 2) + 4g + (rr & 3), rr = h16 >> 1, of the 8-row transposed block j; perm
+    // of that row does not depend on j.
+    // [e][k]: piece k of the pair; the per-step parts (16u RB + 128b) have bit 4 clear, so
+    // they add as immediate offsets
+    int qk_off[2][2], qk_tail[2][2];
+#pragma unroll
+    for (int e = 0; e < 2; e++) {
+        const int r = 16 * e + h16;  // the A row of tile e; tiles u with u & 1 == e share perm
+        qk_off[e][0] = h16 * RB + 16 * ((2 * g) ^ G::perm(r));
+        qk_off[e][1] = qk_off[e][0] ^ 16;
+        qk_tail[e][0] = h16 * RB + 16 * ((32 + 2 * (g & 1)) ^ G::perm(r));
+        qk_tail[e][1] = qk_tail[e][0] ^ 16;
+    }
+    constexpr int VX = RB == 576 ? 4 : 8;  // pieces spanned by perm
+    int v_off[VX];
+    {
+        const int rr = h16 >> 1;
+        const int r0 = 16 * (rr >> 2) + 4 * g + (rr & 3);
+#pragma unroll
+        for (int x = 0; x < VX; x++)
+            v_off[x] = r0 * RB + 16 * (x ^ G::perm(r0)) + 8 * (h16 & 1);
+    }
 
 #pragma unroll 1
     for (int c = 0; c < nchunks; c++) {
         const int buf = c & 1;
         // chunk c has landed (each wave waits for its own loads; the barrier publishes them),
-        // every wave is done with chunk c-1, and cidx of chunk c+1 is visible
+        // every wave is done with chunk c-1, and the sources of chunk c+1 are visible
         wait_all_vm();
         __syncthreads();
-        // raw indices of chunk c+2, consumed (masked, stored) only after this chunk's compute;
-        // branch-free: the load address is clamped into the token's row and the value dropped
-        // past the range
+        // raw indices of chunk c+2, consumed only after this chunk's compute; branch-free: the
+        // load address is clamped into the token's row and the value dropped past the range
         int pre[IDX_PER_THREAD];
         int pre_pos[IDX_PER_THREAD];
 #pragma unroll
@@ -268,44 +289,59 @@ __global__ void __launch_bounds__(64 * TILES) decode_kernel(DecodeParams a)
         const int32_t *ci = cidx[c % 3];
 
         // ---- S^T = K Q^T: 8 tiles of 16 keys ------------------------------------------------
+        // Block-major order: consecutive MFMAs feed different tiles, and the A operand of step
+        // i+1 is read from LDS while the MFMA of step i runs.  Lane groups 2 and 3 read the
+        // tail block's bytes of groups 0 and 1 and multiply them by the zero half of their Q
+        // fragment.
         v4f S[8];
 #pragma unroll
-        for (int u = 0; u < 8; u++) {
-            const int row = 32 * (u >> 1) + 8 * (h16 >> 2) + 4 * (u & 1) + (h16 & 3);
-            const uint8_t *ap = kv + row * G::PITCH + 32 * g;
-            v4f s = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int u = 0; u < 8; u++)
+            S[u] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        {
+            auto a_read = [&](int i) {
+                const int b = i >> 3, u = i & 7;
+                const int e = u & 1;
+                const int imm = (b < QB ? 128 * b : 0) + 16 * u * RB;
+                const int *o = b < QB ? qk_off[e] : qk_tail[e];
+                return join(lds16(kv + o[0], imm), lds16(kv + o[1], imm));
+            };
+            constexpr int STEPS = NQ * 8;
+            v8i a_cur = a_read(0);
 #pragma unroll
-            for (int b = 0; b < QB; b++)
-                s = mfma_fp8(lds_read32(ap + 128 * b), qf[b], s);
-            if constexpr (TAIL) {
-                const uint8_t *tp = kv + row * G::PITCH + 512 + 32 * (g & 1);
-                v8i x = lds_read32(tp);
-                x = g < 2 ? x : v8i{0, 0, 0, 0, 0, 0, 0, 0};
-                s = mfma_fp8(x, qf[QB], s);
+            for (int i = 0; i < STEPS; i++) {
+                v8i a_next = a_cur;
+                if (i + 1 < STEPS)
+                    a_next = a_read(i + 1);
+                S[i & 7] = mfma_fp8(a_cur, qf[i >> 3], S[i & 7]);
+                a_cur = a_next;
             }
-            S[u] = s;
-            __builtin_amdgcn_sched_barrier(0);  // bound the live A operands to one tile
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+            for (int i = 0; i < STEPS - 1; i++) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         }
 
         // ---- mask, scale to base 2, chunk max ----------------------------------------------
         float sc[8][4];
         float mx = -INFINITY;
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-            const v4i lo = *reinterpret_cast<const v4i *>(ci + 32 * j + 8 * g);
-            const v4i hi = *reinterpret_cast<const v4i *>(ci + 32 * j + 8 * g + 4);
+        for (int u = 0; u < 8; u++) {
+            const v4i live = *reinterpret_cast<const v4i *>(ci + 16 * u + 4 * g);
 #pragma unroll
             for (int r = 0; r < 4; r++) {
-                sc[2 * j][r] = lo[r] >= 0 ? S[2 * j][r] * a.scale_log2 : -INFINITY;
-                sc[2 * j + 1][r] = hi[r] >= 0 ? S[2 * j + 1][r] * a.scale_log2 : -INFINITY;
-                mx = fmaxf(mx, fmaxf(sc[2 * j][r], sc[2 * j + 1][r]));
+                sc[u][r] = live[r] >= 0 ? S[u][r] * a.scale_log2 : -INFINITY;
+                mx = fmaxf(mx, sc[u][r]);
             }
         }
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         const float m_new = fmaxf(m_run, mx);
         const float alpha = (m_run == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-        const float bias = m_new - LOG2_ANCHOR;
+        // no active column yet: every score is -inf and so is every P argument (finite bias)
+        const float bias = m_new == -INFINITY ? 0.0f : m_new - LOG2_ANCHOR;
 
         // ---- P = 2^(s2 - m_new + log2 448) as E4M3, FP32 sums of the unquantized P ---------
         int pb[8];
@@ -316,7 +352,7 @@ __global__ void __launch_bounds__(64 * TILES) decode_kernel(DecodeParams a)
             float p[4];
 #pragma unroll
             for (int r = 0; r < 4; r++) {
-                p[r] = sc[u][r] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(sc[u][r] - bias);
+                p[r] = __builtin_amdgcn_exp2f(sc[u][r] - bias);  // exp2(-inf) = 0
                 lsum += p[r];
             }
             int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
@@ -346,31 +382,56 @@ __global__ void __launch_bounds__(64 * TILES) decode_kernel(DecodeParams a)
             acc[v] *= alpha;
 
         // ---- O^T += V^T P^T ----------------------------------------------------------------
-        // (compiler fences: keep each tile pair's V reads next to its MFMAs instead of hoisting
-        // all 128 of them above the softmax, which would hold 256 VGPRs)
+        // 32 column tiles (tile v = latent columns 16v .. 16v+15 = piece v of each row); the V^T
+        // operand of tile v+D is read while the MFMAs of tile v run (D = 1 at 8 waves per
+        // workgroup, where the second wave of each SIMD also hides LDS latency, else 2).
         asm volatile("" ::: "memory");
-        const v8i bp = v8i{pb[0], pb[1], pb[2], pb[3], pb[4], pb[5], pb[6], pb[7]};
-        const v8i br = v8i{pr[0], pr[1], pr[2], pr[3], pr[4], pr[5], pr[6], pr[7]};
+        {
+            constexpr int D = TILES == 8 ? 1 : 2;
+            const v8i bp = v8i{pb[0], pb[1], pb[2], pb[3], pb[4], pb[5], pb[6], pb[7]};
+            const v8i br = v8i{pr[0], pr[1], pr[2], pr[3], pr[4], pr[5], pr[6], pr[7]};
+            auto v_read = [&](int v) {
+                v8i av;
+                const int vb = 16 * (v & ~(VX - 1));
 #pragma unroll
-        for (int v = 0; v < 32; v++) {
-            v8i av;
+                for (int j = 0; j < 4; j++) {
+                    const uint8_t *vp = kv + v_off[v & (VX - 1)] + vb + 32 * j * RB;
+                    const v2i x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((SMLA_LDS(v2i) *)vp);
+                    av[2 * j] = x[0];
+                    av[2 * j + 1] = x[1];
+                }
+                return av;
+            };
+            v8i ab[D + 1];
 #pragma unroll
-            for (int j = 0; j < 4; j++) {
-                const uint8_t *vp = kv + (32 * j + vrow) * G::PITCH + 16 * v + vcol;
-                const v2i x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((SMLA_LDS(v2i) *)vp);
-                av[2 * j] = x[0];
-                av[2 * j + 1] = x[1];
+            for (int k = 0; k < D; k++)
+                ab[k] = v_read(k);
+#pragma unroll
+            for (int v = 0; v < 32; v++) {
+                if (v + D < 32)
+                    ab[(v + D) % (D + 1)] = v_read(v + D);
+                const v8i a0 = ab[v % (D + 1)];
+                acc[v] = mfma_fp8(a0, bp, acc[v]);
+                if constexpr (TWO)
+                    acc[v] = mfma_fp8_b_sixteenth(a0, br, acc[v]);
             }
-            acc[v] = mfma_fp8(av, bp, acc[v]);
-            if constexpr (TWO)
-                acc[v] = mfma_fp8_b_sixteenth(av, br, acc[v]);
+            constexpr int PV_MFMA = TWO ? 2 : 1;
+            __builtin_amdgcn_sched_group_barrier(0x100, 4 * D, 1);
+#pragma unroll
+            for (int v = 0; v < 32 - D; v++) {
+                __builtin_amdgcn_sched_group_barrier(0x008, PV_MFMA, 1);
+                __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, D * PV_MFMA, 1);
         }
 
         // slot (c+2) % 3 held chunk c-1, which every wave finished before this iteration's
         // barrier; when c+2 >= nchunks the values are never read
 #pragma unroll
-        for (int k = 0; k < IDX_PER_THREAD; k++)
-            cidx[(c + 2) % 3][tid + k * NT] = pre_pos[k] < end ? mask_index(pre[k]) : -1;
+        for (int k = 0; k < IDX_PER_THREAD; k++) {
+            const int i = min(tid + k * NT, CHUNK);
+            source_of(pre_pos[k], pre[k], &cidx[(c + 2) % 3][i], &rowsrc[(c + 2) % 3][i]);
+        }
     }
 
     // ---- epilogue: the full sum of head h16 over its 4 lanes --------------------------------
@@ -478,6 +539,7 @@ hipError_t launch_tiles(const DecodeParams &p, int tiles, hipStream_t stream)
     case 1: return launch_one<1, RB, QK, TWO>(p, stream);
     case 2: return launch_one<2, RB, QK, TWO>(p, stream);
     case 4: return launch_one<4, RB, QK, TWO>(p, stream);
+    case 8: return launch_one<8, RB, QK, TWO>(p, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -107,13 +107,13 @@ def test_decode_split_plans(splits):
 def test_tile_grouping_is_bit_identical(one_term):
     """The attn_sparse page claims its wide-CTA variant matches the one-tile kernel bit for bit;
     here a workgroup's tile count changes only which waves share a gathered chunk, so results
-    at a fixed split plan must be bit-identical across 1, 2 and 4 tiles per workgroup."""
-    p = inputs.random_problem(300, 3, 64, 333, pool_rows=4000, lens=np.array([333, 200, 1]),
+    at a fixed split plan must be bit-identical across 1, 2, 4 and 8 tiles per workgroup."""
+    p = inputs.random_problem(300, 3, 128, 333, pool_rows=4000, lens=np.array([333, 200, 1]),
                               neg_frac=0.1, sinks=True)
     d = DeviceProblem(p)
     for splits in (1, 3):
         ref_bits = ref_lse = None
-        for tiles in (1, 2, 4):
+        for tiles in (1, 2, 4, 8):
             d.run(plan=smla.make_plan(splits, tiles), one_term=one_term)
             bits = d.out.view(torch.int16).cpu().clone()
             lb = d.lse.cpu().view(torch.int32).clone()
@@ -166,3 +166,41 @@ def test_invalid_arguments_are_rejected():
         smla.sparse_mla_decode(d.q, d.kv_a, d.indices, d.lens, 1.0, 1.0, d.out,
                                plan=smla.make_plan(1, 3))
     assert e.value.status == smla.SMLA_EINVAL
+
+
+def test_graph_replay_matches_eager():
+    """Calls captured in a HIP graph (split plan: decode + merge kernels, workspace reused)
+    replay to the eager result, bit for bit, on every replay, with unrelated eager work and
+    synchronizations between replays."""
+    p = inputs.random_problem(404, 3, 32, 300, pool_rows=4000, neg_frac=0.1, sinks=True,
+                              lens=np.array([300, 0, 177]))
+    d = DeviceProblem(p)
+    plan = smla.make_plan(3, 2)
+    d.run(plan=plan, poison_out=False)
+    ref_out = d.out.view(torch.int16).clone()
+    ref_lse = d.lse.view(torch.int32).clone()
+    ws = torch.empty(smla.workspace_size(plan, d.T, d.H), dtype=torch.uint8, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+
+    def call(stream):
+        smla.sparse_mla_decode(d.q, d.kv_a, d.indices, d.lens, p["bmm1"], p["bmm2"], d.out,
+                               d.lse, sinks=d.sinks, plan=plan, workspace=ws, stream=stream)
+    with torch.cuda.stream(s):
+        call(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        call(s)
+        call(s)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        d.out.view(torch.int16).fill_(0x7FC0)
+        d.lse.fill_(float("nan"))
+        junk = torch.randn(1 << 16, device="cuda").sum()  # unrelated eager work
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(d.out.view(torch.int16), ref_out), f"replay {rep}: out differs"
+        assert torch.equal(d.lse.view(torch.int32), ref_lse), f"replay {rep}: lse differs"
+        del junk
