@@ -310,6 +310,96 @@ def test_mimic_lse_ignores_p_quantization():
     np.testing.assert_allclose(lm, lse, rtol=1e-12)
 
 
+@pytest.mark.parametrize("splits,chunk,limit", [(1, 64, 64), (3, 8, 1), (2, 5, 2), (4, 16, 96)])
+def test_mimic_frames_without_quantization_is_exact(splits, chunk, limit):
+    p = inputs.random_problem(20, 2, 16, 40, pool_rows=300, neg_frac=0.2, lens=[40, 23],
+                              sinks=True, value_scale=4.0)
+    out, lse = oracle.decode_exact(p)
+    om, lm = oracle.decode_mimic(p, splits=splits, chunk=chunk, quantize=False,
+                                 frame_limit=limit)
+    np.testing.assert_allclose(om, out, rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(lm, lse, rtol=1e-12)
+
+
+def test_mimic_frames_independent_of_limit():
+    """Moving the frame rescales acc and l by exact powers of two and keeps every anchor, so
+    the result does not depend on how often the frame moves (up to the rounding of the final
+    merge, whose exp2/log2 arguments shift by whole numbers)."""
+    p = inputs.random_problem(21, 2, 16, 96, pool_rows=500, neg_frac=0.1, value_scale=8.0)
+    for terms in (1, 2):
+        ref = oracle.decode_mimic(p, splits=2, chunk=8, terms=terms, frame_limit=200)
+        for limit in (1, 2, 3):
+            got = oracle.decode_mimic(p, splits=2, chunk=8, terms=terms, frame_limit=limit)
+            np.testing.assert_allclose(got[0], ref[0], rtol=1e-11, atol=1e-13)
+            np.testing.assert_allclose(got[1], ref[1], rtol=1e-13)
+
+
+def test_mimic_frames_equal_recipe_when_first_chunk_holds_the_max():
+    """If the first chunk holds the maximum score, every anchor of both variants is that
+    maximum, so frame anchoring and the recipe quantize every P identically."""
+    p = inputs.random_problem(22, 1, 1, 48, pool_rows=400)
+    rows = _e4m3_f64(p["kv_a"][p["indices"][0]]).numpy()
+    q = _e4m3_f64(p["q"][0, 0]).numpy()
+    order = np.argsort(-(rows[:, :576] @ q), kind="stable")
+    p["indices"] = np.ascontiguousarray(p["indices"][:, order])
+    for terms in (1, 2):
+        a = oracle.decode_mimic(p, splits=1, chunk=8, terms=terms, frame_limit=64)
+        b = oracle.decode_mimic(p, splits=1, chunk=8, terms=terms)
+        np.testing.assert_allclose(a[0], b[0], rtol=1e-13, atol=1e-15)
+        np.testing.assert_allclose(a[1], b[1], rtol=1e-13)
+    # reversed order: the maximum arrives last, the anchors differ and so does the rounding
+    p["indices"] = np.ascontiguousarray(p["indices"][:, ::-1])
+    a = oracle.decode_mimic(p, splits=1, chunk=8, terms=1, frame_limit=64)
+    b = oracle.decode_mimic(p, splits=1, chunk=8, terms=1)
+    assert np.abs(a[0] - b[0]).max() > 0
+    np.testing.assert_allclose(a[1], b[1], rtol=1e-12)  # the LSE uses unquantized P
+
+
+def test_mimic_frames_worked_example():
+    """Hand-worked frame anchoring (one head, chunks of one column, base-2 scores 0, 1/2 and
+    -40/3): G = 0; the second and third chunks anchor at F = G + ceil(1/2) = 1, so the third
+    column's P = 448 * 2^(-40/3 - 1) = 11.16 * 2^-9 rounds to the E4M3 value 11 * 2^-9 and
+    enters with weight 2^1.  Only the third row has latent column 100 (value 448), so
+    out[100] = bmm2 * 2 * 11 * 2^-9 * 448 / l with l = sum of 2^e * p over the columns.
+    An anchor one binade higher would round 5.58 * 2^-9 to 6 * 2^-9 (13% off)."""
+    def e4(x):
+        return int(torch.tensor([x], dtype=torch.float64).to(torch.float8_e4m3fn)
+                   .view(torch.uint8)[0])
+    q = np.zeros((1, 1, 576), np.uint8)
+    q[0, 0, 0] = e4(1.0)
+    kv = np.zeros((3, 576), np.uint8)
+    kv[1, 0] = e4(0.75)
+    kv[2, 0] = e4(-20.0)
+    kv[2, 100] = e4(448.0)
+    c = 2.0 / 3.0  # base-2 score per unit dot product
+    p = dict(q=q, kv_a=kv, kv_b=None, split_col=3, qk_dim=576,
+             indices=np.array([[0, 1, 2]], np.int32), lens=np.array([3], np.int32),
+             sinks=None, bmm1=c * LN2, bmm2=1.0)
+    out, lse = oracle.decode_mimic(p, splits=1, chunk=1, terms=1, frame_limit=64, lse_log2=True)
+    s2 = np.array([0.0, 0.5, -40.0 / 3.0])
+    e = np.array([0, 1, 1])
+    l = float(np.sum(2.0 ** e * 448.0 * 2.0 ** (s2 - e)))
+    assert abs(out[0, 100] - 2 * 11 * 2.0 ** -9 * 448.0 / l) < 1e-12
+    assert abs(lse[0] - (math.log2(l) - math.log2(448.0))) < 1e-12
+    # the recipe (anchor at the running max 1/2) rounds 448 * 2^(-40/3 - 1/2) = 15.8 * 2^-9
+    # to 16 * 2^-9 with weight 2^(1/2 - 0) folded into its rescale
+    rec, _ = oracle.decode_mimic(p, splits=1, chunk=1, terms=1)
+    assert abs(rec[0, 100] - 16 * 2.0 ** -9 * 448.0 * 2.0 ** 0.5 / l) < 1e-12
+
+
+def test_mimic_frames_accuracy_matches_recipe():
+    """Frame anchoring rounds P with the same relative precision as the recipe (E4M3's
+    precision does not depend on the binade), so both land at the same error level."""
+    p = inputs.random_problem(23, 4, 16, 256, pool_rows=2000)
+    out, _ = oracle.decode_exact(p)
+    nrm = np.linalg.norm(out)
+    for terms in (1, 2):
+        e_rec = np.linalg.norm(oracle.decode_mimic(p, 1, 64, terms=terms)[0] - out) / nrm
+        e_frm = np.linalg.norm(oracle.decode_mimic(p, 1, 64, terms=terms,
+                                                   frame_limit=64)[0] - out) / nrm
+        assert 0.5 < e_frm / e_rec < 2.0, (terms, e_rec, e_frm)
+
+
 # ---------------------------------------------------------------------------
 # lse_merge
 # ---------------------------------------------------------------------------
