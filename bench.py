@@ -119,8 +119,7 @@ def latency_configs(smla, inputs, stream, reps=200):
         out = torch.empty((T, H, 512), dtype=torch.bfloat16, device="cuda")
         lse = torch.empty((T, H), dtype=torch.float32, device="cuda")
         plan = smla.plan_for(T, H, W, p["kv_a"].shape[1])
-        nb = smla.workspace_size(plan, T, H)
-        ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda") if nb else None
+        ws = smla.new_workspace(plan, T, H)
 
         def call(i, s=stream):
             smla.sparse_mla_decode(d["q"], d["kv_a"], d["indices"], d["lens"], p["bmm1"],
@@ -202,8 +201,7 @@ def main():
     plan = smla.plan_for(T, H, W, ROW_BYTES)
     if args.splits or args.tiles:
         plan = smla.make_plan(args.splits or plan.splits, args.tiles or plan.tiles)
-    nb = smla.workspace_size(plan, T, H)
-    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda") if nb else None
+    ws = smla.new_workspace(plan, T, H)
     sets = w["index_sets"]
 
     def call(i, s=stream):

@@ -46,21 +46,23 @@ typedef int32_t smla_status;
 
 /* Flags. */
 #define SMLA_LSE_LOG2 0x1u   /* LSE outputs in base 2 (default: natural log) */
-#define SMLA_P_ONE_TERM 0x2u /* sparse_mla_decode: P as one E4M3 term, the attn_sparse page's
-                                recipe as printed.  Default: two E4M3 terms, P = hi + lo/16 with
-                                hi = E4M3(P) and lo = E4M3(16 (P - hi)), which keeps the E4M3
-                                quantization at the 448 anchor but reaches FP32-level accuracy
-                                (relative output error ~1e-3 instead of ~2e-2). */
+#define SMLA_P_ONE_TERM 0x2u /* sparse_mla_decode: P as one E4M3 term (the attn_sparse page's
+                                recipe, anchored as described under sparse_mla_decode).
+                                Default: two E4M3 terms, P = hi + lo/16 with hi = E4M3(P) and
+                                lo = E4M3(16 (P - hi)), which keeps the E4M3 quantization but
+                                reaches FP32-level accuracy (relative output error ~1e-3
+                                instead of ~2e-2). */
 
 /* The launch decomposition of one sparse_mla_decode call.  A workgroup takes one token, a
- * group of `tiles` 16-head tiles and one of `splits` contiguous ranges of the token's clamped
- * count (range s = [min(n, s*per), +min(n - first, per)), per = ceil(n / splits), as the
- * attn_sparse page's key split); the ranges run in chunks of `chunk` columns and are merged in
- * FP32 when splits > 1. */
+ * group of `tiles` 32-head tiles (heads padded up to a multiple of 32) and one of `splits`
+ * contiguous ranges of the token's clamped count (range s = [min(n, s*per), +min(n - first,
+ * per)), per = ceil(n / splits), as the attn_sparse page's key split); the ranges run in chunks
+ * of `chunk` columns and, when splits > 1, the last range of a (token, head group) to finish
+ * merges the FP32 partials of all of them. */
 typedef struct smla_plan {
-    int32_t splits; /* >= 1 */
-    int32_t tiles;  /* 16-head tiles per workgroup (one wave each): 1, 2, 4 or 8, dividing H / 16 */
-    int32_t chunk;  /* columns per gathered chunk (128 in this build; output only) */
+    int32_t splits; /* 1 .. 64 */
+    int32_t tiles;  /* 32-head tiles per workgroup: 1, 2 or 4, dividing ceil(H / 32) */
+    int32_t chunk;  /* columns per gathered chunk (64 in this build; output only) */
     int32_t reserved;
 } smla_plan;
 
@@ -70,8 +72,10 @@ typedef struct smla_plan {
 smla_status smla_decode_plan(int32_t T, int32_t H, int32_t W, int32_t row_bytes, uint32_t flags,
                              smla_plan *plan);
 
-/* Workspace bytes sparse_mla_decode needs under `plan` (0 when plan->splits == 1): FP32
- * partials [T, H, splits, 512] plus (max, sum) pairs [T, H, splits, 2].  0 for a bad plan. */
+/* Workspace bytes sparse_mla_decode needs under `plan` (0 when plan->splits == 1): arrival
+ * tickets (one int32 per token and head group, rounded up to 256 bytes), FP32 partials
+ * [T, groups, splits, 32 tiles, 512] and (frame, sum) pairs [T, groups, splits, 32 tiles, 2],
+ * groups = ceil(H / 32) / tiles.  0 for a bad plan. */
 size_t smla_decode_workspace_size(const smla_plan *plan, int32_t T, int32_t H);
 
 /*
@@ -96,10 +100,18 @@ size_t smla_decode_workspace_size(const smla_plan *plan, int32_t T, int32_t H);
  *                SMLA_LSE_LOG2); -inf for a token with no active column, whose output is +0.
  *   flags        SMLA_LSE_LOG2 | SMLA_P_ONE_TERM.
  *   plan         NULL for smla_decode_plan's, else an explicit decomposition (results are
- *                bit-identical across `tiles` for a fixed `splits`).
+ *                bit-identical across `tiles` for a fixed `splits`, and from run to run).
  *   workspace    device scratch of workspace_bytes >= smla_decode_workspace_size(plan, T, H),
- *                16-byte aligned (may be NULL when that size is 0).  Its contents on entry do
- *                not matter.  Calls that share a workspace must be stream-ordered.
+ *                16-byte aligned (may be NULL when that size is 0).  Zero-fill it once before
+ *                its first use: its first bytes hold arrival tickets that must start at zero,
+ *                and every call leaves them at zero again (the rest is overwritten before it
+ *                is read).  Calls that share a workspace must be stream-ordered.
+ *
+ * P anchoring: within a key range, the first chunk with an active column fixes the frame G
+ * (its running maximum) and each chunk quantizes P = 2^(s2 - F + log2 448) at F = G +
+ * ceil(m - G) >= m, m the running maximum, so P <= 448 as in the recipe while the chunk's
+ * products enter the FP32 accumulator with the exact weight 2^(F - G) (the matrix
+ * instruction's E8M0 block scale) instead of rescaling the accumulator.
  *
  * T == 0 is a no-op returning SMLA_OK after the size, flag and plan checks (the pointers are
  * not examined: empty tensors may have null data).  Errors: SMLA_EINVAL (null required

@@ -98,8 +98,15 @@ def workspace_size(plan: Plan, T: int, H: int) -> int:
     return int(_load().smla_decode_workspace_size(ctypes.byref(plan), T, H))
 
 
+def new_workspace(plan: Plan, T: int, H: int, device="cuda"):
+    """A zero-filled workspace for `plan` (None when the plan needs none)."""
+    import torch
+    n = workspace_size(plan, T, H)
+    return torch.zeros(n, dtype=torch.uint8, device=device) if n else None
+
+
 def make_plan(splits: int, tiles: int) -> Plan:
-    return Plan(splits, tiles, 128, 0)
+    return Plan(splits, tiles, 64, 0)
 
 
 def sparse_mla_decode(q, kv_a, indices, lens, bmm1_scale, bmm2_scale, out, lse=None, *,
@@ -111,7 +118,8 @@ def sparse_mla_decode(q, kv_a, indices, lens, bmm1_scale, bmm2_scale, out, lse=N
     kv_a / kv_b: uint8 [rows, row_bytes]; indices int32 [T, W]; lens int32 [T];
     out bf16 [T, H, 512]; lse float32 [T, H] or None; sinks float32 [H] or None.
     workspace: a uint8 device tensor of at least workspace_size(plan, T, H) bytes when the plan
-    splits the columns (None otherwise)."""
+    splits the columns (None otherwise), zero-filled before its first use (see
+    new_workspace)."""
     T, H, qd = q.shape
     W = indices.shape[1]
     row_bytes = kv_a.shape[1]

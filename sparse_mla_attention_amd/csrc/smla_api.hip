@@ -14,7 +14,8 @@ namespace {
 
 constexpr int kMaxDevices = 64;
 constexpr int kMaxSplits = 64;
-constexpr int kChunk = 128;
+constexpr int kChunk = 64;
+constexpr int kDefaultMaxSplits = 4;
 std::atomic<int> g_cu_count[kMaxDevices];
 
 // Compute units of the current device, queried once per device.
@@ -46,31 +47,25 @@ hipError_t current_cu_count(int *cus)
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
 
-// The largest tile count up to 4 (16-head tiles per workgroup) that divides the head tiles:
-// measured on MI355X, 4 tiles (4 waves, one per SIMD) beat 8 at the large-batch shape because
-// the chunk's LDS operand traffic, not the wave count, bounds a workgroup.
-int default_tiles(int32_t H)
-{
-    const int ht = H / 16;
-    for (int t = 4; t > 1; t /= 2)
-        if (ht % t == 0)
-            return t;
-    return 1;
-}
+// 32-head tiles per workgroup: 2 when the head tiles pair up (a workgroup then holds 64 heads
+// of accumulators, 128 registers per lane, and a token's head groups share its gathered rows
+// through L2), else 1.
+int32_t head_tiles(int32_t H) { return (H + 31) / 32; }
 
-// Key ranges per (token, head group): enough workgroups to cover every compute unit, with at
-// least half a chunk of columns per range on average and at most kMaxSplits ranges.
+int default_tiles(int32_t H) { return head_tiles(H) % 2 == 0 ? 2 : 1; }
+
+// Key ranges per (token, head group): enough workgroups to cover every compute unit, at least
+// one chunk of columns per range, and at most kDefaultMaxSplits ranges (the last range of a
+// (token, head group) reads every other range's partial to merge them).
 int default_splits(int32_t T, int32_t groups, int32_t W, int cus)
 {
     const int64_t units = (int64_t)T * groups;
     int64_t want = units > 0 ? (cus + units - 1) / units : 1;
-    int64_t cap = (W + kChunk / 2 - 1) / (kChunk / 2);
-    if (cap < 1)
-        cap = 1;
+    int64_t cap = (W + kChunk - 1) / kChunk;
+    if (cap > kDefaultMaxSplits)
+        cap = kDefaultMaxSplits;
     if (want > cap)
         want = cap;
-    if (want > kMaxSplits)
-        want = kMaxSplits;
     return want < 1 ? 1 : (int)want;
 }
 
@@ -78,9 +73,31 @@ bool plan_ok(const smla_plan *p, int32_t H)
 {
     if (p->splits < 1 || p->splits > kMaxSplits)
         return false;
-    if (p->tiles != 1 && p->tiles != 2 && p->tiles != 4 && p->tiles != 8)
+    if (p->tiles != 1 && p->tiles != 2 && p->tiles != 4)
         return false;
-    return (H / 16) % p->tiles == 0;
+    return head_tiles(H) % p->tiles == 0;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Workspace layout under a valid plan: tickets [T, groups] int32 (zero between calls), then
+// FP32 partials [T, groups, splits, 32 tiles, 512], then (frame, sum) [T, groups, splits,
+// 32 tiles, 2].
+struct WsLayout {
+    size_t counters, partials, ml, total;
+};
+
+WsLayout ws_layout(const smla_plan *plan, int32_t T, int32_t H)
+{
+    const size_t groups = (size_t)(head_tiles(H) / plan->tiles);
+    const size_t hg = 32 * (size_t)plan->tiles;
+    const size_t units = (size_t)T * groups * (size_t)plan->splits;
+    WsLayout w;
+    w.counters = 0;
+    w.partials = align256((size_t)T * groups * sizeof(int32_t));
+    w.ml = w.partials + units * hg * 512 * sizeof(float);
+    w.total = w.ml + units * hg * 2 * sizeof(float);
+    return w;
 }
 
 }  // namespace
@@ -112,7 +129,7 @@ smla_status smla_decode_plan(int32_t T, int32_t H, int32_t W, int32_t row_bytes,
     if (current_cu_count(&cus) != hipSuccess)
         return SMLA_EHIP;
     plan->tiles = default_tiles(H);
-    plan->splits = default_splits(T, H / 16 / plan->tiles, W, cus);
+    plan->splits = default_splits(T, head_tiles(H) / plan->tiles, W, cus);
     plan->chunk = kChunk;
     plan->reserved = 0;
     return SMLA_OK;
@@ -124,8 +141,7 @@ size_t smla_decode_workspace_size(const smla_plan *plan, int32_t T, int32_t H)
         return 0;
     if (plan->splits == 1)
         return 0;
-    const size_t units = (size_t)T * (size_t)H * (size_t)plan->splits;
-    return units * 512 * sizeof(float) + units * 2 * sizeof(float);
+    return ws_layout(plan, T, H).total;
 }
 
 smla_status sparse_mla_decode(const void *q, int64_t q_stride_t, int64_t q_stride_h,
@@ -200,13 +216,16 @@ smla_status sparse_mla_decode(const void *q, int64_t q_stride_t, int64_t q_strid
     p.lse = lse;
     p.lse_log2 = (flags & SMLA_LSE_LOG2) ? 1 : 0;
     p.splits = chosen.splits;
-    p.groups = H / 16 / chosen.tiles;
+    p.groups = head_tiles(H) / chosen.tiles;
     p.ws_o = nullptr;
     p.ws_ml = nullptr;
+    p.counters = nullptr;
     if (need > 0) {
-        const size_t units = (size_t)T * (size_t)H * (size_t)chosen.splits;
-        p.ws_o = static_cast<float *>(workspace);
-        p.ws_ml = p.ws_o + units * 512;
+        const WsLayout w = ws_layout(&chosen, T, H);
+        uint8_t *base = static_cast<uint8_t *>(workspace);
+        p.counters = reinterpret_cast<int32_t *>(base + w.counters);
+        p.ws_o = reinterpret_cast<float *>(base + w.partials);
+        p.ws_ml = reinterpret_cast<float *>(base + w.ml);
     }
     const hipError_t e = smla::launch_decode(p, chosen.tiles, row_bytes, qk_dim,
                                              (flags & SMLA_P_ONE_TERM) == 0, stream);

@@ -17,6 +17,10 @@ LN2 = math.log(2.0)
 EXACT_REL_L2 = 1e-2
 EXACT_MAX_ABS = 3e-2
 LSE_ABS = 2e-3
+# The kernel moves a range's softmax frame when the anchor offset would exceed this many
+# binades (documented with sparse_mla_decode); mimic mode models the same rule.
+FRAME_LIMIT = 64
+
 # The one-term E4M3-P path against mimic mode of the same plan: the two model the same
 # quantization points and differ only by FP32 summation order, the FP32 logits and exp2, and
 # the BF16 output rounding, which alone contributes ~1.7e-3 relative L2 (8 significant bits:
@@ -62,6 +66,19 @@ class DeviceProblem:
         self.out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=device)
         self.lse = torch.empty((T, H), dtype=torch.float32, device=device)
 
+    def workspace(self, plan):
+        """The problem's workspace for `plan`: tickets zero (they are zero between calls), the
+        rest NaN garbage, which the kernels must overwrite before reading."""
+        nbytes = smla.workspace_size(plan, self.T, self.H)
+        if not nbytes:
+            return None
+        groups = ((self.H + 31) // 32) // plan.tiles
+        tickets = (self.T * groups * 4 + 255) // 256 * 256
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=self.q.device)
+        ws[:tickets].zero_()
+        ws[tickets:].fill_(0xFF)
+        return ws
+
     def run(self, plan=None, one_term=False, lse_log2=None, poison_out=True):
         p = self.p
         if lse_log2 is None:
@@ -71,10 +88,7 @@ class DeviceProblem:
             self.lse.fill_(float("nan"))
         use = plan if plan is not None else smla.plan_for(self.T, self.H, p["indices"].shape[1],
                                                          self.kv_a.shape[1])
-        nbytes = smla.workspace_size(use, self.T, self.H)
-        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=self.q.device) if nbytes else None
-        if ws is not None:
-            ws.fill_(0xFF)  # NaN garbage: the kernels must not depend on its contents
+        ws = self.workspace(use)
         smla.sparse_mla_decode(self.q, self.kv_a, self.indices, self.lens, p["bmm1"], p["bmm2"],
                                self.out, self.lse, kv_b=self.kv_b, split_col=p["split_col"],
                                sinks=self.sinks, qk_dim=p["qk_dim"], lse_log2=lse_log2,

@@ -7,9 +7,9 @@ import torch
 import oracle
 import sparse_mla_attention_amd as smla
 from sparse_mla_attention_amd import inputs
-from smla_testlib import (EXACT_MAX_ABS, EXACT_REL_L2, LSE_ABS, MIMIC_MAX_ABS, MIMIC_REL_L2,
-                          DeviceProblem, bf16_to_f64, check_empty_rows_exact, dev, log, lse_err,
-                          rel_l2)
+from smla_testlib import (EXACT_MAX_ABS, EXACT_REL_L2, FRAME_LIMIT, LSE_ABS, MIMIC_MAX_ABS,
+                          MIMIC_REL_L2, DeviceProblem, bf16_to_f64, check_empty_rows_exact, dev,
+                          log, lse_err, rel_l2)
 
 pytestmark = pytest.mark.gpu
 
@@ -39,7 +39,7 @@ def test_config_one_term_matches_mimic(name):
     out, lse, plan = d.run(one_term=True)
     check_empty_rows_exact(d.out, d.lse, p)
     ref, ref_lse = oracle.decode_mimic(p, plan.splits, plan.chunk, terms=1,
-                                       lse_log2=p["lse_log2"])
+                                       lse_log2=p["lse_log2"], frame_limit=FRAME_LIMIT)
     if p["lse_log2"]:
         ref_lse, lse = ref_lse * LN2, lse * LN2
     r, m, le = rel_l2(out, ref), float(np.abs(out - ref).max()), lse_err(lse, ref_lse)
@@ -47,7 +47,9 @@ def test_config_one_term_matches_mimic(name):
     log(f"  {p['name']} one-term {plan}: vs mimic rel_l2={r:.3e} max_abs={m:.3e} lse={le:.3e}; "
         f"vs exact rel_l2={rel_l2(out, ex):.3e}")
     assert r <= MIMIC_REL_L2 and m <= MIMIC_MAX_ABS and le <= LSE_ABS
-    assert float(np.abs(out - ex).max()) <= EXACT_MAX_ABS
+    # against the exact formula: the recipe's own rounding (mimic vs exact) plus the tolerance
+    bound = float(np.abs(ref - ex).max()) + MIMIC_MAX_ABS
+    assert float(np.abs(out - ex).max()) <= bound
 
 
 def _throughput_units(T=64, H=128, count=48, seed=7):
@@ -67,8 +69,7 @@ def test_throughput_config_sampled_parity():
     out = torch.empty((T, H, 512), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((T, H), dtype=torch.float32, device="cuda")
     plan = smla.plan_for(T, H, W, 576)
-    nbytes = smla.workspace_size(plan, T, H)
-    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+    ws = smla.new_workspace(plan, T, H)
     idx = w["index_sets"][0]
     for one_term in (False, True):
         smla.sparse_mla_decode(w["q"], w["kv_a"], idx, w["lens"], w["bmm1"], w["bmm2"], out, lse,
@@ -82,7 +83,7 @@ def test_throughput_config_sampled_parity():
         got_lse = np.array([float(lse[t, h]) for t, h in units])
         if one_term:
             ref, ref_lse = oracle.decode_mimic(host, plan.splits, plan.chunk, terms=1,
-                                               units=units)
+                                               units=units, frame_limit=FRAME_LIMIT)
             tr, ta = MIMIC_REL_L2, MIMIC_MAX_ABS
         else:
             ref, ref_lse = oracle.decode_exact(host, units=units)

@@ -6,8 +6,9 @@ import torch
 import oracle
 import sparse_mla_attention_amd as smla
 from sparse_mla_attention_amd import inputs
-from smla_testlib import (EXACT_MAX_ABS, EXACT_REL_L2, LSE_ABS, MIMIC_MAX_ABS, MIMIC_REL_L2,
-                          DeviceProblem, check_empty_rows_exact, log, lse_err, rel_l2)
+from smla_testlib import (EXACT_MAX_ABS, EXACT_REL_L2, FRAME_LIMIT, LSE_ABS, MIMIC_MAX_ABS,
+                          MIMIC_REL_L2, DeviceProblem, check_empty_rows_exact, log, lse_err,
+                          rel_l2)
 
 pytestmark = pytest.mark.gpu
 
@@ -28,8 +29,9 @@ def _check_exact(p, out, lse, lse_log2, label):
 
 
 def _check_mimic(p, out, lse, lse_log2, plan, label):
+    """One-term path: parity with mimic mode of the same plan; returns the mimic output."""
     ref, ref_lse = oracle.decode_mimic(p, splits=plan.splits, chunk=plan.chunk, terms=1,
-                                       lse_log2=lse_log2)
+                                       lse_log2=lse_log2, frame_limit=FRAME_LIMIT)
     if lse_log2:
         ref_lse, lse = ref_lse * np.log(2), lse * np.log(2)
     r = rel_l2(out, ref)
@@ -38,6 +40,7 @@ def _check_mimic(p, out, lse, lse_log2, plan, label):
     log(f"{label} vs mimic: rel_l2={r:.3e} max_abs={m:.3e} lse={le:.3e}")
     tol_abs = MIMIC_MAX_ABS * max(1.0, p.get("value_scale", 1.0))
     assert r <= MIMIC_REL_L2 and m <= tol_abs and le <= LSE_ABS, (r, m, le)
+    return ref
 
 
 CASES = {
@@ -78,10 +81,14 @@ def test_decode_random_cases(name, one_term):
         check_empty_rows_exact(d.out, d.lse, p)
         label = f"{name} {plan} log2={lse_log2}"
         if one_term:
-            _check_mimic(p, out, lse, lse_log2, plan, label)
-            ref, ref_lse = oracle.decode_exact(p, lse_log2=False)
+            mim = _check_mimic(p, out, lse, lse_log2, plan, label)
+            # against the exact formula, the one-term path may deviate by the recipe's own
+            # E4M3 rounding of P (mimic vs exact) plus the kernel-vs-mimic tolerance
+            ref, _ = oracle.decode_exact(p, lse_log2=False)
             m = float(np.abs(out - ref).max())
-            assert m <= EXACT_MAX_ABS * max(1.0, p.get("value_scale", 1.0)), m
+            bound = (float(np.abs(mim - ref).max()) +
+                     MIMIC_MAX_ABS * max(1.0, p.get("value_scale", 1.0)))
+            assert m <= bound, (m, bound)
         else:
             _check_exact(p, out, lse, lse_log2, label)
 
@@ -94,7 +101,7 @@ def test_decode_split_plans(splits):
                               lens=np.array([300, 40, 0]), neg_frac=0.1, sinks=True)
     d = DeviceProblem(p)
     for one_term in (False, True):
-        plan = smla.make_plan(splits, 2)
+        plan = smla.make_plan(splits, 1)
         out, lse, _ = d.run(plan=plan, one_term=one_term)
         check_empty_rows_exact(d.out, d.lse, p)
         if one_term:
@@ -107,13 +114,14 @@ def test_decode_split_plans(splits):
 def test_tile_grouping_is_bit_identical(one_term):
     """The attn_sparse page claims its wide-CTA variant matches the one-tile kernel bit for bit;
     here a workgroup's tile count changes only which waves share a gathered chunk, so results
-    at a fixed split plan must be bit-identical across 1, 2, 4 and 8 tiles per workgroup."""
+    at a fixed split plan must be bit-identical across 1, 2 and 4 32-head tiles per
+    workgroup."""
     p = inputs.random_problem(300, 3, 128, 333, pool_rows=4000, lens=np.array([333, 200, 1]),
                               neg_frac=0.1, sinks=True)
     d = DeviceProblem(p)
     for splits in (1, 3):
         ref_bits = ref_lse = None
-        for tiles in (1, 2, 4, 8):
+        for tiles in (1, 2, 4):
             d.run(plan=smla.make_plan(splits, tiles), one_term=one_term)
             bits = d.out.view(torch.int16).cpu().clone()
             lb = d.lse.cpu().view(torch.int32).clone()
@@ -133,14 +141,26 @@ def test_padded_q_strides():
 
 
 def test_repeated_calls_are_deterministic():
-    p = inputs.random_problem(401, 4, 32, 500, pool_rows=6000, neg_frac=0.1)
+    """Split ranges finish in any order; the merge sums them in range order, so repeated
+    calls on one workspace (whose tickets each call leaves at zero) agree bit for bit."""
+    p = inputs.random_problem(401, 4, 64, 500, pool_rows=6000, neg_frac=0.1)
     d = DeviceProblem(p)
     plan = smla.make_plan(3, 2)
-    d.run(plan=plan)
+    ws = d.workspace(plan)
+    tickets = (d.T * 1 * 4 + 255) // 256 * 256  # 64 heads: one group of two 32-head tiles
+
+    def call():
+        smla.sparse_mla_decode(d.q, d.kv_a, d.indices, d.lens, p["bmm1"], p["bmm2"], d.out,
+                               d.lse, plan=plan, workspace=ws)
+        torch.cuda.synchronize()
+    call()
     a = d.out.view(torch.int16).cpu().clone()
-    for _ in range(3):
-        d.run(plan=plan)
+    for _ in range(5):
+        call()
         assert torch.equal(d.out.view(torch.int16).cpu(), a)
+        assert int(ws[:tickets].count_nonzero()) == 0, "tickets not reset"
+    out, lse, _ = d.run(plan=plan)
+    _check_exact(p, out, lse, False, "repeated calls")
 
 
 def test_t0_is_a_noop():
@@ -169,17 +189,17 @@ def test_invalid_arguments_are_rejected():
 
 
 def test_graph_replay_matches_eager():
-    """Calls captured in a HIP graph (split plan: decode + merge kernels, workspace reused)
+    """Calls captured in a HIP graph (split plan with the fused merge, workspace reused)
     replay to the eager result, bit for bit, on every replay, with unrelated eager work and
     synchronizations between replays."""
     p = inputs.random_problem(404, 3, 32, 300, pool_rows=4000, neg_frac=0.1, sinks=True,
                               lens=np.array([300, 0, 177]))
     d = DeviceProblem(p)
-    plan = smla.make_plan(3, 2)
+    plan = smla.make_plan(3, 1)
     d.run(plan=plan, poison_out=False)
     ref_out = d.out.view(torch.int16).clone()
     ref_lse = d.lse.view(torch.int32).clone()
-    ws = torch.empty(smla.workspace_size(plan, d.T, d.H), dtype=torch.uint8, device="cuda")
+    ws = d.workspace(plan)
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
 
