@@ -135,8 +135,9 @@ def decode_exact(p, lse_log2=False, units=None):
 def decode_mimic(p, splits, chunk, anchor=448.0, terms=1, quantize=True, lse_log2=False,
                  units=None, frame_limit=0):
     """Mimic mode (the E4M3-P recipe with the given split count and chunk size).
-    frame_limit > 0: frame anchoring (P anchored at G + ceil(m - G), the frame G moving
-    only when that offset exceeds frame_limit); 0: the recipe's exact running-max anchor."""
+    frame_limit > 0: frame anchoring (P anchored at G + ceil(m - G); a range whose offset
+    exceeds frame_limit reruns with G preset to its maximum); 0: the recipe's exact
+    running-max anchor."""
     args, keep, T, H = _problem_args(p)
     u, n = _units_array(units)
     count = n if u is not None else T * H

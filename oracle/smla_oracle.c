@@ -196,6 +196,7 @@ static int check_problem(const problem *p)
 }
 
 #define V_DIM 512 /* V is the first 512 bytes of a row on every page */
+#define E_FLOOR (-120.0) /* frame mode: smallest offset e of a second pass */
 
 /* ---------------------------------------------------------------------------
  * C1: exact mode, the formula of the sparse_mla_cute page, with the LSE
@@ -304,9 +305,12 @@ int oracle_decode_exact(
  * running max after the first chunk that has one, each later chunk anchors P
  * at F = G + e with e = ceil(m_new - G), so P <= anchor still holds; the
  * chunk's p_hat v and p enter acc and l in frame G with weight 2^e, and acc and
- * l are never rescaled, except when e > frame_limit: then both are multiplied
- * by 2^-e and G moves to G + e.  The range reports m = G.  A single chunk gives
- * e = 0, i.e. the recipe itself; without quantization it is exact mode.
+ * l are never rescaled.  If some chunk's e exceeds frame_limit (the scores grew
+ * by that many binades), the range is run a second time with G fixed in advance
+ * at the range's maximum: then e = ceil(m_new - G) <= 0, raised to E_FLOOR when
+ * lower (P <= anchor still holds), and 0 while the range has no active column.
+ * The range reports m = G.  A single chunk gives e = 0, i.e. the recipe itself;
+ * without quantization either pass is exact mode.
  * ------------------------------------------------------------------------- */
 int oracle_decode_mimic(
     const uint8_t *q, int64_t q_stride_t, int64_t q_stride_h,
@@ -357,7 +361,10 @@ int oracle_decode_mimic(
             int mine = n - first < per ? n - first : per;
             double m_run = -INFINITY, l_run = 0.0;
             double frame = -INFINITY; /* frame mode: the base G of acc and l_run */
+            int preset = 0;           /* frame mode, second pass: G fixed in advance */
+            double e_max = 0.0;       /* frame mode: largest offset e of the pass */
             double *acc = acc_s + (int64_t)s * V_DIM;
+        range_pass:
             for (int j = 0; j < V_DIM; j++)
                 acc[j] = 0.0;
             for (int base = first; base < first + mine && status == ORACLE_OK; base += chunk) {
@@ -387,15 +394,12 @@ int oracle_decode_mimic(
                     double e = 0.0;
                     if (frame == -INFINITY)
                         frame = m_new; /* first chunk with an active column (or still -inf) */
-                    else
+                    else if (m_new != -INFINITY)
                         e = ceil(m_new - frame);
-                    if (e > frame_limit) {
-                        for (int j = 0; j < V_DIM; j++)
-                            acc[j] = ldexp(acc[j], -(int)e);
-                        l_run = ldexp(l_run, -(int)e);
-                        frame += e;
-                        e = 0.0;
-                    }
+                    if (preset && e < E_FLOOR)
+                        e = E_FLOOR;
+                    if (e > e_max)
+                        e_max = e;
                     alpha = ldexp(1.0, (int)e); /* weight of this chunk's terms in frame G */
                     bias = (frame == -INFINITY) ? 0.0 : frame + e - log2(anchor);
                 } else {
@@ -433,6 +437,15 @@ int oracle_decode_mimic(
                         acc[j] += w * oracle_e4m3_value(row[j]);
                 }
                 m_run = m_new;
+            }
+            if (status == ORACLE_OK && frame_limit > 0 && !preset && e_max > frame_limit) {
+                /* second pass: G = the range's maximum, known now */
+                preset = 1;
+                frame = m_run;
+                m_run = -INFINITY;
+                l_run = 0.0;
+                e_max = 0.0;
+                goto range_pass;
             }
             m_s[s] = frame_limit > 0 ? frame : m_run;
             l_s[s] = l_run;

@@ -321,17 +321,61 @@ def test_mimic_frames_without_quantization_is_exact(splits, chunk, limit):
     np.testing.assert_allclose(lm, lse, rtol=1e-12)
 
 
-def test_mimic_frames_independent_of_limit():
-    """Moving the frame rescales acc and l by exact powers of two and keeps every anchor, so
-    the result does not depend on how often the frame moves (up to the rounding of the final
-    merge, whose exp2/log2 arguments shift by whole numbers)."""
-    p = inputs.random_problem(21, 2, 16, 96, pool_rows=500, neg_frac=0.1, value_scale=8.0)
-    for terms in (1, 2):
-        ref = oracle.decode_mimic(p, splits=2, chunk=8, terms=terms, frame_limit=200)
-        for limit in (1, 2, 3):
-            got = oracle.decode_mimic(p, splits=2, chunk=8, terms=terms, frame_limit=limit)
-            np.testing.assert_allclose(got[0], ref[0], rtol=1e-11, atol=1e-13)
-            np.testing.assert_allclose(got[1], ref[1], rtol=1e-13)
+def _frame_problem(dots, marker_row, marker_col, c=2.0 / 3.0):
+    """One head, q = e_0, row r = dots[r] at column 0 (and 448 at marker_col of marker_row):
+    base-2 score of row r = c * dots[r]."""
+    def e4(x):
+        return int(torch.tensor([x], dtype=torch.float64).to(torch.float8_e4m3fn)
+                   .view(torch.uint8)[0])
+    n = len(dots)
+    q = np.zeros((1, 1, 576), np.uint8)
+    q[0, 0, 0] = e4(1.0)
+    kv = np.zeros((n, 576), np.uint8)
+    for r, x in enumerate(dots):
+        assert float(torch.tensor([x]).to(torch.float8_e4m3fn).to(torch.float64)[0]) == x
+        kv[r, 0] = e4(x)
+    kv[marker_row, marker_col] = e4(448.0)
+    return dict(q=q, kv_a=kv, kv_b=None, split_col=n, qk_dim=576,
+                indices=np.arange(n, dtype=np.int32)[None], lens=np.array([n], np.int32),
+                sinks=None, bmm1=c * LN2, bmm2=1.0)
+
+
+def test_mimic_frames_second_pass_worked_example():
+    """Hand-worked second pass (chunks of one column, base-2 scores 0, 3/2, -40/3; only the
+    last row has latent column 100 = 448).  The first pass sets G = 0 and the second chunk's
+    offset is ceil(3/2) = 2.  Limit 2: no second pass; the third column's P = 448 * 2^(-40/3
+    - 2) = 5.55 * 2^-9 rounds to 6 * 2^-9 (E4M3 subnormal step) with weight 2^2.  Limit 1:
+    the range reruns with G = 3/2: offsets -1, 0, 0, P = 448 * 2^-1/2 -> 320 (weight 1/2),
+    448, and 448 * 2^(-40/3 - 3/2) = 7.86 * 2^-9 -> 8 * 2^-9 (weight 1).  Both passes give the
+    same l in their frames, so the LSE agrees."""
+    p = _frame_problem([0.0, 2.25, -20.0], 2, 100)
+    s2 = np.array([0.0, 1.5, -40.0 / 3.0])
+    o2, l2 = oracle.decode_mimic(p, splits=1, chunk=1, terms=1, frame_limit=2, lse_log2=True)
+    lf = 448.0 * (1.0 + 2.0 ** 1.5 + 2.0 ** s2[2])           # frame G = 0
+    assert abs(o2[0, 100] - 4 * 6 * 2.0 ** -9 * 448.0 / lf) < 1e-12
+    # column 0: rows 1 and 2 (values 2.25 and -20) with P 320 (weight 4) and 6 * 2^-9 (4)
+    assert abs(o2[0, 0] - 4 * (320 * 2.25 - 6 * 2.0 ** -9 * 20) / lf) < 1e-12
+    o1, l1 = oracle.decode_mimic(p, splits=1, chunk=1, terms=1, frame_limit=1, lse_log2=True)
+    lg = 448.0 * (2.0 ** -1.5 + 1.0 + 2.0 ** (s2[2] - 1.5))  # frame G = 3/2
+    assert abs(o1[0, 100] - 8 * 2.0 ** -9 * 448.0 / lg) < 1e-12
+    assert abs(o1[0, 0] - (448 * 2.25 - 8 * 2.0 ** -9 * 20) / lg) < 1e-12
+    assert abs(l1[0] - (1.5 + math.log2(lg) - math.log2(448.0))) < 1e-12
+    assert abs(l1[0] - l2[0]) < 1e-12
+
+
+def test_mimic_frames_second_pass_floor():
+    """The second pass raises offsets below -120 to -120: with base-2 scores 0 and 149.33 (G =
+    149.33), the first column's P = 448 * 2^(0 - 149.33 + 120) = 7e-7 rounds to E4M3 zero, so
+    its marker column (200, first row) is exactly 0, while the unquantized sum (and so the LSE)
+    still holds it; without the floor P would be 352 at weight 2^-149."""
+    p = _frame_problem([0.0, 224.0], 0, 200)
+    s_top = 224.0 * 2.0 / 3.0
+    out, lse = oracle.decode_mimic(p, splits=1, chunk=1, terms=1, frame_limit=1, lse_log2=True)
+    assert out[0, 200] == 0.0
+    assert abs(out[0, 0] - 224.0 / (1.0 + 2.0 ** -s_top)) < 1e-12 * 224.0
+    assert abs(lse[0] - (s_top + math.log2(1.0 + 2.0 ** -s_top))) < 1e-12
+    ex, _ = oracle.decode_exact(p, lse_log2=True)
+    assert ex[0, 200] > 0.0
 
 
 def test_mimic_frames_equal_recipe_when_first_chunk_holds_the_max():
@@ -343,13 +387,13 @@ def test_mimic_frames_equal_recipe_when_first_chunk_holds_the_max():
     order = np.argsort(-(rows[:, :576] @ q), kind="stable")
     p["indices"] = np.ascontiguousarray(p["indices"][:, order])
     for terms in (1, 2):
-        a = oracle.decode_mimic(p, splits=1, chunk=8, terms=terms, frame_limit=64)
+        a = oracle.decode_mimic(p, splits=1, chunk=8, terms=terms, frame_limit=96)
         b = oracle.decode_mimic(p, splits=1, chunk=8, terms=terms)
         np.testing.assert_allclose(a[0], b[0], rtol=1e-13, atol=1e-15)
         np.testing.assert_allclose(a[1], b[1], rtol=1e-13)
     # reversed order: the maximum arrives last, the anchors differ and so does the rounding
     p["indices"] = np.ascontiguousarray(p["indices"][:, ::-1])
-    a = oracle.decode_mimic(p, splits=1, chunk=8, terms=1, frame_limit=64)
+    a = oracle.decode_mimic(p, splits=1, chunk=8, terms=1, frame_limit=96)
     b = oracle.decode_mimic(p, splits=1, chunk=8, terms=1)
     assert np.abs(a[0] - b[0]).max() > 0
     np.testing.assert_allclose(a[1], b[1], rtol=1e-12)  # the LSE uses unquantized P
@@ -375,7 +419,7 @@ def test_mimic_frames_worked_example():
     p = dict(q=q, kv_a=kv, kv_b=None, split_col=3, qk_dim=576,
              indices=np.array([[0, 1, 2]], np.int32), lens=np.array([3], np.int32),
              sinks=None, bmm1=c * LN2, bmm2=1.0)
-    out, lse = oracle.decode_mimic(p, splits=1, chunk=1, terms=1, frame_limit=64, lse_log2=True)
+    out, lse = oracle.decode_mimic(p, splits=1, chunk=1, terms=1, frame_limit=96, lse_log2=True)
     s2 = np.array([0.0, 0.5, -40.0 / 3.0])
     e = np.array([0, 1, 1])
     l = float(np.sum(2.0 ** e * 448.0 * 2.0 ** (s2 - e)))
@@ -396,8 +440,13 @@ def test_mimic_frames_accuracy_matches_recipe():
     for terms in (1, 2):
         e_rec = np.linalg.norm(oracle.decode_mimic(p, 1, 64, terms=terms)[0] - out) / nrm
         e_frm = np.linalg.norm(oracle.decode_mimic(p, 1, 64, terms=terms,
-                                                   frame_limit=64)[0] - out) / nrm
+                                                   frame_limit=96)[0] - out) / nrm
         assert 0.5 < e_frm / e_rec < 2.0, (terms, e_rec, e_frm)
+        # limit 1: most ranges rerun with a preset frame, at the same error level
+        e_two = np.linalg.norm(oracle.decode_mimic(p, 1, 8, terms=terms,
+                                                   frame_limit=1)[0] - out) / nrm
+        e_r8 = np.linalg.norm(oracle.decode_mimic(p, 1, 8, terms=terms)[0] - out) / nrm
+        assert 0.5 < e_two / e_r8 < 2.0, (terms, e_r8, e_two)
 
 
 # ---------------------------------------------------------------------------
