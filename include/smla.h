@@ -61,7 +61,7 @@ typedef int32_t smla_status;
  * merges the FP32 partials of all of them. */
 typedef struct smla_plan {
     int32_t splits; /* 1 .. 64 */
-    int32_t tiles;  /* 32-head tiles per workgroup: 1, 2 or 4, dividing ceil(H / 32) */
+    int32_t tiles;  /* 32-head tiles per workgroup: 1 in this build */
     int32_t chunk;  /* columns per gathered chunk (64 in this build; output only) */
     int32_t reserved;
 } smla_plan;
@@ -100,7 +100,7 @@ size_t smla_decode_workspace_size(const smla_plan *plan, int32_t T, int32_t H);
  *                SMLA_LSE_LOG2); -inf for a token with no active column, whose output is +0.
  *   flags        SMLA_LSE_LOG2 | SMLA_P_ONE_TERM.
  *   plan         NULL for smla_decode_plan's, else an explicit decomposition (results are
- *                bit-identical across `tiles` for a fixed `splits`, and from run to run).
+ *                bit-identical from run to run for a fixed plan).
  *   workspace    device scratch of workspace_bytes >= smla_decode_workspace_size(plan, T, H),
  *                16-byte aligned (may be NULL when that size is 0).  Zero-fill it once before
  *                its first use: its first bytes hold arrival tickets that must start at zero,
@@ -111,7 +111,11 @@ size_t smla_decode_workspace_size(const smla_plan *plan, int32_t T, int32_t H);
  * (its running maximum) and each chunk quantizes P = 2^(s2 - F + log2 448) at F = G +
  * ceil(m - G) >= m, m the running maximum, so P <= 448 as in the recipe while the chunk's
  * products enter the FP32 accumulator with the exact weight 2^(F - G) (the matrix
- * instruction's E8M0 block scale) instead of rescaling the accumulator.
+ * instruction's E8M0 block scale) instead of rescaling the accumulator.  If some head's
+ * offset F - G would exceed 96 (scores that rise by more than 96 binades within a range),
+ * the workgroup computes its range a second time with that head's G preset to the head's
+ * maximum over the range (offsets F - G <= 0, floored at -120), so no accumulator is ever
+ * rescaled.
  *
  * T == 0 is a no-op returning SMLA_OK after the size, flag and plan checks (the pointers are
  * not examined: empty tensors may have null data).  Errors: SMLA_EINVAL (null required

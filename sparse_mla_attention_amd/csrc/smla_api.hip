@@ -47,12 +47,11 @@ hipError_t current_cu_count(int *cus)
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
 
-// 32-head tiles per workgroup: 2 when the head tiles pair up (a workgroup then holds 64 heads
-// of accumulators, 128 registers per lane, and a token's head groups share its gathered rows
-// through L2), else 1.
 int32_t head_tiles(int32_t H) { return (H + 31) / 32; }
 
-int default_tiles(int32_t H) { return head_tiles(H) % 2 == 0 ? 2 : 1; }
+// 32-head tiles per workgroup: one in this build (a workgroup's LDS holds four chunk slots of
+// rows and the P buffers of 32 heads).
+int default_tiles(int32_t) { return 1; }
 
 // Key ranges per (token, head group): enough workgroups to cover every compute unit, at least
 // one chunk of columns per range, and at most kDefaultMaxSplits ranges (the last range of a
@@ -73,7 +72,7 @@ bool plan_ok(const smla_plan *p, int32_t H)
 {
     if (p->splits < 1 || p->splits > kMaxSplits)
         return false;
-    if (p->tiles != 1 && p->tiles != 2 && p->tiles != 4)
+    if (p->tiles != 1)
         return false;
     return head_tiles(H) % p->tiles == 0;
 }

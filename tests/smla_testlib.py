@@ -17,9 +17,9 @@ LN2 = math.log(2.0)
 EXACT_REL_L2 = 1e-2
 EXACT_MAX_ABS = 3e-2
 LSE_ABS = 2e-3
-# The kernel moves a range's softmax frame when the anchor offset would exceed this many
+# The kernel reruns a range with a preset softmax frame when an anchor offset exceeds this many
 # binades (documented with sparse_mla_decode); mimic mode models the same rule.
-FRAME_LIMIT = 64
+FRAME_LIMIT = 96
 
 # The one-term E4M3-P path against mimic mode of the same plan: the two model the same
 # quantization points and differ only by FP32 summation order, the FP32 logits and exp2, and
