@@ -157,6 +157,17 @@ __device__ inline void mfma_result_pad()
     __builtin_amdgcn_sched_barrier(0);
 }
 
+// Workgroup barrier that orders LDS only.  __syncthreads() is a workgroup fence over all
+// memory, which makes every wave wait for its outstanding global loads before the barrier: the
+// gather's loads in flight across iterations would be drained at every chunk.  The gathered
+// rows reach LDS through registers, whose loads the compiler waits for before the LDS store.
+__device__ inline void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Device-scope (all XCDs) relaxed accesses of the split exchange: coherent without a fence
 __device__ inline void store_device(float *p, float v)
 {
@@ -269,8 +280,11 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(DecodeParams a)
         return g_row * RB + 16 * ((4 * k + g_q) ^ Gm::sw(g_row));
     };
     v4i stage_a[GI], stage_b[GI];  // register stages: chunk x lives in stage (x even ? a : b)
-    auto gather_load = [&](int x, v4i(&stage)[GI]) {
-        const uint8_t *row = row_tab[(x % RING) * CHUNK + g_row];
+    // Loads are issued for every chunk slot of the pipeline, reading the zero row past the
+    // range, so that the number of loads in flight is the same on every path and the compiler's
+    // wait counts stay partial (a conditional load makes it wait for every load in flight).
+    auto gather_load = [&](int x, bool live, v4i(&stage)[GI]) {
+        const uint8_t *row = live ? row_tab[(x % RING) * CHUNK + g_row] : g_zero_row;
 #pragma unroll
         for (int k = 0; k < GI; k++)
             // global (not flat) loads: flat loads would also hold the LDS counter, and every
@@ -481,28 +495,21 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(DecodeParams a)
         if (tid < 32)
             reinterpret_cast<int *>(lds + L::ESC)[32 + tid] = 127;
     }
-    __syncthreads();
-    int raw_next = -1;
-    if (nch > 0) {
-        gather_load(0, stage_a);
-        gather_store(0, stage_a);
-        if (1 < nch)
-            gather_load(1, stage_b);
-        if (2 < nch)
-            gather_load(2, stage_a);
-        if (wave == 0 && 3 < nch)
-            raw_next = load_raw(3);
-    }
-    __syncthreads();
+    lds_barrier();
+    gather_load(0, 0 < nch, stage_a);
+    gather_store(0, stage_a);
+    gather_load(1, 1 < nch, stage_b);
+    int raw = load_raw(3);
+    gather_load(2, 2 < nch, stage_a);
+    lds_barrier();
     if (nch > 0 && qk_wave) {
         s_cur = qk(0, &mloc_cur);
         if (u == 0)
             reinterpret_cast<float *>(lds + L::MX)[kt * 32 + hl] = mloc_cur;
     }
-    if (1 < nch)
-        gather_store(1, stage_b);
+    gather_store(1, stage_b);
     if (wave == 0 && 3 < nch)
-        build(3, raw_next);
+        build(3, raw);
 
     // ---- main loop: iteration c runs QK(c+1), softmax(c), P.V(c-1) --------------------------
     // On entry to iteration c: chunks c and c+1 are in their slots, chunk c+2 is in flight in
@@ -511,12 +518,9 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(DecodeParams a)
     // c+3 into stage `ld`, stores chunk c+2 into slot (c+2) % 4 (which held chunk c-2, done) and
     // builds the table of chunk c+4.
     auto iteration = [&](int c, v4i(&st)[GI], v4i(&ld)[GI]) __attribute__((always_inline)) {
-        __syncthreads();
-        raw_next = -1;
-        if (wave == 0 && c + 4 < nch)
-            raw_next = load_raw(c + 4);
-        if (c + 3 < nch)
-            gather_load(c + 3, ld);
+        lds_barrier();
+        raw = load_raw(c + 4);  // every wave (fixed load count); wave 0 builds the table
+        gather_load(c + 3, c + 3 < nch, ld);
         if (qk_wave) {
             float mloc_next;
             const v16f s_next = qk(c + 1, &mloc_next);  // stale slot when c+1 == nch: unused
@@ -529,10 +533,9 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(DecodeParams a)
         } else {
             pv(c - 1);
         }
-        if (c + 2 < nch)
-            gather_store(c + 2, st);
+        gather_store(c + 2, st);  // past the range: zero rows into a slot no chunk reads
         if (wave == 0 && c + 4 < nch)
-            build(c + 4, raw_next);
+            build(c + 4, raw);
     };
     for (int c = 0; c < nch; c += 2) {
         iteration(c, stage_a, stage_b);
@@ -541,7 +544,7 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(DecodeParams a)
     }
     // drain: P.V of the last chunk
     if (nch > 0) {
-        __syncthreads();
+        lds_barrier();
         if (!qk_wave)
             pv(nch - 1);
     }
@@ -553,10 +556,10 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(DecodeParams a)
     run_range();
     // second pass for the heads whose offset overflowed (rare): restart the range with their
     // frames fixed at their final maxima
-    __syncthreads();
+    lds_barrier();
     if (qk_wave && __any(overflow) && lane == 0)
         *flag = 1;
-    __syncthreads();
+    lds_barrier();
     if (*flag != 0) {
         if (qk_wave) {
             preset = overflow;
@@ -570,13 +573,13 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(DecodeParams a)
             for (int ct = 0; ct < NCT; ct++)
                 acc[ct] = v16f{};
         }
-        __syncthreads();
+        lds_barrier();
         run_range();
     }
 
     // ---- epilogue ---------------------------------------------------------------------------
     float *fin = reinterpret_cast<float *>(lds + L::FIN);  // [l kt0][l kt1][G][e int] x 32
-    __syncthreads();
+    lds_barrier();
     if (qk_wave) {
         const float lt = l_lane + __shfl_xor(l_lane, 32);
         if (u == 0)
@@ -586,7 +589,7 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(DecodeParams a)
             reinterpret_cast<int *>(fin)[3 * HG + hl] = ecur;
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // this lane's head: frame G and the sum l in frame G
     float g_h = fin[2 * HG + hl];
@@ -620,7 +623,7 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(DecodeParams a)
         if (tid == 0)
             *ticket = __hip_atomic_fetch_add(a.counters + tg, 1, __ATOMIC_RELAXED,
                                              __HIP_MEMORY_SCOPE_AGENT);
-        __syncthreads();
+        lds_barrier();
         if (*ticket != a.splits - 1)
             return;
         // last range: merge every range's partial in range order (its own included, read back
@@ -685,7 +688,7 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(DecodeParams a)
             a.lse[(int64_t)t * a.H + head] = a.lse_log2 ? lse2 : lse2 * LN2;
         }
     }
-    __syncthreads();
+    lds_barrier();
     const int heads_here = min(HG, a.H - hg * HG);
     for (int x = tid; x < heads_here * 64; x += NT) {
         const int row = x >> 6, part = x & 63;
