@@ -65,7 +65,7 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 constexpr int CHUNK = 64;                          // columns per chunk
 constexpr int NT = 512;                            // threads per workgroup (8 waves)
 constexpr int HG = 32;                             // heads per workgroup
-constexpr int VSLOTS = 4;                          // V slots in LDS: chunks c-1 .. c+2
+constexpr int VSLOTS = 3;                          // V slots in LDS: chunks c-1 .. c+1
 constexpr int NCT = 4;                             // 32-column P.V tiles per O wave
 constexpr float ANCHOR = 448.0f;                   // P anchor: E4M3's largest finite value
 constexpr float LOG2_ANCHOR = 8.807354922057604f;  // log2(448)
@@ -81,13 +81,16 @@ __device__ __attribute__((aligned(16))) uint8_t g_zero_row[576];
 struct Lds {
     static constexpr int VSLOT = CHUNK * 512;                  // latent bytes of one chunk
     static constexpr int V = 0;                                // [VSLOTS][64 keys][512]
-    static constexpr int P = VSLOTS * VSLOT;                   // [2 buf][2 term][32][64]
+    static constexpr int SC = VSLOTS * VSLOT;                  // [2 buf][4 waves][64 lanes][8]
+    static constexpr int P = SC + 2 * 4 * 64 * 8 * 4;          // [2 buf][2 term][32][64]
     static constexpr int PTERM = HG * 64;
     static constexpr int PBUF = 2 * PTERM;
     static constexpr int ESC = P + 2 * PBUF;                   // [2 buf][32] int: E8M0 byte
     static constexpr int MX = ESC + 2 * HG * 4;                // [2 buf][32 heads][4 S waves]
     static constexpr int FIN = MX + 2 * HG * 4 * 4;            // [4 S waves][32] l, G, e
-    static constexpr int MISC = FIN + 6 * HG * 4;              // ticket, overflow flag
+    static constexpr int IDX = FIN + 6 * HG * 4;               // [4 chunks][64] int indices
+    static constexpr int QR = IDX + 4 * CHUNK * 4;             // [4 S waves][32][64] q rope
+    static constexpr int MISC = QR + 4 * HG * 64;              // ticket, overflow flag
     static constexpr int TOTAL = MISC + 16;
     static constexpr int OUT_TILE = HG * 1024;                 // BF16 [32][512], after the loop
     static_assert(OUT_TILE <= P, "output tile must fit in the V slots");
@@ -98,6 +101,9 @@ struct Lds {
 // a 32-byte column pair on eight distinct bank groups (the transposed reads of P.V) and
 // sixteen consecutive keys put one piece on sixteen (the S waves' row writes).
 __device__ inline int vsw(int key) { return ((key & 7) << 1) | ((key >> 3) & 1); }
+
+// V slot of chunk x (x >= -1).
+__device__ inline int vslot(int x) { return (x + VSLOTS) % VSLOTS; }
 
 // XOR on the 16-byte piece index of head h's 64-byte P row.
 __device__ inline int psw(int h) { return (h >> 2) & 3; }
@@ -118,6 +124,64 @@ template <typename T>
 __device__ inline T lds_load(const uint8_t *base, int off)
 {
     return *reinterpret_cast<const T *>(base + off);
+}
+
+// Row loads of the QK waves, issued from inline assembly so that the compiler's wait counting
+// does not see them: with the three register stages rotating through an unrolled loop it made
+// every trip wait for nearly every load in flight.  The kernel waits for them itself with
+// counts that follow from the fixed issue order (NLD loads per chunk, nothing else).  The stage
+// registers are operands of those waits, so no use of a stage is scheduled before its wait;
+// the registers of a stage are never copied or reused while its loads are in flight (values
+// that the compiler could copy, such as the row indices, are not loaded this way).
+
+__device__ inline void gload_row_async(v4i (&st)[9], const uint8_t *row)
+{
+    asm volatile("global_load_dwordx4 %0, %9, off\n\t"
+                 "global_load_dwordx4 %1, %9, off offset:64\n\t"
+                 "global_load_dwordx4 %2, %9, off offset:128\n\t"
+                 "global_load_dwordx4 %3, %9, off offset:192\n\t"
+                 "global_load_dwordx4 %4, %9, off offset:256\n\t"
+                 "global_load_dwordx4 %5, %9, off offset:320\n\t"
+                 "global_load_dwordx4 %6, %9, off offset:384\n\t"
+                 "global_load_dwordx4 %7, %9, off offset:448\n\t"
+                 "global_load_dwordx4 %8, %9, off offset:512"
+                 : "=&v"(st[0]), "=&v"(st[1]), "=&v"(st[2]), "=&v"(st[3]), "=&v"(st[4]),
+                   "=&v"(st[5]), "=&v"(st[6]), "=&v"(st[7]), "=&v"(st[8])
+                 : "v"(row));
+}
+
+__device__ inline void gload_row_async(v4i (&st)[8], const uint8_t *row)
+{
+    asm volatile("global_load_dwordx4 %0, %8, off\n\t"
+                 "global_load_dwordx4 %1, %8, off offset:64\n\t"
+                 "global_load_dwordx4 %2, %8, off offset:128\n\t"
+                 "global_load_dwordx4 %3, %8, off offset:192\n\t"
+                 "global_load_dwordx4 %4, %8, off offset:256\n\t"
+                 "global_load_dwordx4 %5, %8, off offset:320\n\t"
+                 "global_load_dwordx4 %6, %8, off offset:384\n\t"
+                 "global_load_dwordx4 %7, %8, off offset:448"
+                 : "=&v"(st[0]), "=&v"(st[1]), "=&v"(st[2]), "=&v"(st[3]), "=&v"(st[4]),
+                   "=&v"(st[5]), "=&v"(st[6]), "=&v"(st[7])
+                 : "v"(row));
+}
+
+// Wait until at most N vector memory loads are in flight; `x` is live across the wait.
+template <int N>
+__device__ inline void wait_vm(v4i (&st)[9])
+{
+    asm volatile("s_waitcnt vmcnt(%9)"
+                 : "+v"(st[0]), "+v"(st[1]), "+v"(st[2]), "+v"(st[3]), "+v"(st[4]),
+                   "+v"(st[5]), "+v"(st[6]), "+v"(st[7]), "+v"(st[8])
+                 : "i"(N));
+}
+
+template <int N>
+__device__ inline void wait_vm(v4i (&st)[8])
+{
+    asm volatile("s_waitcnt vmcnt(%8)"
+                 : "+v"(st[0]), "+v"(st[1]), "+v"(st[2]), "+v"(st[3]), "+v"(st[4]),
+                   "+v"(st[5]), "+v"(st[6]), "+v"(st[7])
+                 : "i"(N));
 }
 
 // 16x16x128 FP8, unit scales (QK).
@@ -348,10 +412,11 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(DecodeParams a)
         const int key = 16 * w + r;                // this lane's key within a chunk
 
         // Q fragments, B operand of QK: lane (n, g) holds, for head 16 ht + n and step s, the
-        // q pieces 8 s + g and 8 s + 4 + g (the same permutation as the K rows), and for the
-        // rope the piece 32 + g (two 8-byte halves, one per 16x16x32 step).
+        // q pieces 8 s + g and 8 s + 4 + g (the same permutation as the K rows).  The rope
+        // pieces (32 + g, two 8-byte halves, one per 16x16x32 step) wait in this wave's own
+        // LDS copy and are read per chunk, which keeps the loop within the register budget.
         v8i qf[2][4];
-        v4i qt[2];
+        uint8_t *qr = lds + L::QR + w * HG * 64;
 #pragma unroll
         for (int ht = 0; ht < 2; ht++) {
             const int head = hg * HG + 16 * ht + r;
@@ -366,38 +431,33 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(DecodeParams a)
                 }
                 qf[ht][s] = join(lo, hi);
             }
-            qt[ht] = v4i{0, 0, 0, 0};
-            if (TAIL && live)
-                qt[ht] = gload(qp + 16 * (32 + g));
+            if constexpr (TAIL) {
+                v4i qt = v4i{0, 0, 0, 0};
+                if (live)
+                    qt = gload(qp + 16 * (32 + g));
+                *reinterpret_cast<v4i *>(qr + (16 * ht + r) * 64 + 16 * g) = qt;
+            }
         }
 
-        // raw index of this lane's key in chunk x (address clamped into the token's row)
-        auto load_raw = [&](int x) { return idx_row[min(first + x * CHUNK + key, a.W - 1)]; };
-        // Issue the row loads of chunk x into `st`; returns the chunk's mask of active keys
-        // (bit k: key 16 w + k of the chunk), wave-uniform.
+        // raw index of this lane's key in chunk x, from the index ring (written by the P.V
+        // waves at least one barrier earlier)
+        const int *idx_ring = reinterpret_cast<const int *>(lds + L::IDX);
+        auto load_raw = [&](int x) { return idx_ring[(x & 3) * CHUNK + key]; };
+        // Issue the row loads of chunk x into `st` (raw: the index, arrived); returns the
+        // chunk's mask of active keys (bit k: key 16 w + k of the chunk), wave-uniform.  Lane
+        // (r, g) loads pieces 8 s + 4 j + g into st[2 s + j] and the rope piece 32 + g.
         auto issue = [&](int x, int raw, v4i(&st)[NLD]) {
             const int pos = first + x * CHUNK + key;
             const bool valid = pos < end && raw >= 0;
             const uint8_t *pool = (a.kv_b != nullptr && pos >= a.split_col) ? a.kv_b : a.kv_a;
-            const uint8_t *row = valid ? pool + (int64_t)raw * RB : g_zero_row;
-#pragma unroll
-            for (int s = 0; s < 4; s++)
-#pragma unroll
-                for (int j = 0; j < 2; j++)
-                    st[2 * s + j] = gload(row + 16 * (8 * s + 4 * j + g));
-            if constexpr (TAIL)
-                st[8] = gload(row + 16 * (32 + g));
+            const uint8_t *row = (valid ? pool + (int64_t)raw * RB : g_zero_row) + 16 * g;
+            gload_row_async(st, row);
             return (uint32_t)(__ballot(valid) & 0xFFFFu);
         };
 
-        // ---- state --------------------------------------------------------------------------
-        const int kq = lane >> 4;                  // score lanes: keys 4 kq + i of head nh
-        const int nh = lane & 15;
-        float m_run[2] = {-INFINITY, -INFINITY}, frame[2], l_lane[2];
-        int ecur[2];
-        bool preset[2] = {false, false};
-        bool ovf[2];                               // this head overflowed (first pass)
-        v4f s_cur[2];
+        // Per chunk the QK waves issue NLD row loads, in chunk order, so a chunk's rows have
+        // arrived at its QK once the next two chunks' loads (2 NLD) are behind them.
+        constexpr int BEHIND = 2 * NLD;
 
         // QK products of the chunk held in `st` (16 keys x 32 heads as two 16-head tiles)
         auto qk_issue = [&](const v4i(&st)[NLD], v4f &c0, v4f &c1) {
@@ -410,38 +470,46 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(DecodeParams a)
                 c1 = mfma16(av, qf[1][s], c1);
             }
             if constexpr (TAIL) {
+                const v4i q0 = lds_load<v4i>(qr, r * 64 + 16 * g);
+                const v4i q1 = lds_load<v4i>(qr, (16 + r) * 64 + 16 * g);
 #pragma unroll
                 for (int hh = 0; hh < 2; hh++) {
                     const v2i av = v2i{st[8][2 * hh], st[8][2 * hh + 1]};
-                    c0 = mfma16k32(av, v2i{qt[0][2 * hh], qt[0][2 * hh + 1]}, c0);
-                    c1 = mfma16k32(av, v2i{qt[1][2 * hh], qt[1][2 * hh + 1]}, c1);
+                    c0 = mfma16k32(av, v2i{q0[2 * hh], q0[2 * hh + 1]}, c0);
+                    c1 = mfma16k32(av, v2i{q1[2 * hh], q1[2 * hh + 1]}, c1);
                 }
             }
         };
-        // base-2 scores with masked keys at -inf, and this wave's 16-key maximum per head
-        // written to chunk x's MX buffer
-        auto qk_finish = [&](int x, v4f c0, v4f c1, uint32_t mk, v4f(&s2)[2]) {
+        // Base-2 scores of chunk x with masked keys at -inf (lane (n, q): head 16 ht + n, keys
+        // 16 w + 4 q + i) to the chunk's score buffer, in lane order for the P.V wave that owns
+        // the same keys, and this wave's 16-key maximum per head to the chunk's MX buffer.
+        auto qk_finish = [&](int x, v4f c0, v4f c1, uint32_t mk) {
             mfma_result_pad();
+            v4f s0, s1;
             float mx0 = -INFINITY, mx1 = -INFINITY;
 #pragma unroll
             for (int i = 0; i < 4; i++) {
-                const float b = ((mk >> (4 * kq + i)) & 1u) ? 0.0f : -INFINITY;
-                s2[0][i] = fmaf(c0[i], a.scale_log2, b);
-                s2[1][i] = fmaf(c1[i], a.scale_log2, b);
-                mx0 = fmaxf(mx0, s2[0][i]);
-                mx1 = fmaxf(mx1, s2[1][i]);
+                const float b = ((mk >> (4 * g + i)) & 1u) ? 0.0f : -INFINITY;
+                s0[i] = fmaf(c0[i], a.scale_log2, b);
+                s1[i] = fmaf(c1[i], a.scale_log2, b);
+                mx0 = fmaxf(mx0, s0[i]);
+                mx1 = fmaxf(mx1, s1[i]);
             }
+            float *sc = reinterpret_cast<float *>(lds + L::SC) + (x & 1) * (4 * 64 * 8) +
+                        (w * 64 + lane) * 8;
+            *reinterpret_cast<v4f *>(sc) = s0;
+            *reinterpret_cast<v4f *>(sc + 4) = s1;
             mx0 = fmaxf(mx0, __shfl_xor(mx0, 16));
             mx0 = fmaxf(mx0, __shfl_xor(mx0, 32));
             mx1 = fmaxf(mx1, __shfl_xor(mx1, 16));
             mx1 = fmaxf(mx1, __shfl_xor(mx1, 32));
             float *mxb = reinterpret_cast<float *>(lds + L::MX) + (x & 1) * HG * 4;
-            if (kq < 2)
-                mxb[(16 * kq + nh) * 4 + w] = kq == 0 ? mx0 : mx1;
+            if (g < 2)
+                mxb[(16 * g + r) * 4 + w] = g == 0 ? mx0 : mx1;
         };
-        // latent bytes of the chunk in `st` to V slot x & 3 (pieces 8 s + 4 j + g of row key)
+        // latent bytes of the chunk in `st` to its V slot (pieces 8 s + 4 j + g of row key)
         auto write_v = [&](int x, const v4i(&st)[NLD]) {
-            uint8_t *vs = lds + L::V + (x & (VSLOTS - 1)) * L::VSLOT + key * 512;
+            uint8_t *vs = lds + L::V + vslot(x) * L::VSLOT + key * 512;
             const int sw = vsw(key);
 #pragma unroll
             for (int s = 0; s < 4; s++)
@@ -450,103 +518,35 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(DecodeParams a)
                     *reinterpret_cast<v4i *>(vs + 16 * ((8 * s + 4 * j + g) ^ sw)) =
                         st[2 * s + j];
         };
-        // softmax of chunk x (branch-free): frame, P (to the chunk's P buffer) and E8M0 scales.
-        // First pass: G is the running maximum after the first chunk with an active column and
-        // e = ceil(m - G) >= 0; an offset beyond FRAME_LIMIT marks the head for the second
-        // pass, which fixes G at the head's final maximum before the range starts (e = ceil(m -
-        // G) <= 0, at least E_MIN), so no pass ever rescales the accumulators.
-        auto softmax = [&](int x, const v4f(&s2)[2]) {
-            const uint8_t *mxb = lds + L::MX + (x & 1) * HG * 16;
-            uint8_t *pbase = lds + L::P + (x & 1) * L::PBUF;
-#pragma unroll
-            for (int ht = 0; ht < 2; ht++) {
-                const int head = 16 * ht + nh;
-                const v4f m4 = lds_load<v4f>(mxb, head * 16);
-                const float m_chunk = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
-                const float m_new = fmaxf(m_run[ht], m_chunk);
-                const bool fresh = frame[ht] == -INFINITY;
-                const float diff = fresh || m_new == -INFINITY ? 0.0f : m_new - frame[ht];
-                int e = (int)ceilf(fmaxf(diff, (float)E_MIN));
-                ovf[ht] = ovf[ht] || e > FRAME_LIMIT;
-                e = min(e, FRAME_LIMIT);            // first pass after an overflow: unused
-                const int shift = fresh ? 0 : ecur[ht] - e;
-                frame[ht] = fresh ? m_new : frame[ht];
-                ecur[ht] = e;
-                m_run[ht] = m_new;
-                const float fb =
-                    frame[ht] == -INFINITY ? 0.0f : (frame[ht] + (float)e) - LOG2_ANCHOR;
-                float p[4];
-                float lsum = 0.0f;
-#pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    p[i] = __builtin_amdgcn_exp2f(s2[ht][i] - fb);  // exp2(-inf) = 0
-                    lsum += p[i];
-                }
-                l_lane[ht] = ldexpf(l_lane[ht], shift) + lsum;
-                int hi = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
-                hi = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], hi, true);
-                const int off = head * 64 + 16 * (w ^ psw(head)) + 4 * kq;
-                *reinterpret_cast<int *>(pbase + off) = hi;
-                if constexpr (TWO) {
-                    const float h0 = __builtin_amdgcn_cvt_f32_fp8(hi, 0);
-                    const float h1 = __builtin_amdgcn_cvt_f32_fp8(hi, 1);
-                    const float h2 = __builtin_amdgcn_cvt_f32_fp8(hi, 2);
-                    const float h3 = __builtin_amdgcn_cvt_f32_fp8(hi, 3);
-                    int lo = __builtin_amdgcn_cvt_pk_fp8_f32(16.0f * (p[0] - h0),
-                                                             16.0f * (p[1] - h1), 0, false);
-                    lo = __builtin_amdgcn_cvt_pk_fp8_f32(16.0f * (p[2] - h2),
-                                                         16.0f * (p[3] - h3), lo, true);
-                    *reinterpret_cast<int *>(pbase + L::PTERM + off) = lo;
-                }
-                if (w == 0 && kq == ht)
-                    reinterpret_cast<int *>(lds + L::ESC)[(x & 1) * HG + head] = 127 + e;
-            }
-        };
 
         v4i st0[NLD], st1[NLD], st2[NLD];
         uint32_t mk0 = 0, mk1 = 0, mk2 = 0;
-        int raw_q = 0;                             // raw index of the next chunk to issue
 
-        // Iteration c: row loads of chunk c+3 into `ld` (the stage chunk c left), QK and V
-        // slot of chunk c+1 from `cur`, softmax of chunk c.
-        auto iteration = [&](int c, v4i(&ld)[NLD], uint32_t &mld, const v4i(&cur)[NLD],
+        // Iteration c: row loads of chunk c+3 into `ld` (the stage chunk c left), QK, scores
+        // and V slot of chunk c+1 from `cur`.
+        auto iteration = [&](int c, v4i(&ld)[NLD], uint32_t &mld, v4i(&cur)[NLD],
                              uint32_t mcur) __attribute__((always_inline)) {
             lds_barrier();
-            const int raw_next = load_raw(c + 4);   // first: its wait counts stay partial
-            mld = issue(c + 3, raw_q, ld);
-            raw_q = raw_next;
+            mld = issue(c + 3, load_raw(c + 3), ld);
+            wait_vm<BEHIND>(cur);                   // the rows of chunk c+1
             v4f c0, c1;
             qk_issue(cur, c0, c1);
-            softmax(c, s_cur);
-            v4f s_next[2];
-            qk_finish(c + 1, c0, c1, mcur, s_next);
+            qk_finish(c + 1, c0, c1, mcur);
             write_v(c + 1, cur);
-            s_cur[0] = s_next[0];
-            s_cur[1] = s_next[1];
         };
 
         auto run_range = [&]() __attribute__((always_inline)) {
-#pragma unroll
-            for (int ht = 0; ht < 2; ht++) {
-                frame[ht] = preset[ht] ? m_run[ht] : -INFINITY;
-                m_run[ht] = -INFINITY;
-                l_lane[ht] = 0.0f;
-                ecur[ht] = 0;
-                ovf[ht] = false;
-            }
             if (nch == 0)
                 return;
+            lds_barrier();                          // the index ring holds chunks 0 .. 3
+            mk0 = issue(0, load_raw(0), st0);
+            mk1 = issue(1, load_raw(1), st1);
+            mk2 = issue(2, load_raw(2), st2);
             {
-                const int r0 = load_raw(0), r1 = load_raw(1), r2 = load_raw(2);
-                raw_q = load_raw(3);
-                mk0 = issue(0, r0, st0);
-                mk1 = issue(1, r1, st1);
-                mk2 = issue(2, r2, st2);
-            }
-            {
+                wait_vm<BEHIND>(st0);
                 v4f c0, c1;
                 qk_issue(st0, c0, c1);
-                qk_finish(0, c0, c1, mk0, s_cur);
+                qk_finish(0, c0, c1, mk0);
             }
             write_v(0, st0);
             for (int c = 0;; c += 3) {
@@ -560,37 +560,18 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(DecodeParams a)
                 if (c + 3 >= nch)
                     break;
             }
+            // every load has landed before the registers it targets can be reused
+            wait_vm<0>(st0);
+            wait_vm<0>(st1);
+            wait_vm<0>(st2);
             lds_barrier();                          // drain: the O waves' P.V of chunk nch-1
         };
 
         run_range();
-        // second pass for the heads whose offset overflowed (rare): restart the range with
-        // their frames fixed at their final maxima
+        lds_barrier();                              // the P.V waves decide on a second pass
         lds_barrier();
-        if (__any(ovf[0] || ovf[1]) && lane == 0)
-            *flag = 1;
-        lds_barrier();
-        if (*flag != 0) {
-            preset[0] = ovf[0];
-            preset[1] = ovf[1];
+        if (*flag != 0)
             run_range();
-        }
-
-        // ---- per-head results: l (per wave), G and e ---------------------------------------
-#pragma unroll
-        for (int ht = 0; ht < 2; ht++) {
-            float lt = l_lane[ht];
-            lt += __shfl_xor(lt, 16);
-            lt += __shfl_xor(lt, 32);
-            const int head = 16 * ht + nh;
-            if (kq == ht) {
-                fin[w * HG + head] = lt;
-                if (w == 0) {
-                    fin[4 * HG + head] = frame[ht];
-                    reinterpret_cast<int *>(fin)[5 * HG + head] = ecur[ht];
-                }
-            }
-        }
         v16f none[NCT];
 #pragma unroll
         for (int ct = 0; ct < NCT; ct++)
@@ -615,9 +596,73 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(DecodeParams a)
                 v_off[ct][rho] = k * 512 + 16 * (piece ^ vsw(k)) + 8 * (i16 & 1);
             }
 
+        // ---- softmax state: lane (nh, kq) owns heads nh and 16 + nh, keys 16 w + 4 kq + i --
+        const int kq = lane >> 4, nh = lane & 15;
+        float m_run[2] = {-INFINITY, -INFINITY}, frame[2], l_lane[2];
+        int ecur[2];
+        bool preset[2] = {false, false};
+        bool ovf[2];                               // this head overflowed (first pass)
+
+        // softmax of chunk x (branch-free): frame, P (to the chunk's P buffer) and E8M0 scales.
+        // First pass: G is the running maximum after the first chunk with an active column and
+        // e = ceil(m - G) >= 0; an offset beyond FRAME_LIMIT marks the head for the second
+        // pass, which fixes G at the head's final maximum before the range starts (e = ceil(m -
+        // G) <= 0, at least E_MIN), so no pass ever rescales the accumulators.
+        auto softmax = [&](int x) {
+            const uint8_t *mxb = lds + L::MX + (x & 1) * HG * 16;
+            const float *sc = reinterpret_cast<const float *>(lds + L::SC) +
+                              (x & 1) * (4 * 64 * 8) + (w * 64 + lane) * 8;
+            const v4f sv[2] = {*reinterpret_cast<const v4f *>(sc),
+                               *reinterpret_cast<const v4f *>(sc + 4)};
+            uint8_t *pbase = lds + L::P + (x & 1) * L::PBUF;
+#pragma unroll
+            for (int ht = 0; ht < 2; ht++) {
+                const int head = 16 * ht + nh;
+                const v4f m4 = lds_load<v4f>(mxb, head * 16);
+                const float m_chunk = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+                const float m_new = fmaxf(m_run[ht], m_chunk);
+                const bool fresh = frame[ht] == -INFINITY;
+                const float diff = fresh || m_new == -INFINITY ? 0.0f : m_new - frame[ht];
+                int e = (int)ceilf(fmaxf(diff, (float)E_MIN));
+                ovf[ht] = ovf[ht] || e > FRAME_LIMIT;
+                e = min(e, FRAME_LIMIT);            // first pass after an overflow: unused
+                const int shift = fresh ? 0 : ecur[ht] - e;
+                frame[ht] = fresh ? m_new : frame[ht];
+                ecur[ht] = e;
+                m_run[ht] = m_new;
+                const float fb =
+                    frame[ht] == -INFINITY ? 0.0f : (frame[ht] + (float)e) - LOG2_ANCHOR;
+                float p[4];
+                float lsum = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    p[i] = __builtin_amdgcn_exp2f(sv[ht][i] - fb);  // exp2(-inf) = 0
+                    lsum += p[i];
+                }
+                l_lane[ht] = ldexpf(l_lane[ht], shift) + lsum;
+                int hi = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+                hi = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], hi, true);
+                const int off = head * 64 + 16 * (w ^ psw(head)) + 4 * kq;
+                *reinterpret_cast<int *>(pbase + off) = hi;
+                if constexpr (TWO) {
+                    const float h0 = __builtin_amdgcn_cvt_f32_fp8(hi, 0);
+                    const float h1 = __builtin_amdgcn_cvt_f32_fp8(hi, 1);
+                    const float h2 = __builtin_amdgcn_cvt_f32_fp8(hi, 2);
+                    const float h3 = __builtin_amdgcn_cvt_f32_fp8(hi, 3);
+                    int lo = __builtin_amdgcn_cvt_pk_fp8_f32(16.0f * (p[0] - h0),
+                                                             16.0f * (p[1] - h1), 0, false);
+                    lo = __builtin_amdgcn_cvt_pk_fp8_f32(16.0f * (p[2] - h2),
+                                                         16.0f * (p[3] - h3), lo, true);
+                    *reinterpret_cast<int *>(pbase + L::PTERM + off) = lo;
+                }
+                if (w == 0 && kq == ht)
+                    reinterpret_cast<int *>(lds + L::ESC)[(x & 1) * HG + head] = 127 + e;
+            }
+        };
+
         // P.V of chunk x over this wave's 4 column tiles
         auto pv = [&](int x) {
-            const uint8_t *vs = lds + L::V + (x & (VSLOTS - 1)) * L::VSLOT;
+            const uint8_t *vs = lds + L::V + vslot(x) * L::VSLOT;
             const uint8_t *pbuf = lds + L::P + (x & 1) * L::PBUF;
             const int escw = reinterpret_cast<const int *>(lds + L::ESC)[(x & 1) * HG + hl];
             const v8i bh = join(lds_load<v4i>(pbuf, p_off0), lds_load<v4i>(pbuf, p_off1));
@@ -649,7 +694,35 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(DecodeParams a)
             }
         };
 
+        // Indices of the QK waves' row loads: the P.V waves load chunk x's 64 raw indices
+        // (address clamped into the token's row) one iteration before they store them to the
+        // index ring, which the QK waves read one iteration later still.
+        int *idx_ring = reinterpret_cast<int *>(lds + L::IDX);
+        auto idx_load = [&](int x) { return idx_row[min(first + x * CHUNK + lane, a.W - 1)]; };
+        int idx_next = 0;
+
+        // Iteration c: index of chunk c+4 to the ring (loaded last iteration) and the load of
+        // chunk c+5's, softmax of chunk c (its scores and maxima arrived last iteration), then
+        // P.V of chunk c-1 (its P and V slot arrived last iteration).
+        auto iteration = [&](int c) __attribute__((always_inline)) {
+            lds_barrier();
+            if (w == 0) {
+                idx_ring[((c + 4) & 3) * CHUNK + lane] = idx_next;
+                idx_next = idx_load(c + 5);
+            }
+            softmax(c);
+            pv(c - 1);
+        };
+
         auto run_range = [&]() __attribute__((always_inline)) {
+#pragma unroll
+            for (int ht = 0; ht < 2; ht++) {
+                frame[ht] = preset[ht] ? m_run[ht] : -INFINITY;
+                m_run[ht] = -INFINITY;
+                l_lane[ht] = 0.0f;
+                ecur[ht] = 0;
+                ovf[ht] = false;
+            }
 #pragma unroll
             for (int ct = 0; ct < NCT; ct++)
                 acc[ct] = v16f{};
@@ -658,7 +731,7 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(DecodeParams a)
             // chunk -1 (read by P.V in iteration 0): a zero V slot, zero P and a unit scale
             {
                 const int ot = tid - 256;
-                uint8_t *z = lds + L::V + (VSLOTS - 1) * L::VSLOT;
+                uint8_t *z = lds + L::V + vslot(-1) * L::VSLOT;
                 for (int x = ot; x < L::VSLOT / 16; x += 256)
                     *reinterpret_cast<v4i *>(z + 16 * x) = v4i{0, 0, 0, 0};
                 for (int x = ot; x < L::PBUF / 16; x += 256)
@@ -666,17 +739,21 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(DecodeParams a)
                 if (ot < HG)
                     reinterpret_cast<int *>(lds + L::ESC)[HG + ot] = 127;
             }
+            if (w == 0) {
+#pragma unroll
+                for (int x = 0; x < 4; x++)
+                    idx_ring[x * CHUNK + lane] = idx_load(x);
+                idx_next = idx_load(4);
+            }
+            lds_barrier();                          // the index ring holds chunks 0 .. 3
             for (int c = 0;; c += 3) {
-                lds_barrier();
-                pv(c - 1);
+                iteration(c);
                 if (c + 1 >= nch)
                     break;
-                lds_barrier();
-                pv(c);
+                iteration(c + 1);
                 if (c + 2 >= nch)
                     break;
-                lds_barrier();
-                pv(c + 1);
+                iteration(c + 2);
                 if (c + 3 >= nch)
                     break;
             }
@@ -685,10 +762,33 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(DecodeParams a)
         };
 
         run_range();
+        // second pass for the heads whose offset overflowed (rare): restart the range with
+        // their frames fixed at their final maxima
         lds_barrier();
+        if (__any(ovf[0] || ovf[1]) && lane == 0)
+            *flag = 1;
         lds_barrier();
-        if (*flag != 0)
+        if (*flag != 0) {
+            preset[0] = ovf[0];
+            preset[1] = ovf[1];
             run_range();
+        }
+
+        // ---- per-head results: l (per wave), G and e ---------------------------------------
+#pragma unroll
+        for (int ht = 0; ht < 2; ht++) {
+            float lt = l_lane[ht];
+            lt += __shfl_xor(lt, 16);
+            lt += __shfl_xor(lt, 32);
+            const int head = 16 * ht + nh;
+            if (kq == ht) {
+                fin[w * HG + head] = lt;
+                if (w == 0) {
+                    fin[4 * HG + head] = frame[ht];
+                    reinterpret_cast<int *>(fin)[5 * HG + head] = ecur[ht];
+                }
+            }
+        }
         epilogue(acc);
     }
 }

@@ -1,0 +1,123 @@
+"""The decode kernel's QK waves issue their row loads from inline assembly and wait for them
+with explicit counts; the compiler does not know those registers fill asynchronously.  This
+CPU test compiles the kernel to gfx950 assembly and checks, for every such load block in the
+QK waves' loop, that no instruction touches its destination registers between the block and
+the first matrix instruction that consumes them (scanning the loop body cyclically), and that
+an explicit wait sits in that window.  A copy or reuse of those registers while a load is in
+flight would read or clobber data that has not landed (the failure this guards against: a row
+address built from such a copy)."""
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+from sparse_mla_attention_amd import build
+
+SRC = os.path.join(build.CSRC, "smla_decode.hip")
+
+
+def _regs(tok):
+    m = re.match(r"v\[(\d+):(\d+)\]", tok)
+    if m:
+        return set(range(int(m.group(1)), int(m.group(2)) + 1))
+    m = re.match(r"v(\d+)$", tok)
+    return {int(m.group(1))} if m else set()
+
+
+def _operands(line):
+    parts = line.split(None, 1)
+    if len(parts) < 2:
+        return (parts[0] if parts else ""), set(), set()
+    op, ops = parts[0], [o.strip() for o in parts[1].split(",")]
+    if op.startswith(("ds_write", "global_store", "buffer_store", "s_")):
+        src = set()
+        for o in ops:
+            src |= _regs(o.split()[0])
+        return op, set(), src
+    dst = _regs(ops[0].split()[0])
+    src = set()
+    for o in ops[1:]:
+        src |= _regs(o.split()[0])
+    return op, dst, src
+
+
+def _asm_loop(body):
+    lines = body.split("\n")
+    for h, l in enumerate(lines):
+        if "Loop Header" not in l:
+            continue
+        lab = l.split(":")[0].strip()
+        ends = [i for i, x in enumerate(lines)
+                if re.search(r"s_c?branch\S*\s+" + re.escape(lab) + r"$", x.strip())]
+        if not ends:
+            continue
+        seg = lines[h:max(ends) + 1]
+        if any("ASMSTART" in x for x in seg) and any("global_load_dwordx4" in x for x in seg):
+            return seg
+    return None
+
+
+def _check(body):
+    seg = _asm_loop(body)
+    assert seg is not None, "no loop with inline-assembly row loads"
+    ins, in_asm = [], False
+    for l in seg:
+        s = l.strip()
+        if "ASMSTART" in s:
+            in_asm = True
+            ins.append(("start", s))
+        elif "ASMEND" in s:
+            in_asm = False
+            ins.append(("end", s))
+        elif s and not s.startswith((";", ".")):
+            ins.append(("asm" if in_asm else "cc", s))
+    n, blocks, problems = len(ins), 0, []
+    i = 0
+    while i < n:
+        if ins[i][0] == "start" and i + 1 < n and "global_load" in ins[i + 1][1]:
+            d, j = set(), i + 1
+            while ins[j][0] != "end":
+                d |= _regs(ins[j][1].split()[1].rstrip(","))
+                j += 1
+            blocks += 1
+            waited, k = False, (j + 1) % n
+            for _ in range(n):
+                kind, s = ins[k]
+                if kind == "asm" and s.startswith("s_waitcnt vmcnt"):
+                    waited = True
+                elif kind == "asm" and "global_load" in s and _regs(s.split()[1].rstrip(",")) & d:
+                    problems.append("reloaded before use: " + s)
+                    break
+                elif kind == "cc":
+                    op, dst, src = _operands(s)
+                    if op.startswith("v_mfma") and src & d:
+                        if not waited:
+                            problems.append("consumed before its wait: " + s)
+                        break
+                    if (dst | src) & d:
+                        problems.append("touched in flight: " + s)
+                k = (k + 1) % n
+            i = j
+        i += 1
+    return blocks, problems
+
+
+def test_async_row_loads_are_never_touched_in_flight():
+    with tempfile.TemporaryDirectory() as tmp:
+        out = os.path.join(tmp, "decode.s")
+        cmd = [build.HIPCC, *build.FLAGS, "--cuda-device-only", "-S", SRC, "-o", out]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            pytest.fail(r.stdout + r.stderr)
+        text = open(out).read()
+    kernels = re.findall(r"^(_ZN\S*decode_kernel\S*):[^\n]*\n(.*?)s_endpgm", text, re.S | re.M)
+    assert len(kernels) == 6  # 3 row shapes x one/two-term P
+    for name, body in kernels:
+        blocks, problems = _check(body)
+        assert blocks == 3, name
+        assert not problems, (name, problems[:5])
+    # the same kernels spill nothing (the compiler's waits for a spill reload do not know the
+    # row loads in flight, so they would drain them)
+    assert not re.search(r"\.vgpr_spill_count:\s+[1-9]", text)
