@@ -15,30 +15,35 @@
 //
 // Two roles, one wave of each per SIMD, so that one role's matrix work overlaps the other's
 // vector and LDS work:
-//   S waves (0..3): wave w owns keys 16 w .. 16 w + 15 of every chunk.  Lane (r, g) = (lane %
-//     16, lane / 16) loads row 16 w + r of the chunk straight into registers, 16-byte pieces
+//   QK waves (0..3): wave w owns keys 16 w .. 16 w + 15 of every chunk.  Lane (r, g) = (lane
+//     % 16, lane / 16) loads row 16 w + r of the chunk straight into registers, 16-byte pieces
 //     8 s + 4 j + g (s < 4, j < 2) and the rope piece 32 + g: each load instruction reads 64
 //     contiguous bytes of 16 rows.  Those registers are the A operand of QK on
 //     v_mfma_scale_f32_16x16x128_f8f6f4 (16 keys x 16 heads x 128 bytes; the Q fragments, the
-//     B operand, are loaded once with the same byte permutation), so K never goes through
-//     LDS; the 512 latent bytes are written to an LDS slot for P.V.  Rows are loaded two
-//     chunks ahead of their QK (three register stages).  Masked columns read a zero row.
-//     The softmax: s2 = S bmm1 log2(e) (-inf for masked keys), chunk maximum over the four S
-//     waves through LDS, running maximum m.  P is anchored at F = G + e, e = ceil(m - G) (G:
-//     the running maximum after the first chunk that has one): P = 2^(s2 - F + log2 448) <=
-//     448, rounded to E4M3 by v_cvt_pk_fp8_f32 (two-term default: P = hi + lo/16, lo =
-//     E4M3(16 (P - hi))).  The accumulators stay in frame G and the chunk enters with weight
-//     2^e through the P.V instruction's per-lane E8M0 B scale, so they are never rescaled; a
-//     head whose offset would exceed FRAME_LIMIT makes the workgroup compute its range again
-//     with that head's G preset to its maximum.  FP32 sums of the unquantized P are kept per
-//     lane in frame F.
-//   O waves (4..7): wave 4 + j owns latent columns 128 j .. 128 j + 127: O^T (32 columns x 32
-//     heads) += V^T (32 columns x 64 keys, ds_read_b64_tr_b8 from the slot) P^T (64 keys x 32
-//     heads, from the P buffer) on v_mfma_scale_f32_32x32x64_f8f6f4, 4 tiles per chunk (8
-//     instructions with two-term P).
-//   Software pipeline: iteration c runs, in the S waves, the row loads of chunk c+3, QK of
-//   chunk c+1 (and its V slot) and the softmax of chunk c, and in the O waves P.V of chunk
-//   c-1, with a single workgroup barrier per iteration; four V slots hold chunks c-1 .. c+2.
+//     B operand, are loaded once with the same byte permutation; the rope step runs on two
+//     16x16x32 FP8 instructions), so K never goes through LDS; the 512 latent bytes are
+//     written to an LDS slot for P.V.  Rows are loaded two chunks ahead of their QK (three
+//     register stages, issued from inline assembly with explicit waits); masked columns read
+//     a zero row.  The base-2 scores s2 = S bmm1 log2(e) (-inf for masked keys) go to LDS in
+//     lane order, with this wave's 16-key maximum per head.
+//   P.V waves (4..7): wave 4 + j owns latent columns 128 j .. 128 j + 127 and, for the
+//     softmax, the keys 16 j .. 16 j + 15 of every chunk (the same lanes as the QK wave that
+//     computed their scores).  Softmax: chunk maximum over the four key quarters, running
+//     maximum m.  P is anchored at F = G + e, e = ceil(m - G) (G: the running maximum after the
+//     first chunk that has one): P = 2^(s2 - F + log2 448) <= 448, rounded to E4M3 by
+//     v_cvt_pk_fp8_f32 (two-term default: P = hi + lo/16, lo = E4M3(16 (P - hi))).  The
+//     accumulators stay in frame G and the chunk enters with weight 2^e through the P.V
+//     instruction's per-lane E8M0 B scale, so they are never rescaled; a head whose offset
+//     would exceed FRAME_LIMIT makes the workgroup compute its range again with that head's G
+//     preset to its maximum.  FP32 sums of the unquantized P are kept per lane in frame F.
+//     P.V: O^T (32 columns x 32 heads) += V^T (32 columns x 64 keys, ds_read_b64_tr_b8 from
+//     the slot) P^T (64 keys x 32 heads, from the P buffer) on
+//     v_mfma_scale_f32_32x32x64_f8f6f4, 4 tiles per chunk (8 instructions with two-term P).
+//     One of these waves also loads the row indices into an LDS ring for the QK waves.
+//   Software pipeline: iteration c runs, in the QK waves, the row loads of chunk c+3 and QK
+//   (scores, maxima, V slot) of chunk c+1, and in the P.V waves the softmax of chunk c and
+//   P.V of chunk c-1, with a single workgroup barrier per iteration; three V slots hold
+//   chunks c-1 .. c+1.
 //
 // Epilogue: one range (S = 1): merge with the sink, BF16 output through an LDS tile (coalesced
 // row stores) and the LSE.  S > 1: every range writes its FP32 partial (in register order, so
@@ -66,7 +71,7 @@ constexpr int CHUNK = 64;                          // columns per chunk
 constexpr int NT = 512;                            // threads per workgroup (8 waves)
 constexpr int HG = 32;                             // heads per workgroup
 constexpr int VSLOTS = 3;                          // V slots in LDS: chunks c-1 .. c+1
-constexpr int NCT = 4;                             // 32-column P.V tiles per O wave
+constexpr int NCT = 4;                             // 32-column P.V tiles per P.V wave
 constexpr float ANCHOR = 448.0f;                   // P anchor: E4M3's largest finite value
 constexpr float LOG2_ANCHOR = 8.807354922057604f;  // log2(448)
 constexpr float LN2 = 0.6931471805599453f;
@@ -86,10 +91,10 @@ struct Lds {
     static constexpr int PTERM = HG * 64;
     static constexpr int PBUF = 2 * PTERM;
     static constexpr int ESC = P + 2 * PBUF;                   // [2 buf][32] int: E8M0 byte
-    static constexpr int MX = ESC + 2 * HG * 4;                // [2 buf][32 heads][4 S waves]
-    static constexpr int FIN = MX + 2 * HG * 4 * 4;            // [4 S waves][32] l, G, e
+    static constexpr int MX = ESC + 2 * HG * 4;                // [2 buf][32 heads][4 key quarters]
+    static constexpr int FIN = MX + 2 * HG * 4 * 4;            // [4 key quarters][32] l, [32] G, e
     static constexpr int IDX = FIN + 6 * HG * 4;               // [4 chunks][64] int indices
-    static constexpr int QR = IDX + 4 * CHUNK * 4;             // [4 S waves][32][64] q rope
+    static constexpr int QR = IDX + 4 * CHUNK * 4;             // [4 QK waves][32][64] q rope
     static constexpr int MISC = QR + 4 * HG * 64;              // ticket, overflow flag
     static constexpr int TOTAL = MISC + 16;
     static constexpr int OUT_TILE = HG * 1024;                 // BF16 [32][512], after the loop
@@ -99,7 +104,7 @@ struct Lds {
 
 // XOR on the 16-byte piece index of latent row `key` in a V slot: eight consecutive keys put
 // a 32-byte column pair on eight distinct bank groups (the transposed reads of P.V) and
-// sixteen consecutive keys put one piece on sixteen (the S waves' row writes).
+// sixteen consecutive keys put one piece on sixteen (the QK waves' row writes).
 __device__ inline int vsw(int key) { return ((key & 7) << 1) | ((key >> 3) & 1); }
 
 // V slot of chunk x (x >= -1).
@@ -293,7 +298,7 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(DecodeParams a)
     if (tid == 0)
         *flag = 0;
 
-    // ---- epilogue (every wave; `acc` holds the O waves' accumulators) -----------------------
+    // ---- epilogue (every wave; `acc` holds the P.V waves' accumulators) ---------------------
     // acc[ct]: O^T tile of columns 32 (4 w + ct) + .. x 32 heads; lane l holds head l % 32,
     // columns 8 (r / 4) + 4 (l / 32) + r % 4 of the tile in register r.
     auto epilogue = [&](v16f(&acc)[NCT]) __attribute__((always_inline)) {
@@ -407,7 +412,7 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(DecodeParams a)
     };
 
     if (s_wave) {
-        // =================================== S waves ======================================
+        // =================================== QK waves =====================================
         const int r = lane & 15, g = lane >> 4;    // row r of this wave's 16 keys, piece group
         const int key = 16 * w + r;                // this lane's key within a chunk
 
@@ -564,7 +569,7 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(DecodeParams a)
             wait_vm<0>(st0);
             wait_vm<0>(st1);
             wait_vm<0>(st2);
-            lds_barrier();                          // drain: the O waves' P.V of chunk nch-1
+            lds_barrier();                          // drain: the P.V waves' P.V of chunk nch-1
         };
 
         run_range();
@@ -578,7 +583,7 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(DecodeParams a)
             none[ct] = v16f{};
         epilogue(none);
     } else {
-        // =================================== O waves ======================================
+        // =================================== P.V waves ====================================
         v16f acc[NCT];
         const int hl = lane & 31, u = lane >> 5;   // head of the B / C columns, key block
         const int q4 = lane >> 4, i16 = lane & 15;
