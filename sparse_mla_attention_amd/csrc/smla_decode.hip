@@ -39,7 +39,8 @@
 //     P.V: O^T (32 columns x 32 heads) += V^T (32 columns x 64 keys, ds_read_b64_tr_b8 from
 //     the slot) P^T (64 keys x 32 heads, from the P buffer) on
 //     v_mfma_scale_f32_32x32x64_f8f6f4, 4 tiles per chunk (8 instructions with two-term P).
-//     One of these waves also loads the row indices into an LDS ring for the QK waves.
+//     One of these waves also loads the row indices, eight chunks at a time and at least
+//     eight chunks ahead, into an LDS ring for the QK waves.
 //   Software pipeline: iteration c runs, in the QK waves, the row loads of chunk c+3 and QK
 //   (scores, maxima, V slot) of chunk c+1, and in the P.V waves the softmax of chunk c and
 //   P.V of chunk c-1, with a single workgroup barrier per iteration; three V slots hold
@@ -72,6 +73,8 @@ constexpr int NT = 512;                            // threads per workgroup (8 w
 constexpr int HG = 32;                             // heads per workgroup
 constexpr int VSLOTS = 3;                          // V slots in LDS: chunks c-1 .. c+1
 constexpr int NCT = 4;                             // 32-column P.V tiles per P.V wave
+constexpr int IRING = 16;                          // chunks of row indices held in LDS
+constexpr int IBLK = 8;                            // chunks of indices loaded per refill
 constexpr float ANCHOR = 448.0f;                   // P anchor: E4M3's largest finite value
 constexpr float LOG2_ANCHOR = 8.807354922057604f;  // log2(448)
 constexpr float LN2 = 0.6931471805599453f;
@@ -93,8 +96,8 @@ struct Lds {
     static constexpr int ESC = P + 2 * PBUF;                   // [2 buf][32] int: E8M0 byte
     static constexpr int MX = ESC + 2 * HG * 4;                // [2 buf][32 heads][4 key quarters]
     static constexpr int FIN = MX + 2 * HG * 4 * 4;            // [4 key quarters][32] l, [32] G, e
-    static constexpr int IDX = FIN + 6 * HG * 4;               // [4 chunks][64] int indices
-    static constexpr int QR = IDX + 4 * CHUNK * 4;             // [4 QK waves][32][64] q rope
+    static constexpr int IDX = FIN + 6 * HG * 4;               // [16 chunks][64] int indices
+    static constexpr int QR = IDX + IRING * CHUNK * 4;         // [4 QK waves][32][64] q rope
     static constexpr int MISC = QR + 4 * HG * 64;              // ticket, overflow flag
     static constexpr int TOTAL = MISC + 16;
     static constexpr int OUT_TILE = HG * 1024;                 // BF16 [32][512], after the loop
@@ -447,7 +450,7 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(DecodeParams a)
         // raw index of this lane's key in chunk x, from the index ring (written by the P.V
         // waves at least one barrier earlier)
         const int *idx_ring = reinterpret_cast<const int *>(lds + L::IDX);
-        auto load_raw = [&](int x) { return idx_ring[(x & 3) * CHUNK + key]; };
+        auto load_raw = [&](int x) { return idx_ring[(x % IRING) * CHUNK + key]; };
         // Issue the row loads of chunk x into `st` (raw: the index, arrived); returns the
         // chunk's mask of active keys (bit k: key 16 w + k of the chunk), wave-uniform.  Lane
         // (r, g) loads pieces 8 s + 4 j + g into st[2 s + j] and the rope piece 32 + g.
@@ -543,7 +546,7 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(DecodeParams a)
         auto run_range = [&]() __attribute__((always_inline)) {
             if (nch == 0)
                 return;
-            lds_barrier();                          // the index ring holds chunks 0 .. 3
+            lds_barrier();                          // the index ring holds chunks 0 .. 7
             mk0 = issue(0, load_raw(0), st0);
             mk1 = issue(1, load_raw(1), st1);
             mk2 = issue(2, load_raw(2), st2);
@@ -699,21 +702,27 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(DecodeParams a)
             }
         };
 
-        // Indices of the QK waves' row loads: the P.V waves load chunk x's 64 raw indices
-        // (address clamped into the token's row) one iteration before they store them to the
-        // index ring, which the QK waves read one iteration later still.
+        // Indices of the QK waves' row loads, in an LDS ring of IRING chunks (slot x % IRING),
+        // filled by wave 4 in blocks of IBLK chunks: at iteration c = 0 mod IBLK it stores the
+        // block of chunks c + IBLK .. c + 2 IBLK - 1, loaded IBLK iterations earlier, and loads
+        // the next block, so no iteration waits on an index load.  The QK waves read chunk x's
+        // slot at iteration x - 3, and its previous chunk (x - IRING) was read long before.
+        // Addresses are clamped into the token's row.
         int *idx_ring = reinterpret_cast<int *>(lds + L::IDX);
         auto idx_load = [&](int x) { return idx_row[min(first + x * CHUNK + lane, a.W - 1)]; };
-        int idx_next = 0;
+        int idx_blk[IBLK];
 
-        // Iteration c: index of chunk c+4 to the ring (loaded last iteration) and the load of
-        // chunk c+5's, softmax of chunk c (its scores and maxima arrived last iteration), then
-        // P.V of chunk c-1 (its P and V slot arrived last iteration).
+        // Iteration c: index block refill (every IBLK iterations), softmax of chunk c (its
+        // scores and maxima arrived last iteration), then P.V of chunk c-1 (its P and V slot
+        // arrived last iteration).
         auto iteration = [&](int c) __attribute__((always_inline)) {
             lds_barrier();
-            if (w == 0) {
-                idx_ring[((c + 4) & 3) * CHUNK + lane] = idx_next;
-                idx_next = idx_load(c + 5);
+            if (w == 0 && c % IBLK == 0) {
+#pragma unroll
+                for (int j = 0; j < IBLK; j++) {
+                    idx_ring[((c + IBLK + j) % IRING) * CHUNK + lane] = idx_blk[j];
+                    idx_blk[j] = idx_load(c + 2 * IBLK + j);
+                }
             }
             softmax(c);
             pv(c - 1);
@@ -746,11 +755,13 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(DecodeParams a)
             }
             if (w == 0) {
 #pragma unroll
-                for (int x = 0; x < 4; x++)
+                for (int x = 0; x < IBLK; x++)
                     idx_ring[x * CHUNK + lane] = idx_load(x);
-                idx_next = idx_load(4);
+#pragma unroll
+                for (int j = 0; j < IBLK; j++)
+                    idx_blk[j] = idx_load(IBLK + j);
             }
-            lds_barrier();                          // the index ring holds chunks 0 .. 3
+            lds_barrier();                          // the index ring holds chunks 0 .. IBLK-1
             for (int c = 0;; c += 3) {
                 iteration(c);
                 if (c + 1 >= nch)
