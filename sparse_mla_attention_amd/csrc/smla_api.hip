@@ -49,8 +49,7 @@ bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
 
 int32_t head_tiles(int32_t H) { return (H + 31) / 32; }
 
-// 32-head tiles per workgroup: one in this build (a workgroup's LDS holds four chunk slots of
-// rows and the P buffers of 32 heads).
+// 32-head tiles per workgroup: 1 (the 32-head kernel) or 2 (the 64-head wide kernel).
 int default_tiles(int32_t) { return 1; }
 
 // Key ranges per (token, head group): enough workgroups to cover every compute unit, at least
@@ -72,7 +71,7 @@ bool plan_ok(const smla_plan *p, int32_t H)
 {
     if (p->splits < 1 || p->splits > kMaxSplits)
         return false;
-    if (p->tiles != 1)
+    if (p->tiles != 1 && p->tiles != 2)
         return false;
     return head_tiles(H) % p->tiles == 0;
 }
@@ -80,8 +79,8 @@ bool plan_ok(const smla_plan *p, int32_t H)
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Workspace layout under a valid plan: tickets [T, groups] int32 (zero between calls), then
-// FP32 partials [T, groups, splits, 32 tiles, 512], then (frame, sum) [T, groups, splits,
-// 32 tiles, 2].
+// FP32 partials [T, groups, splits, 32 tiles heads, 512], then (frame, sum) [T, groups,
+// splits, 32 tiles heads, 2].
 struct WsLayout {
     size_t counters, partials, ml, total;
 };
@@ -191,6 +190,8 @@ smla_status sparse_mla_decode(const void *q, int64_t q_stride_t, int64_t q_strid
         if (st != SMLA_OK)
             return st;
     }
+    if (chosen.tiles == 2 && !(row_bytes == 576 && qk_dim == 576))
+        return SMLA_EUNSUPPORTED;  // the 64-head kernel takes 576-byte rows, QK over all 576
     const size_t need = smla_decode_workspace_size(&chosen, T, H);
     if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
         return SMLA_EWORKSPACE;

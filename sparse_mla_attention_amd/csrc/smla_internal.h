@@ -22,16 +22,19 @@ struct DecodeParams {
     uint16_t *out;              // BF16 [T, H, 512]
     float *lse;                 // [T, H] or null
     int32_t lse_log2;           // 1: base-2 LSE
-    float *ws_o;                // FP32 partials [T, groups, splits, 32 tiles, 512] (splits > 1)
-    float *ws_ml;               // (frame, sum) [T, groups, splits, 32 tiles, 2] (splits > 1)
+    float *ws_o;                // FP32 partials [T, groups, splits, heads per group, 512]
+    float *ws_ml;               // (frame, sum) [T, groups, splits, heads per group, 2]
     int32_t *counters;          // arrival tickets [T, groups], zero between calls (splits > 1)
     int32_t splits;             // key ranges per (token, head group)
     int32_t groups;             // head groups per token = ceil(H / 32) / tiles
 };
 
-// Launch the decode (the split merge is fused into it) on `stream`.
+// Launch the decode (the split merge is fused into it) on `stream`: 32 heads per workgroup
+// (tiles = 1) or the wide kernel's 64 (tiles = 2).
 hipError_t launch_decode(const DecodeParams &p, int tiles, int row_bytes, int qk_dim,
                          bool two_term, hipStream_t stream);
+hipError_t launch_decode_wide(const DecodeParams &p, int row_bytes, int qk_dim, bool two_term,
+                              hipStream_t stream);
 
 struct LseMergeParams {
     const uint16_t *partials;   // BF16 [S, T, H, D]

@@ -1,0 +1,194 @@
+"""Parity of the 64-head (wide) decode kernel, plan tiles=2, with the FP64 oracle, and bit
+equality with the 32-head kernel: both run the same instructions per (column tile, head tile)
+in the same order (QK steps, frame rule, P bytes, P.V chunk order, l sums, split merge), so for
+the same split plan their outputs must agree bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_mla_attention_amd as smla
+from sparse_mla_attention_amd import inputs
+from smla_testlib import (EXACT_MAX_ABS, EXACT_REL_L2, FRAME_LIMIT, LSE_ABS, MIMIC_MAX_ABS,
+                          MIMIC_REL_L2, DeviceProblem, check_empty_rows_exact, log, lse_err,
+                          rel_l2)
+
+pytestmark = pytest.mark.gpu
+
+LN2 = np.log(2.0)
+
+
+def _exact(p, out, lse, lse_log2, label):
+    ref, ref_lse = oracle.decode_exact(p, lse_log2=lse_log2)
+    if lse_log2:
+        ref_lse, lse = ref_lse * LN2, lse * LN2
+    r, m, le = rel_l2(out, ref), float(np.abs(out - ref).max()), lse_err(lse, ref_lse)
+    log(f"{label}: rel_l2={r:.3e} max_abs={m:.3e} lse={le:.3e}")
+    assert np.all(np.isfinite(out)), "non-finite output"
+    tol_abs = EXACT_MAX_ABS * max(1.0, p.get("value_scale", 1.0))
+    assert r <= EXACT_REL_L2 and m <= tol_abs and le <= LSE_ABS, (r, m, le)
+
+
+def _mimic(p, out, lse, plan, label, check_max_abs=True):
+    """One-term path against mimic mode of the same plan.  Both quantize P to E4M3, but from
+    scores computed in FP32 (kernel) and FP64 (oracle): a P that sits within rounding distance
+    of an E4M3 midpoint may round to neighbouring codes on the two sides, one code step (1/16 to
+    1/8 of P) apart.  On unit-scale data that stays inside the max-abs tolerance; on softmaxes
+    dominated by a few keys (the large-score case) one such step moves an output by several
+    percent of a V value, so there only rel-L2 and the LSE are gated (that case is also held
+    bit-equal to the 32-head kernel)."""
+    ref, ref_lse = oracle.decode_mimic(p, splits=plan.splits, chunk=plan.chunk, terms=1,
+                                       frame_limit=FRAME_LIMIT)
+    r, m, le = rel_l2(out, ref), float(np.abs(out - ref).max()), lse_err(lse, ref_lse)
+    log(f"{label} vs mimic: rel_l2={r:.3e} max_abs={m:.3e} lse={le:.3e}")
+    tol_abs = MIMIC_MAX_ABS * max(1.0, p.get("value_scale", 1.0))
+    assert r <= MIMIC_REL_L2 and le <= LSE_ABS, (r, m, le)
+    if check_max_abs:
+        assert m <= tol_abs, (r, m, le)
+
+
+def _same_bits(d, p, splits, one_term):
+    """Run the 32-head and the 64-head kernel under the same split count; return both bit
+    patterns (out as int16, lse as int32)."""
+    res = []
+    for tiles in (1, 2):
+        d.run(plan=smla.make_plan(splits, tiles), one_term=one_term)
+        res.append((d.out.view(torch.int16).cpu().clone(), d.lse.view(torch.int32).cpu().clone()))
+    return res
+
+
+CASES = {
+    "H64_one_chunk": dict(seed=500, T=1, H=64, W=64),
+    "H128_ragged": dict(seed=501, T=3, H=128, W=300, lens=[300, 129, 77], neg_frac=0.1),
+    "H64_empty_rows": dict(seed=502, T=4, H=64, W=200, lens=[150, 0, -3, 200], neg_frac=0.05),
+    "H48_padded_heads": dict(seed=503, T=2, H=48, W=260, lens=[260, 61], sinks=True),
+    "H64_sinks_amax": dict(seed=504, T=3, H=64, W=390, kv_scale_to_amax=True, sinks=True,
+                           lens=[390, 5, 255], neg_frac=0.1),
+    "H64_large_scores": dict(seed=505, T=2, H=64, W=300, value_scale=4.0),
+    "H64_duplicates": dict(seed=506, T=2, H=64, W=200, duplicates=True, pool_rows=50),
+    "H64_W1": dict(seed=507, T=3, H=64, W=1, lens=[1, 0, 1]),
+}
+
+
+def _problem(name):
+    kw = dict(CASES[name])
+    seed, T, H, W = kw.pop("seed"), kw.pop("T"), kw.pop("H"), kw.pop("W")
+    if "lens" in kw:
+        kw["lens"] = np.array(kw["lens"])
+    kw.setdefault("pool_rows", 3000)
+    return inputs.random_problem(seed, T, H, W, **kw)
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_wide_exact_parity(name):
+    p = _problem(name)
+    log(f"wide case {name}")
+    d = DeviceProblem(p)
+    for splits in (1, 3):
+        for lse_log2 in (False, True):
+            out, lse, plan = d.run(plan=smla.make_plan(splits, 2), lse_log2=lse_log2)
+            check_empty_rows_exact(d.out, d.lse, p)
+            _exact(p, out, lse, lse_log2, f"{name} {plan} log2={lse_log2}")
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_wide_one_term_matches_mimic(name):
+    p = _problem(name)
+    d = DeviceProblem(p)
+    for splits in (1, 2):
+        plan = smla.make_plan(splits, 2)
+        out, lse, _ = d.run(plan=plan, one_term=True)
+        check_empty_rows_exact(d.out, d.lse, p)
+        _mimic(p, out, lse, plan, f"{name} {plan} one-term",
+               check_max_abs=name != "H64_large_scores")
+
+
+@pytest.mark.parametrize("name", list(CASES))
+@pytest.mark.parametrize("one_term", [False, True])
+def test_wide_equals_32_head_kernel_bitwise(name, one_term):
+    p = _problem(name)
+    d = DeviceProblem(p)
+    for splits in (1, 4):
+        (o1, l1), (o2, l2) = _same_bits(d, p, splits, one_term)
+        assert torch.equal(o1, o2), f"splits={splits}: outputs differ"
+        assert torch.equal(l1, l2), f"splits={splits}: LSE differs"
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 7, 16])
+def test_wide_split_plans(splits):
+    p = inputs.random_problem(520 + splits, 3, 64, 300, pool_rows=3000,
+                              lens=np.array([300, 40, 0]), neg_frac=0.1, sinks=True)
+    d = DeviceProblem(p)
+    out, lse, plan = d.run(plan=smla.make_plan(splits, 2))
+    check_empty_rows_exact(d.out, d.lse, p)
+    _exact(p, out, lse, False, f"wide splits={splits}")
+    out, lse, plan = d.run(plan=smla.make_plan(splits, 2), one_term=True)
+    _mimic(p, out, lse, plan, f"wide splits={splits} one-term")
+
+
+def test_wide_rising_scores_rerun_the_range():
+    """Scores climbing ~250 binades along the row: the first pass's frame offset passes the
+    limit and the range is computed again with a preset frame (same problem as the 32-head
+    kernel's test, at 64 heads)."""
+    from test_gpu_decode import _rising_scores_problem
+    p = _rising_scores_problem(530, 2, 64, 700, [700, 377])
+    d = DeviceProblem(p)
+    for splits in (1, 2):
+        plan = smla.make_plan(splits, 2)
+        out, lse, _ = d.run(plan=plan)
+        _exact(p, out, lse, False, f"wide rising scores splits={splits}")
+        out, lse, _ = d.run(plan=plan, one_term=True)
+        _mimic(p, out, lse, plan, f"wide rising scores splits={splits} one-term")
+        (o1, l1), (o2, l2) = _same_bits(d, p, splits, False)
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_wide_padded_q_strides():
+    p = inputs.random_problem(531, 2, 64, 150, pool_rows=2000)
+    d = DeviceProblem(p, q_pad_heads=16)
+    out, lse, _ = d.run(plan=smla.make_plan(1, 2))
+    _exact(p, out, lse, False, "wide padded q")
+
+
+def test_wide_verify_row_config():
+    p = inputs.CONFIGS["verify"]()
+    d = DeviceProblem(p)
+    for splits in (1, 2, 4):
+        out, lse, plan = d.run(plan=smla.make_plan(splits, 2))
+        check_empty_rows_exact(d.out, d.lse, p)
+        _exact(p, out, lse, p["lse_log2"], f"verify-row wide {plan}")
+
+
+def test_wide_graph_replay_matches_eager():
+    p = inputs.random_problem(532, 3, 128, 300, pool_rows=4000, neg_frac=0.1, sinks=True,
+                              lens=np.array([300, 0, 177]))
+    d = DeviceProblem(p)
+    plan = smla.make_plan(3, 2)
+    d.run(plan=plan, poison_out=False)
+    ref_out = d.out.view(torch.int16).clone()
+    ref_lse = d.lse.view(torch.int32).clone()
+    ws = d.workspace(plan)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+
+    def call(stream):
+        smla.sparse_mla_decode(d.q, d.kv_a, d.indices, d.lens, p["bmm1"], p["bmm2"], d.out,
+                               d.lse, sinks=d.sinks, plan=plan, workspace=ws, stream=stream)
+    with torch.cuda.stream(s):
+        call(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        call(s)
+        call(s)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        d.out.view(torch.int16).fill_(0x7FC0)
+        d.lse.fill_(float("nan"))
+        junk = torch.randn(1 << 16, device="cuda").sum()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(d.out.view(torch.int16), ref_out), f"replay {rep}: out differs"
+        assert torch.equal(d.lse.view(torch.int32), ref_lse), f"replay {rep}: lse differs"
+        del junk
