@@ -61,7 +61,10 @@ typedef int32_t smla_status;
  * merges the FP32 partials of all of them. */
 typedef struct smla_plan {
     int32_t splits; /* 1 .. 64 */
-    int32_t tiles;  /* 32-head tiles per workgroup: 1 in this build */
+    int32_t tiles;  /* 32-head tiles per workgroup: 1 (32 heads, rows loaded into registers) or
+                       2 (64 heads, rows gathered straight into LDS; needs an even number of
+                       32-head tiles and ranges of at most 2048 columns, ceil(W / splits) <=
+                       2048, else SMLA_EUNSUPPORTED) */
     int32_t chunk;  /* columns per gathered chunk (64 in this build; output only) */
     int32_t reserved;
 } smla_plan;

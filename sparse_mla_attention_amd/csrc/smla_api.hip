@@ -190,8 +190,8 @@ smla_status sparse_mla_decode(const void *q, int64_t q_stride_t, int64_t q_strid
         if (st != SMLA_OK)
             return st;
     }
-    if (chosen.tiles == 2 && !(row_bytes == 576 && qk_dim == 576))
-        return SMLA_EUNSUPPORTED;  // the 64-head kernel takes 576-byte rows, QK over all 576
+    if (chosen.tiles == 2 && (W + chosen.splits - 1) / chosen.splits > smla::G64_MAX_RANGE)
+        return SMLA_EUNSUPPORTED;  // the 64-head kernel stages a range's indices in LDS
     const size_t need = smla_decode_workspace_size(&chosen, T, H);
     if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
         return SMLA_EWORKSPACE;

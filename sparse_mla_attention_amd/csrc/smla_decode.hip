@@ -663,7 +663,7 @@ hipError_t launch_decode(const DecodeParams &p, int tiles, int row_bytes, int qk
                          bool two_term, hipStream_t stream)
 {
     if (tiles == 2)
-        return launch_decode_wide(p, row_bytes, qk_dim, two_term, stream);
+        return launch_decode_g64(p, row_bytes, qk_dim, two_term, stream);
     if (tiles != 1)
         return hipErrorInvalidValue;
     return two_term ? launch_shape<true>(p, row_bytes, qk_dim, stream)

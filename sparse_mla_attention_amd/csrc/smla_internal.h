@@ -29,12 +29,16 @@ struct DecodeParams {
     int32_t groups;             // head groups per token = ceil(H / 32) / tiles
 };
 
+// Longest key range (columns) the 64-head kernel takes: its range's row indices are staged in
+// LDS.  The host picks or checks split counts against it.
+constexpr int G64_MAX_RANGE = 2048;
+
 // Launch the decode (the split merge is fused into it) on `stream`: 32 heads per workgroup
-// (tiles = 1) or the wide kernel's 64 (tiles = 2).
+// (tiles = 1) or the 64-head kernel (tiles = 2).
 hipError_t launch_decode(const DecodeParams &p, int tiles, int row_bytes, int qk_dim,
                          bool two_term, hipStream_t stream);
-hipError_t launch_decode_wide(const DecodeParams &p, int row_bytes, int qk_dim, bool two_term,
-                              hipStream_t stream);
+hipError_t launch_decode_g64(const DecodeParams &p, int row_bytes, int qk_dim, bool two_term,
+                             hipStream_t stream);
 
 struct LseMergeParams {
     const uint16_t *partials;   // BF16 [S, T, H, D]

@@ -27,6 +27,21 @@ FRAME_LIMIT = 96
 # a half-ulp of 2^-9..2^-8 relative, uniformly distributed).
 MIMIC_REL_L2 = 3e-3
 MIMIC_MAX_ABS = 1e-2
+# Both sides round P to E4M3, the kernel from FP32 scores and the oracle from FP64 ones, so a P
+# that lies within rounding distance of an E4M3 midpoint can land one code step apart (up to
+# 32 of the 448 anchor).  On unit-scale rows of a few hundred keys such a flip moves an output
+# element by up to ~1e-2 (step 32 x |v| ~ 3 over a row sum ~ 1e4): a handful of isolated
+# outputs may exceed MIMIC_MAX_ABS, none may exceed the exact-mode gate.
+MIMIC_FLIP_FRACTION = 1e-4
+
+
+def mimic_max_abs_ok(out, ref, tol: float, cap: float) -> bool:
+    """Max-abs parity with mimic mode: every |out - ref| <= tol, except at most a fraction
+    MIMIC_FLIP_FRACTION of the elements (one-code E4M3 flips), which must stay <= cap."""
+    err = np.abs(np.asarray(out) - np.asarray(ref))
+    if float(err.max()) <= tol:
+        return True
+    return float(err.max()) <= cap and float((err > tol).mean()) <= MIMIC_FLIP_FRACTION
 
 
 def log(msg: str) -> None:

@@ -78,10 +78,12 @@ def test_decode_rejects_bad_arguments(kw):
     assert _decode(**kw) == smla.SMLA_EINVAL
 
 
-def test_wide_plan_takes_576_byte_rows_only():
-    wide = smla.make_plan(1, 2)
-    assert _decode(H=64, row_bytes=512, qk_dim=512, plan=wide) == smla.SMLA_EUNSUPPORTED
-    assert _decode(H=64, row_bytes=576, qk_dim=512, plan=wide) == smla.SMLA_EUNSUPPORTED
+def test_64_head_plan_limits_the_range_length():
+    """The 64-head kernel stages a key range's row indices in LDS (at most 2048 columns): a plan
+    whose ranges could be longer is refused before anything is launched."""
+    g64 = smla.make_plan(1, 2)
+    assert _decode(H=64, W=4096, plan=g64) == smla.SMLA_EUNSUPPORTED
+    assert _decode(H=64, W=2049, plan=g64) == smla.SMLA_EUNSUPPORTED
 
 
 def test_decode_rejects_missing_or_small_workspace():

@@ -1,7 +1,7 @@
-"""Parity of the 64-head (wide) decode kernel, plan tiles=2, with the FP64 oracle, and bit
-equality with the 32-head kernel: both run the same instructions per (column tile, head tile)
-in the same order (QK steps, frame rule, P bytes, P.V chunk order, l sums, split merge), so for
-the same split plan their outputs must agree bit for bit."""
+"""Parity of the 64-head decode kernel (plan tiles=2: rows gathered straight into LDS) with the
+FP64 oracle, and bit equality with the 32-head kernel: both run the same instructions per
+(column tile, head tile) in the same order (QK steps, frame rule, P bytes, P.V chunk order, l
+sums, split merge), so for the same split plan their outputs must agree bit for bit."""
 import numpy as np
 import pytest
 import torch
@@ -11,7 +11,7 @@ import sparse_mla_attention_amd as smla
 from sparse_mla_attention_amd import inputs
 from smla_testlib import (EXACT_MAX_ABS, EXACT_REL_L2, FRAME_LIMIT, LSE_ABS, MIMIC_MAX_ABS,
                           MIMIC_REL_L2, DeviceProblem, check_empty_rows_exact, log, lse_err,
-                          rel_l2)
+                          mimic_max_abs_ok, rel_l2)
 
 pytestmark = pytest.mark.gpu
 
@@ -44,7 +44,7 @@ def _mimic(p, out, lse, plan, label, check_max_abs=True):
     tol_abs = MIMIC_MAX_ABS * max(1.0, p.get("value_scale", 1.0))
     assert r <= MIMIC_REL_L2 and le <= LSE_ABS, (r, m, le)
     if check_max_abs:
-        assert m <= tol_abs, (r, m, le)
+        assert mimic_max_abs_ok(out, ref, tol_abs, EXACT_MAX_ABS * max(1.0, p.get("value_scale", 1.0))), (r, m, le)
 
 
 def _same_bits(d, p, splits, one_term):
@@ -67,6 +67,12 @@ CASES = {
     "H64_large_scores": dict(seed=505, T=2, H=64, W=300, value_scale=4.0),
     "H64_duplicates": dict(seed=506, T=2, H=64, W=200, duplicates=True, pool_rows=50),
     "H64_W1": dict(seed=507, T=3, H=64, W=1, lens=[1, 0, 1]),
+    "H64_rows512_two_pools": dict(seed=508, T=3, H=64, W=300, row_bytes=512, two_pools=True,
+                                  split_col=128, rows_b=5000, sinks=True, neg_frac=0.1,
+                                  lens=[300, 129, 250]),
+    "H128_rows576_qk512": dict(seed=509, T=2, H=128, W=200, qk_dim=512, lens=[200, 71]),
+    "H64_long_range": dict(seed=510, T=2, H=64, W=2048, lens=[2048, 1000], neg_frac=0.05,
+                           pool_rows=6000),
 }
 
 
@@ -80,9 +86,9 @@ def _problem(name):
 
 
 @pytest.mark.parametrize("name", list(CASES))
-def test_wide_exact_parity(name):
+def test_g64_exact_parity(name):
     p = _problem(name)
-    log(f"wide case {name}")
+    log(f"64-head case {name}")
     d = DeviceProblem(p)
     for splits in (1, 3):
         for lse_log2 in (False, True):
@@ -92,7 +98,7 @@ def test_wide_exact_parity(name):
 
 
 @pytest.mark.parametrize("name", list(CASES))
-def test_wide_one_term_matches_mimic(name):
+def test_g64_one_term_matches_mimic(name):
     p = _problem(name)
     d = DeviceProblem(p)
     for splits in (1, 2):
@@ -105,7 +111,7 @@ def test_wide_one_term_matches_mimic(name):
 
 @pytest.mark.parametrize("name", list(CASES))
 @pytest.mark.parametrize("one_term", [False, True])
-def test_wide_equals_32_head_kernel_bitwise(name, one_term):
+def test_g64_equals_32_head_kernel_bitwise(name, one_term):
     p = _problem(name)
     d = DeviceProblem(p)
     for splits in (1, 4):
@@ -115,18 +121,18 @@ def test_wide_equals_32_head_kernel_bitwise(name, one_term):
 
 
 @pytest.mark.parametrize("splits", [1, 2, 3, 7, 16])
-def test_wide_split_plans(splits):
+def test_g64_split_plans(splits):
     p = inputs.random_problem(520 + splits, 3, 64, 300, pool_rows=3000,
                               lens=np.array([300, 40, 0]), neg_frac=0.1, sinks=True)
     d = DeviceProblem(p)
     out, lse, plan = d.run(plan=smla.make_plan(splits, 2))
     check_empty_rows_exact(d.out, d.lse, p)
-    _exact(p, out, lse, False, f"wide splits={splits}")
+    _exact(p, out, lse, False, f"64-head splits={splits}")
     out, lse, plan = d.run(plan=smla.make_plan(splits, 2), one_term=True)
-    _mimic(p, out, lse, plan, f"wide splits={splits} one-term")
+    _mimic(p, out, lse, plan, f"64-head splits={splits} one-term")
 
 
-def test_wide_rising_scores_rerun_the_range():
+def test_g64_rising_scores_rerun_the_range():
     """Scores climbing ~250 binades along the row: the first pass's frame offset passes the
     limit and the range is computed again with a preset frame (same problem as the 32-head
     kernel's test, at 64 heads)."""
@@ -136,30 +142,30 @@ def test_wide_rising_scores_rerun_the_range():
     for splits in (1, 2):
         plan = smla.make_plan(splits, 2)
         out, lse, _ = d.run(plan=plan)
-        _exact(p, out, lse, False, f"wide rising scores splits={splits}")
+        _exact(p, out, lse, False, f"64-head rising scores splits={splits}")
         out, lse, _ = d.run(plan=plan, one_term=True)
-        _mimic(p, out, lse, plan, f"wide rising scores splits={splits} one-term")
+        _mimic(p, out, lse, plan, f"64-head rising scores splits={splits} one-term")
         (o1, l1), (o2, l2) = _same_bits(d, p, splits, False)
         assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
-def test_wide_padded_q_strides():
+def test_g64_padded_q_strides():
     p = inputs.random_problem(531, 2, 64, 150, pool_rows=2000)
     d = DeviceProblem(p, q_pad_heads=16)
     out, lse, _ = d.run(plan=smla.make_plan(1, 2))
-    _exact(p, out, lse, False, "wide padded q")
+    _exact(p, out, lse, False, "64-head padded q")
 
 
-def test_wide_verify_row_config():
+def test_g64_verify_row_config():
     p = inputs.CONFIGS["verify"]()
     d = DeviceProblem(p)
     for splits in (1, 2, 4):
         out, lse, plan = d.run(plan=smla.make_plan(splits, 2))
         check_empty_rows_exact(d.out, d.lse, p)
-        _exact(p, out, lse, p["lse_log2"], f"verify-row wide {plan}")
+        _exact(p, out, lse, p["lse_log2"], f"verify-row 64-head {plan}")
 
 
-def test_wide_graph_replay_matches_eager():
+def test_g64_graph_replay_matches_eager():
     p = inputs.random_problem(532, 3, 128, 300, pool_rows=4000, neg_frac=0.1, sinks=True,
                               lens=np.array([300, 0, 177]))
     d = DeviceProblem(p)
