@@ -76,7 +76,7 @@ smla_status smla_decode_plan(int32_t T, int32_t H, int32_t W, int32_t row_bytes,
                              smla_plan *plan);
 
 /* Workspace bytes sparse_mla_decode needs under `plan` (0 when plan->splits == 1): arrival
- * tickets (one int32 per token and head group, rounded up to 256 bytes), FP32 partials
+ * counters (two int32 per token and head group, rounded up to 256 bytes), FP32 partials
  * [T, groups, splits, 32 tiles, 512] and (frame, sum) pairs [T, groups, splits, 32 tiles, 2],
  * groups = ceil(H / 32) / tiles.  0 for a bad plan. */
 size_t smla_decode_workspace_size(const smla_plan *plan, int32_t T, int32_t H);
@@ -106,7 +106,7 @@ size_t smla_decode_workspace_size(const smla_plan *plan, int32_t T, int32_t H);
  *                bit-identical from run to run for a fixed plan).
  *   workspace    device scratch of workspace_bytes >= smla_decode_workspace_size(plan, T, H),
  *                16-byte aligned (may be NULL when that size is 0).  Zero-fill it once before
- *                its first use: its first bytes hold arrival tickets that must start at zero,
+ *                its first use: its first bytes hold arrival counters that must start at zero,
  *                and every call leaves them at zero again (the rest is overwritten before it
  *                is read).  Calls that share a workspace must be stream-ordered.
  *

@@ -78,7 +78,8 @@ bool plan_ok(const smla_plan *p, int32_t H)
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Workspace layout under a valid plan: tickets [T, groups] int32 (zero between calls), then
+// Workspace layout under a valid plan: counters [T, groups, 2] int32 (arrival ticket and
+// ready count, zero between calls), then
 // FP32 partials [T, groups, splits, 32 tiles heads, 512], then (frame, sum) [T, groups,
 // splits, 32 tiles heads, 2].
 struct WsLayout {
@@ -92,7 +93,7 @@ WsLayout ws_layout(const smla_plan *plan, int32_t T, int32_t H)
     const size_t units = (size_t)T * groups * (size_t)plan->splits;
     WsLayout w;
     w.counters = 0;
-    w.partials = align256((size_t)T * groups * sizeof(int32_t));
+    w.partials = align256((size_t)T * groups * 2 * sizeof(int32_t));
     w.ml = w.partials + units * hg * 512 * sizeof(float);
     w.total = w.ml + units * hg * 2 * sizeof(float);
     return w;

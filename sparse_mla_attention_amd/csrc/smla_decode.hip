@@ -167,7 +167,7 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(DecodeParams a)
             __syncthreads();
             int *ticket = reinterpret_cast<int *>(lds + L::MISC);
             if (tid == 0)
-                *ticket = __hip_atomic_fetch_add(a.counters + tg, 1, __ATOMIC_RELAXED,
+                *ticket = __hip_atomic_fetch_add(a.counters + 2 * tg, 1, __ATOMIC_RELAXED,
                                                  __HIP_MEMORY_SCOPE_AGENT);
             __syncthreads();
             if (*ticket != a.splits - 1)
@@ -198,7 +198,7 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(DecodeParams a)
             }
             g_h = big_g;
             if (tid == 0)  // every range has arrived: ready for the next call
-                __hip_atomic_store(a.counters + tg, 0, __ATOMIC_RELAXED,
+                __hip_atomic_store(a.counters + 2 * tg, 0, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
         }
 

@@ -24,7 +24,8 @@ struct DecodeParams {
     int32_t lse_log2;           // 1: base-2 LSE
     float *ws_o;                // FP32 partials [T, groups, splits, heads per group, 512]
     float *ws_ml;               // (frame, sum) [T, groups, splits, heads per group, 2]
-    int32_t *counters;          // arrival tickets [T, groups], zero between calls (splits > 1)
+    int32_t *counters;          // [T, groups, 2]: arrival ticket, ready count; zero between
+                                // calls (splits > 1)
     int32_t splits;             // key ranges per (token, head group)
     int32_t groups;             // head groups per token = ceil(H / 32) / tiles
 };

@@ -82,16 +82,16 @@ class DeviceProblem:
         self.lse = torch.empty((T, H), dtype=torch.float32, device=device)
 
     def workspace(self, plan):
-        """The problem's workspace for `plan`: tickets zero (they are zero between calls), the
+        """The problem's workspace for `plan`: counters zero (they are zero between calls), the
         rest NaN garbage, which the kernels must overwrite before reading."""
         nbytes = smla.workspace_size(plan, self.T, self.H)
         if not nbytes:
             return None
         groups = ((self.H + 31) // 32) // plan.tiles
-        tickets = (self.T * groups * 4 + 255) // 256 * 256
+        counters = (self.T * groups * 2 * 4 + 255) // 256 * 256
         ws = torch.empty(nbytes, dtype=torch.uint8, device=self.q.device)
-        ws[:tickets].zero_()
-        ws[tickets:].fill_(0xFF)
+        ws[:counters].zero_()
+        ws[counters:].fill_(0xFF)
         return ws
 
     def run(self, plan=None, one_term=False, lse_log2=None, poison_out=True):

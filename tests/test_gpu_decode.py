@@ -179,12 +179,12 @@ def test_padded_q_strides():
 
 def test_repeated_calls_are_deterministic():
     """Split ranges finish in any order; the merge sums them in range order, so repeated
-    calls on one workspace (whose tickets each call leaves at zero) agree bit for bit."""
+    calls on one workspace (whose arrival counters each call leaves at zero) agree bit for bit."""
     p = inputs.random_problem(401, 4, 64, 500, pool_rows=6000, neg_frac=0.1)
     d = DeviceProblem(p)
     plan = smla.make_plan(3, 1)
     ws = d.workspace(plan)
-    tickets = (d.T * 2 * 4 + 255) // 256 * 256  # 64 heads: two groups of 32
+    counters = (d.T * 2 * 2 * 4 + 255) // 256 * 256  # 64 heads: two groups of 32
 
     def call():
         smla.sparse_mla_decode(d.q, d.kv_a, d.indices, d.lens, p["bmm1"], p["bmm2"], d.out,
@@ -195,7 +195,7 @@ def test_repeated_calls_are_deterministic():
     for _ in range(5):
         call()
         assert torch.equal(d.out.view(torch.int16).cpu(), a)
-        assert int(ws[:tickets].count_nonzero()) == 0, "tickets not reset"
+        assert int(ws[:counters].count_nonzero()) == 0, "arrival counters not reset"
     out, lse, _ = d.run(plan=plan)
     _check_exact(p, out, lse, False, "repeated calls")
 
