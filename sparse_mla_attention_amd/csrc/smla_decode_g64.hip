@@ -350,8 +350,13 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
         const int r = lane & 15, g = lane >> 4;    // row r of a 16-key tile, lane group g
         const int head = 16 * w + r;               // this lane's head within the group
 
-        // Q fragments, B operand of QK: lane (n, g) holds, for head 16 w + n and step s, the q
-        // pieces 8 s + g and 8 s + 4 + g, and the rope piece 32 + g.
+        // Which 16-byte pieces lane group g holds (the same for Q and K, so the products are
+        // unchanged): latent pieces 8 s + pg and 8 s + 4 + pg of step s, rope piece 32 + pr.
+        // The two lane groups that share an LDS pass (g = 2h, 2h + 1) then read disjoint bank
+        // sets under the row swizzles below, so the K reads run without bank conflicts.
+        const int pg = ((g & 1) << 1) | (g >> 1);
+        const int pr = g ^ ((g & 1) << 1);
+        // Q fragments, B operand of QK: lane (n, g) holds head 16 w + n.
         v8i qf[4];
         v4i qt = v4i{0, 0, 0, 0};
         {
@@ -361,17 +366,17 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
             const int keep = live ? -1 : 0;        // padding heads keep zeros
 #pragma unroll
             for (int s = 0; s < 4; s++)
-                qf[s] = join(gload(qp + 16 * (8 * s + g)) & keep,
-                             gload(qp + 16 * (8 * s + 4 + g)) & keep);
+                qf[s] = join(gload(qp + 16 * (8 * s + pg)) & keep,
+                             gload(qp + 16 * (8 * s + 4 + pg)) & keep);
             if (TAIL)
-                qt = gload(qp + 16 * (32 + g)) & keep;
+                qt = gload(qp + 16 * (32 + pr)) & keep;
         }
 
-        // per-lane LDS offsets (loop invariant): pieces g and 4 + g of slice s of row 16 kt + r
-        // at kb0 / kb1 + s * SLICE + kt * 2048; rope piece 32 + g at rb + kt * 1024
-        const int kb0 = r * 128 + 16 * (g ^ fsw(r));
-        const int kb1 = r * 128 + 16 * ((4 + g) ^ fsw(r));
-        const int rb = L::LAT + r * 64 + 16 * (g ^ ((r >> 2) & 3));
+        // per-lane LDS offsets (loop invariant): pieces pg and 4 + pg of slice s of row 16 kt + r
+        // at kb0 / kb1 + s * SLICE + kt * 2048; rope piece 32 + pr at rb + kt * 1024
+        const int kb0 = r * 128 + 16 * (pg ^ fsw(r));
+        const int kb1 = r * 128 + 16 * ((4 + pg) ^ fsw(r));
+        const int rb = L::LAT + r * 64 + 16 * (pr ^ ((r >> 2) & 3));
         int pw[4];                                 // P bytes of key tile kt in a P buffer
 #pragma unroll
         for (int kt = 0; kt < 4; kt++)
@@ -391,34 +396,56 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
             const uint8_t *slot = lds + (x % SLOTS) * L::SLOTB;
             const uint8_t *ab = reinterpret_cast<const uint8_t *>(addr) + x * CHUNK * 8;
             const uint64_t mk = __ballot(lds_load<uint64_t>(ab, lane * 8) != zero);
+            // every K fragment of the chunk is read first (in the order the products use them),
+            // and the products run step-major over the four independent key-tile chains
+            v8i av[4][4];
+            v4i rr[4];
+#pragma unroll
+            for (int s = 0; s < 4; s++)
+#pragma unroll
+                for (int kt = 0; kt < 4; kt++)
+                    av[s][kt] = join(lds_load<v4i>(slot + s * SLICE + kt * 2048, kb0),
+                                     lds_load<v4i>(slot + s * SLICE + kt * 2048, kb1));
+            if constexpr (TAIL) {
+#pragma unroll
+                for (int kt = 0; kt < 4; kt++)
+                    rr[kt] = lds_load<v4i>(slot + kt * 1024, rb);
+            }
             v4f sc[4];
 #pragma unroll
-            for (int kt = 0; kt < 4; kt++) {
-                v4f c = v4f{0.f, 0.f, 0.f, 0.f};
+            for (int kt = 0; kt < 4; kt++)
+                sc[kt] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int s = 0; s < 4; s++) {
-                    const v8i av = join(lds_load<v4i>(slot + s * SLICE + kt * 2048, kb0),
-                                        lds_load<v4i>(slot + s * SLICE + kt * 2048, kb1));
-                    c = mfma16(av, qf[s], c);
-                }
-                if constexpr (TAIL) {
-                    const v4i rr = lds_load<v4i>(slot + kt * 1024, rb);
+            for (int s = 0; s < 4; s++)
 #pragma unroll
-                    for (int q2 = 0; q2 < 2; q2++)
-                        c = mfma16k32(v2i{rr[2 * q2], rr[2 * q2 + 1]},
-                                      v2i{qt[2 * q2], qt[2 * q2 + 1]}, c);
-                }
-                sc[kt] = c;
+                for (int kt = 0; kt < 4; kt++)
+                    sc[kt] = mfma16(av[s][kt], qf[s], sc[kt]);
+            if constexpr (TAIL) {
+#pragma unroll
+                for (int q2 = 0; q2 < 2; q2++)
+#pragma unroll
+                    for (int kt = 0; kt < 4; kt++)
+                        sc[kt] = mfma16k32(v2i{rr[kt][2 * q2], rr[kt][2 * q2 + 1]},
+                                           v2i{qt[2 * q2], qt[2 * q2 + 1]}, sc[kt]);
             }
+            // the scheduler keeps this order: every K read of the chunk, then the products
+            __builtin_amdgcn_sched_group_barrier(0x100, TAIL ? 36 : 32, 0);  // LDS reads
+            __builtin_amdgcn_sched_group_barrier(0x008, TAIL ? 24 : 16, 0);  // MFMA
+            // active-column bits of this lane's keys 16 kt + 4 g + i: bit 16 (kt & 1) + i of
+            // word kt >> 1
             const uint64_t bits = mk >> (4 * g);
+            const uint32_t word[2] = {(uint32_t)bits, (uint32_t)(bits >> 32)};
             mfma_result_pad();
             float mx = -INFINITY;
 #pragma unroll
             for (int kt = 0; kt < 4; kt++) {
 #pragma unroll
                 for (int i = 0; i < 4; i++) {
-                    const float b = ((bits >> (16 * kt + i)) & 1u) ? 0.0f : -INFINITY;
-                    sc[kt][i] = fmaf(sc[kt][i], a.scale_log2, b);
+                    // all ones for an active column, else zero; a masked score becomes -inf
+                    const int on = (int)(word[kt >> 1] << (31 - (16 * (kt & 1) + i))) >> 31;
+                    const float v = sc[kt][i] * a.scale_log2;
+                    sc[kt][i] = __uint_as_float((__float_as_uint(v) & (uint32_t)on) |
+                                                (0xFF800000u & ~(uint32_t)on));
                     mx = fmaxf(mx, sc[kt][i]);
                 }
             }
@@ -446,25 +473,21 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
 #pragma unroll
             for (int kt = 0; kt < 4; kt++) {
                 float p[4];
-                float lsum = 0.0f;
 #pragma unroll
-                for (int i = 0; i < 4; i++) {
+                for (int i = 0; i < 4; i++)
                     p[i] = __builtin_amdgcn_exp2f(sc[kt][i] - fb);  // exp2(-inf) = 0
-                    lsum += p[i];
-                }
+                const float lsum = ((p[0] + p[1]) + p[2]) + p[3];
                 l_lane[kt] = ldexpf(l_lane[kt], shift) + lsum;
                 int hi = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
                 hi = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], hi, true);
                 *reinterpret_cast<int *>(pbase + pw[kt]) = hi;
                 if constexpr (TWO) {
-                    const float h0 = __builtin_amdgcn_cvt_f32_fp8(hi, 0);
-                    const float h1 = __builtin_amdgcn_cvt_f32_fp8(hi, 1);
-                    const float h2 = __builtin_amdgcn_cvt_f32_fp8(hi, 2);
-                    const float h3 = __builtin_amdgcn_cvt_f32_fp8(hi, 3);
-                    int lo = __builtin_amdgcn_cvt_pk_fp8_f32(16.0f * (p[0] - h0),
-                                                             16.0f * (p[1] - h1), 0, false);
-                    lo = __builtin_amdgcn_cvt_pk_fp8_f32(16.0f * (p[2] - h2),
-                                                         16.0f * (p[3] - h3), lo, true);
+                    const v2f h01 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
+                    const v2f h23 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
+                    int lo = __builtin_amdgcn_cvt_pk_fp8_f32(16.0f * (p[0] - h01[0]),
+                                                             16.0f * (p[1] - h01[1]), 0, false);
+                    lo = __builtin_amdgcn_cvt_pk_fp8_f32(16.0f * (p[2] - h23[0]),
+                                                         16.0f * (p[3] - h23[1]), lo, true);
                     *reinterpret_cast<int *>(pbase + L::PTERM + pw[kt]) = lo;
                 }
             }
