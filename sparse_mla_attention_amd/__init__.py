@@ -109,6 +109,24 @@ def make_plan(splits: int, tiles: int) -> Plan:
     return Plan(splits, tiles, 64, 0)
 
 
+def _decode_args(q, kv_a, indices, lens, bmm1_scale, bmm2_scale, out, lse, kv_b, split_col,
+                 sinks, qk_dim, lse_log2, one_term, plan, workspace, stream):
+    T, H, qd = q.shape
+    W = indices.shape[1]
+    row_bytes = kv_a.shape[1]
+    qk_dim = qd if qk_dim is None else qk_dim
+    flags = (SMLA_LSE_LOG2 if lse_log2 else 0) | (SMLA_P_ONE_TERM if one_term else 0)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return (_ptr(q), q.stride(0) * q.element_size(), q.stride(1) * q.element_size(),
+            _ptr(kv_a), kv_a.shape[0],
+            _ptr(kv_b), 0 if kv_b is None else kv_b.shape[0],
+            W if split_col is None else int(split_col),
+            row_bytes, qk_dim, _ptr(indices), _ptr(lens), T, H, W,
+            float(bmm1_scale), float(bmm2_scale), _ptr(sinks), _ptr(out), _ptr(lse), flags,
+            None if plan is None else ctypes.byref(plan), _ptr(workspace), ws_bytes,
+            _stream(stream))
+
+
 def sparse_mla_decode(q, kv_a, indices, lens, bmm1_scale, bmm2_scale, out, lse=None, *,
                       kv_b=None, split_col=None, sinks=None, qk_dim=None, lse_log2=False,
                       one_term=False, plan=None, workspace=None, stream=None):
@@ -120,24 +138,33 @@ def sparse_mla_decode(q, kv_a, indices, lens, bmm1_scale, bmm2_scale, out, lse=N
     workspace: a uint8 device tensor of at least workspace_size(plan, T, H) bytes when the plan
     splits the columns (None otherwise), zero-filled before its first use (see
     new_workspace)."""
-    T, H, qd = q.shape
-    W = indices.shape[1]
-    row_bytes = kv_a.shape[1]
-    qk_dim = qd if qk_dim is None else qk_dim
-    flags = (SMLA_LSE_LOG2 if lse_log2 else 0) | (SMLA_P_ONE_TERM if one_term else 0)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = _load().sparse_mla_decode(
-        _ptr(q), q.stride(0) * q.element_size(), q.stride(1) * q.element_size(),
-        _ptr(kv_a), kv_a.shape[0],
-        _ptr(kv_b), 0 if kv_b is None else kv_b.shape[0],
-        W if split_col is None else int(split_col),
-        row_bytes, qk_dim, _ptr(indices), _ptr(lens), T, H, W,
-        float(bmm1_scale), float(bmm2_scale), _ptr(sinks), _ptr(out), _ptr(lse), flags,
-        None if plan is None else ctypes.byref(plan), _ptr(workspace), ws_bytes,
-        _stream(stream))
+    st = _load().sparse_mla_decode(*_decode_args(
+        q, kv_a, indices, lens, bmm1_scale, bmm2_scale, out, lse, kv_b, split_col, sinks,
+        qk_dim, lse_log2, one_term, plan, workspace, stream))
     if st != SMLA_OK:
         raise SmlaError(st, "sparse_mla_decode")
     return out, lse
+
+
+def prepare_decode(q, kv_a, indices, lens, bmm1_scale, bmm2_scale, out, lse=None, *,
+                   kv_b=None, split_col=None, sinks=None, qk_dim=None, lse_log2=False,
+                   one_term=False, plan=None, workspace=None, stream=None):
+    """The same call with its arguments converted once, for loops that launch it repeatedly on
+    the same buffers: returns a function of no arguments that launches it (on `stream`, else on
+    the stream current when this was called) and raises SmlaError on a bad status.  The tensors
+    must stay alive and in place while the function is used."""
+    f = _load().sparse_mla_decode
+    args = _decode_args(q, kv_a, indices, lens, bmm1_scale, bmm2_scale, out, lse, kv_b,
+                        split_col, sinks, qk_dim, lse_log2, one_term, plan, workspace, stream)
+    keep = (q, kv_a, indices, lens, out, lse, kv_b, sinks, plan, workspace)
+
+    def launch():
+        st = f(*args)
+        if st != SMLA_OK:
+            raise SmlaError(st, "sparse_mla_decode")
+        return keep[4], keep[5]
+
+    return launch
 
 
 def lse_merge(partials, lse2, out, lse_out=None, *, lse_log2=False, stream=None):

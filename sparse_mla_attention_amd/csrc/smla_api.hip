@@ -16,6 +16,7 @@ constexpr int kMaxDevices = 64;
 constexpr int kMaxSplits = 64;
 constexpr int kChunk = 64;
 constexpr int kDefaultMaxSplits = 4;
+constexpr int kFewChunks = 6;
 std::atomic<int> g_cu_count[kMaxDevices];
 
 // Compute units of the current device, queried once per device.
@@ -49,21 +50,37 @@ bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
 
 int32_t head_tiles(int32_t H) { return (H + 31) / 32; }
 
-// 32-head tiles per workgroup: 1 (the 32-head kernel) or 2 (the 64-head wide kernel).
-int default_tiles(int32_t) { return 1; }
-
-// Key ranges per (token, head group): enough workgroups to cover every compute unit, at least
-// one chunk of columns per range, and at most kDefaultMaxSplits ranges (the last range of a
-// (token, head group) reads every other range's partial to merge them).
-int default_splits(int32_t T, int32_t groups, int32_t W, int cus)
+// 32-head tiles per workgroup: 2 (the 64-head kernel, which gathers each row once for 64
+// heads) when the head tiles pair up and its units alone cover at least half of the compute
+// units; 1 (the 32-head kernel) for small batches, where its shorter fixed path wins.
+int default_tiles(int32_t T, int32_t H, int cus)
 {
+    const int64_t ht = head_tiles(H);
+    if (ht % 2 != 0)
+        return 1;
+    return (int64_t)T * (ht / 2) * 2 >= cus ? 2 : 1;
+}
+
+// Key ranges per (token, head group): one range when a token has at most kFewChunks chunks of
+// columns (a split merge costs more than it saves there); else enough workgroups to cover every
+// compute unit, at most kDefaultMaxSplits ranges (the last range of a (token, head group) reads
+// every other range's partial to merge them) and at least one chunk of columns per range.  The
+// 64-head kernel also needs ranges of at most G64_MAX_RANGE columns.
+int default_splits(int32_t T, int32_t groups, int32_t W, int cus, int tiles)
+{
+    const int64_t chunks = (W + kChunk - 1) / kChunk;
+    const int64_t need = tiles == 2 ? (W + smla::G64_MAX_RANGE - 1) / smla::G64_MAX_RANGE : 1;
+    if (chunks <= kFewChunks)
+        return (int)need;
     const int64_t units = (int64_t)T * groups;
     int64_t want = units > 0 ? (cus + units - 1) / units : 1;
-    int64_t cap = (W + kChunk - 1) / kChunk;
+    int64_t cap = chunks;
     if (cap > kDefaultMaxSplits)
         cap = kDefaultMaxSplits;
     if (want > cap)
         want = cap;
+    if (want < need)
+        want = need;
     return want < 1 ? 1 : (int)want;
 }
 
@@ -127,8 +144,8 @@ smla_status smla_decode_plan(int32_t T, int32_t H, int32_t W, int32_t row_bytes,
     int cus = 0;
     if (current_cu_count(&cus) != hipSuccess)
         return SMLA_EHIP;
-    plan->tiles = default_tiles(H);
-    plan->splits = default_splits(T, head_tiles(H) / plan->tiles, W, cus);
+    plan->tiles = default_tiles(T, H, cus);
+    plan->splits = default_splits(T, head_tiles(H) / plan->tiles, W, cus, plan->tiles);
     plan->chunk = kChunk;
     plan->reserved = 0;
     return SMLA_OK;

@@ -200,6 +200,30 @@ def test_repeated_calls_are_deterministic():
     _check_exact(p, out, lse, False, "repeated calls")
 
 
+def test_prepared_call_matches_direct_call():
+    """prepare_decode converts the arguments once; its launches give the direct call's bytes
+    (64-head plan with two ranges, so the fused merge and the arrival counters are exercised
+    across repeated prepared launches)."""
+    p = inputs.random_problem(405, 3, 128, 700, pool_rows=6000, neg_frac=0.1, sinks=True,
+                              lens=np.array([700, 0, 431]))
+    d = DeviceProblem(p)
+    plan = smla.make_plan(2, 2)
+    d.run(plan=plan, poison_out=False)
+    ref = d.out.view(torch.int16).clone()
+    ref_lse = d.lse.view(torch.int32).clone()
+    ws = d.workspace(plan)
+    launch = smla.prepare_decode(d.q, d.kv_a, d.indices, d.lens, p["bmm1"], p["bmm2"], d.out,
+                                 d.lse, kv_b=d.kv_b, split_col=p["split_col"], sinks=d.sinks,
+                                 qk_dim=p["qk_dim"], lse_log2=bool(p.get("lse_log2", False)),
+                                 plan=plan, workspace=ws)
+    for _ in range(3):
+        d.out.view(torch.int16).fill_(0x7FC0)
+        launch()
+        torch.cuda.synchronize()
+        assert torch.equal(d.out.view(torch.int16), ref)
+        assert torch.equal(d.lse.view(torch.int32), ref_lse)
+
+
 def test_t0_is_a_noop():
     p = inputs.random_problem(402, 1, 16, 8, pool_rows=64)
     d = DeviceProblem(p)
