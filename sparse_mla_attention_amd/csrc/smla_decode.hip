@@ -224,7 +224,7 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(DecodeParams a)
                            (bf16_bits(acc[ct][4 * i + 1] * inv) << 16);
                     pk.y = bf16_bits(acc[ct][4 * i + 2] * inv) |
                            (bf16_bits(acc[ct][4 * i + 3] * inv) << 16);
-                    *reinterpret_cast<uint2 *>(tile + hl * 1024 + 2 * col) = pk;
+                    *reinterpret_cast<uint2 *>(tile + tile_off(hl, 2 * col)) = pk;
                 }
             }
         }
@@ -236,7 +236,7 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(DecodeParams a)
         const int heads_here = min(HG, a.H - hg * HG);
         for (int x = tid; x < heads_here * 64; x += NT) {
             const int row = x >> 6, part = x & 63;
-            const v4i v = lds_load<v4i>(tile, row * 1024 + 16 * part);
+            const v4i v = lds_load<v4i>(tile, tile_off(row, 16 * part));
             *reinterpret_cast<v4i *>(a.out + ((int64_t)t * a.H + hg * HG + row) * 512 +
                                      8 * part) = v;
         }

@@ -176,10 +176,16 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
                              reinterpret_cast<const int *>(fin)[5 * HG + head]);
         }
         const int64_t tg = (int64_t)t * a.groups + hg;
-        // register-order index of accumulator element rr of tile (ct, h2): one 256-byte run
-        // per register and tile, so every store and load instruction of the exchange is one run
-        auto part_idx = [&](int ct, int h2, int rr) {
-            return (((NCT * w + ct) * 2 + h2) * 16 + rr) * 64 + lane;
+        // Byte offset of accumulator registers 4 j .. 4 j + 3 of tile (ct, h2) in a range's
+        // partial: 16 bytes per lane, one 1 KB run per (tile, j) across the wave, so every
+        // store and load of the exchange is one 16-byte access per lane.
+        auto part_off = [&](int ct, int h2, int j) {
+            return ((((NCT * w + ct) * 2 + h2) * 4 + j) * 64 + lane) * 16;
+        };
+        constexpr int SC1 = 16;  // cache policy of device-scope (write-through) accesses
+        auto part_rsrc = [&](int64_t unit) {
+            return __builtin_amdgcn_make_buffer_rsrc(a.ws_o + unit * (HG * 512), 0, HG * 512 * 4,
+                                                     0x00020000);
         };
         if (a.splits > 1) {
             // Split merge.  Each range takes an arrival ticket first.  Every range but the last
@@ -197,15 +203,20 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
             __syncthreads();
             if (*ticket != a.splits - 1) {
                 const int64_t ui = tg * a.splits + split;
-                float *po = a.ws_o + ui * (HG * 512);
                 if (!qk_wave) {
+                    const auto rs = part_rsrc(ui);
 #pragma unroll
                     for (int ct = 0; ct < NCT; ct++)
 #pragma unroll
                         for (int h2 = 0; h2 < 2; h2++)
 #pragma unroll
-                            for (int rr = 0; rr < 16; rr++)
-                                store_device(po + part_idx(ct, h2, rr), acc[ct][h2][rr]);
+                            for (int j = 0; j < 4; j++)
+                                __builtin_amdgcn_raw_buffer_store_b128(
+                                    v4i{__float_as_int(acc[ct][h2][4 * j]),
+                                        __float_as_int(acc[ct][h2][4 * j + 1]),
+                                        __float_as_int(acc[ct][h2][4 * j + 2]),
+                                        __float_as_int(acc[ct][h2][4 * j + 3])},
+                                    rs, part_off(ct, h2, j), 0, SC1);
                 }
                 if (wave == 4 && u == 0) {
 #pragma unroll
@@ -235,64 +246,140 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
             for (int h2 = 0; h2 < 2; h2++) {
                 own_g[h2] = g_h[h2];
                 own_l[h2] = l_h[h2];
-                const int head = 32 * h2 + hl;
-                float big_g = -INFINITY;
-                for (int s = 0; s < a.splits; s++) {
-                    const float gs =
-                        s == split ? own_g[h2]
-                                   : load_device(a.ws_ml + ((tg * a.splits + s) * HG + head) * 2);
-                    big_g = fmaxf(big_g, gs);
-                }
-                g_h[h2] = big_g;
-                l_h[h2] = 0.0f;
-                for (int s = 0; s < a.splits; s++) {
-                    const int64_t us = tg * a.splits + s;
-                    const float gs =
-                        s == split ? own_g[h2] : load_device(a.ws_ml + (us * HG + head) * 2);
-                    const float ls =
-                        s == split ? own_l[h2] : load_device(a.ws_ml + (us * HG + head) * 2 + 1);
-                    l_h[h2] += (gs == -INFINITY ? 0.0f : exp2f(gs - g_h[h2])) * ls;
-                }
             }
-            if (!qk_wave) {
-                // two 16-register accumulator tiles (both head tiles of a column tile) at a
-                // time: their loads of one range are issued together
+            if (a.splits == 2) {
+                // Two ranges: the other range's (G, l) and its first column tile come in one
+                // round trip, and each column tile's loads go out before the previous one is
+                // summed.
+                const int other = 1 - split;
+                const int64_t uo = tg * 2 + other;
+                float og[2], ol[2];
+                v4i cur[2][4], nxt[2][4];
+                if (!qk_wave) {
+                    const auto rs = part_rsrc(uo);
 #pragma unroll
-                for (int ct = 0; ct < NCT; ct++) {
-                    v16f sum[2] = {v16f{}, v16f{}};
-                    for (int s = 0; s < a.splits; s++) {
-                        const int64_t us = tg * a.splits + s;
-                        float w_s[2];
+                    for (int h2 = 0; h2 < 2; h2++)
 #pragma unroll
-                        for (int h2 = 0; h2 < 2; h2++) {
-                            const float gs =
-                                s == split ? own_g[h2]
-                                           : load_device(a.ws_ml + (us * HG + 32 * h2 + hl) * 2);
-                            w_s[h2] = gs == -INFINITY ? 0.0f : exp2f(gs - g_h[h2]);
+                        for (int j = 0; j < 4; j++)
+                            cur[h2][j] = __builtin_amdgcn_raw_buffer_load_b128(
+                                rs, part_off(0, h2, j), 0, SC1);
+                }
+#pragma unroll
+                for (int h2 = 0; h2 < 2; h2++) {
+                    const int64_t m = (uo * HG + 32 * h2 + hl) * 2;
+                    og[h2] = load_device(a.ws_ml + m);
+                    ol[h2] = load_device(a.ws_ml + m + 1);
+                }
+                float w_s[2][2];  // [range][h2]
+#pragma unroll
+                for (int h2 = 0; h2 < 2; h2++) {
+                    const float gr[2] = {split == 0 ? own_g[h2] : og[h2],
+                                         split == 1 ? own_g[h2] : og[h2]};
+                    const float lr[2] = {split == 0 ? own_l[h2] : ol[h2],
+                                         split == 1 ? own_l[h2] : ol[h2]};
+                    g_h[h2] = fmaxf(fmaxf(-INFINITY, gr[0]), gr[1]);
+                    l_h[h2] = 0.0f;
+#pragma unroll
+                    for (int r = 0; r < 2; r++) {
+                        w_s[r][h2] = gr[r] == -INFINITY ? 0.0f : exp2f(gr[r] - g_h[h2]);
+                        l_h[h2] += w_s[r][h2] * lr[r];
+                    }
+                }
+                if (!qk_wave) {
+                    const auto rs = part_rsrc(uo);
+#pragma unroll
+                    for (int ct = 0; ct < NCT; ct++) {
+                        if (ct + 1 < NCT) {
+#pragma unroll
+                            for (int h2 = 0; h2 < 2; h2++)
+#pragma unroll
+                                for (int j = 0; j < 4; j++)
+                                    nxt[h2][j] = __builtin_amdgcn_raw_buffer_load_b128(
+                                        rs, part_off(ct + 1, h2, j), 0, SC1);
                         }
-                        if (s == split) {
+#pragma unroll
+                        for (int h2 = 0; h2 < 2; h2++)
+#pragma unroll
+                            for (int rr = 0; rr < 16; rr++) {
+                                const float xo = __int_as_float(cur[h2][rr >> 2][rr & 3]);
+                                const float x0 = split == 0 ? acc[ct][h2][rr] : xo;
+                                const float x1 = split == 1 ? acc[ct][h2][rr] : xo;
+                                float sum = 0.0f;
+                                sum += w_s[0][h2] * x0;
+                                sum += w_s[1][h2] * x1;
+                                acc[ct][h2][rr] = sum;
+                            }
+                        if (ct + 1 < NCT) {
 #pragma unroll
                             for (int h2 = 0; h2 < 2; h2++)
 #pragma unroll
-                                for (int rr = 0; rr < 16; rr++)
-                                    sum[h2][rr] += w_s[h2] * acc[ct][h2][rr];
-                        } else {
-                            const float *ps = a.ws_o + us * (HG * 512);
-                            float v[2][16];
-#pragma unroll
-                            for (int h2 = 0; h2 < 2; h2++)
-#pragma unroll
-                                for (int rr = 0; rr < 16; rr++)
-                                    v[h2][rr] = load_device(ps + part_idx(ct, h2, rr));
-#pragma unroll
-                            for (int h2 = 0; h2 < 2; h2++)
-#pragma unroll
-                                for (int rr = 0; rr < 16; rr++)
-                                    sum[h2][rr] += w_s[h2] * v[h2][rr];
+                                for (int j = 0; j < 4; j++)
+                                    cur[h2][j] = nxt[h2][j];
                         }
                     }
-                    acc[ct][0] = sum[0];
-                    acc[ct][1] = sum[1];
+                }
+            } else {
+#pragma unroll
+                for (int h2 = 0; h2 < 2; h2++) {
+                    const int head = 32 * h2 + hl;
+                    float big_g = -INFINITY;
+                    for (int s = 0; s < a.splits; s++) {
+                        const float gs =
+                            s == split ? own_g[h2]
+                                       : load_device(a.ws_ml + ((tg * a.splits + s) * HG + head) * 2);
+                        big_g = fmaxf(big_g, gs);
+                    }
+                    g_h[h2] = big_g;
+                    l_h[h2] = 0.0f;
+                    for (int s = 0; s < a.splits; s++) {
+                        const int64_t us = tg * a.splits + s;
+                        const float gs =
+                            s == split ? own_g[h2] : load_device(a.ws_ml + (us * HG + head) * 2);
+                        const float ls =
+                            s == split ? own_l[h2] : load_device(a.ws_ml + (us * HG + head) * 2 + 1);
+                        l_h[h2] += (gs == -INFINITY ? 0.0f : exp2f(gs - g_h[h2])) * ls;
+                    }
+                }
+                if (!qk_wave) {
+                    // one column tile at a time: its loads of one range are issued together
+#pragma unroll
+                    for (int ct = 0; ct < NCT; ct++) {
+                        v16f sum[2] = {v16f{}, v16f{}};
+                        for (int s = 0; s < a.splits; s++) {
+                            const int64_t us = tg * a.splits + s;
+                            float w_s[2];
+#pragma unroll
+                            for (int h2 = 0; h2 < 2; h2++) {
+                                const float gs =
+                                    s == split ? own_g[h2]
+                                               : load_device(a.ws_ml + (us * HG + 32 * h2 + hl) * 2);
+                                w_s[h2] = gs == -INFINITY ? 0.0f : exp2f(gs - g_h[h2]);
+                            }
+                            if (s == split) {
+#pragma unroll
+                                for (int h2 = 0; h2 < 2; h2++)
+#pragma unroll
+                                    for (int rr = 0; rr < 16; rr++)
+                                        sum[h2][rr] += w_s[h2] * acc[ct][h2][rr];
+                            } else {
+                                const auto rs = part_rsrc(us);
+                                v4i v[2][4];
+#pragma unroll
+                                for (int h2 = 0; h2 < 2; h2++)
+#pragma unroll
+                                    for (int j = 0; j < 4; j++)
+                                        v[h2][j] = __builtin_amdgcn_raw_buffer_load_b128(
+                                            rs, part_off(ct, h2, j), 0, SC1);
+#pragma unroll
+                                for (int h2 = 0; h2 < 2; h2++)
+#pragma unroll
+                                    for (int rr = 0; rr < 16; rr++)
+                                        sum[h2][rr] += w_s[h2] * __int_as_float(v[h2][rr >> 2][rr & 3]);
+                            }
+                        }
+                        acc[ct][0] = sum[0];
+                        acc[ct][1] = sum[1];
+                    }
                 }
             }
             if (tid == 0) {  // every range has arrived and been merged: ready for the next call
@@ -326,7 +413,7 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
                                (bf16_bits(acc[ct][h2][4 * i + 1] * inv) << 16);
                         pk.y = bf16_bits(acc[ct][h2][4 * i + 2] * inv) |
                                (bf16_bits(acc[ct][h2][4 * i + 3] * inv) << 16);
-                        *reinterpret_cast<uint2 *>(tile + (32 * h2 + hl) * 1024 + 2 * col) = pk;
+                        *reinterpret_cast<uint2 *>(tile + tile_off((32 * h2 + hl), 2 * col)) = pk;
                     }
                 }
             }
@@ -339,7 +426,7 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
         const int heads_here = min(HG, a.H - hg * HG);
         for (int x = tid; x < heads_here * 64; x += NT) {
             const int row = x >> 6, part = x & 63;
-            const v4i v = lds_load<v4i>(tile, row * 1024 + 16 * part);
+            const v4i v = lds_load<v4i>(tile, tile_off(row, 16 * part));
             *reinterpret_cast<v4i *>(a.out + ((int64_t)t * a.H + hg * HG + row) * 512 +
                                      8 * part) = v;
         }
@@ -393,6 +480,9 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
         // at the head's final maximum before the range starts (e = ceil(m - G) <= 0, at least
         // E_MIN), so no pass ever rescales the accumulators.
         auto qk_softmax = [&](int x) {
+            // the K reads and products of the QK waves go ahead of the P.V waves' work on
+            // the same SIMD; the softmax then runs at normal priority
+            __builtin_amdgcn_s_setprio(3);
             const uint8_t *slot = lds + (x % SLOTS) * L::SLOTB;
             const uint8_t *ab = reinterpret_cast<const uint8_t *>(addr) + x * CHUNK * 8;
             const uint64_t mk = __ballot(lds_load<uint64_t>(ab, lane * 8) != zero);
@@ -436,6 +526,7 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
             const uint64_t bits = mk >> (4 * g);
             const uint32_t word[2] = {(uint32_t)bits, (uint32_t)(bits >> 32)};
             mfma_result_pad();
+            __builtin_amdgcn_s_setprio(0);
             float mx = -INFINITY;
 #pragma unroll
             for (int kt = 0; kt < 4; kt++) {
@@ -592,37 +683,46 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
                 lds_dma16(src[8], sb + L::LAT + 1024 * w);
         };
 
-        // P.V of chunk x over this wave's 4 column tiles and both 32-head tiles
-        auto pv = [&](int x) {
+        // P.V of chunk x over this wave's 4 column tiles and both 32-head tiles, in two
+        // steps: every V^T and P fragment into registers (after which the slot may be
+        // refilled), then the products
+        struct Frags {
+            v8i vt[NCT];
+            v8i bh[2], bl[2];
+            int escw[2];
+        };
+        auto pv_read = [&](int x, Frags &f) {
             const uint8_t *vs = lds + (x % SLOTS) * L::SLOTB;
             const uint8_t *pbuf = lds + L::P + (x & 1) * L::PBUF;
-            int escw[2];
-            v8i bh[2], bl[2];
 #pragma unroll
             for (int h2 = 0; h2 < 2; h2++) {
-                escw[h2] = esc[(x & 1) * HG + 32 * h2 + hl];
-                bh[h2] = join(lds_load<v4i>(pbuf + 2048 * h2, p_rd0),
-                              lds_load<v4i>(pbuf + 2048 * h2, p_rd1));
-                bl[h2] = bh[h2];
+                f.escw[h2] = esc[(x & 1) * HG + 32 * h2 + hl];
+                f.bh[h2] = join(lds_load<v4i>(pbuf + 2048 * h2, p_rd0),
+                                lds_load<v4i>(pbuf + 2048 * h2, p_rd1));
+                f.bl[h2] = f.bh[h2];
                 if constexpr (TWO)
-                    bl[h2] = join(lds_load<v4i>(pbuf + L::PTERM + 2048 * h2, p_rd0),
-                                  lds_load<v4i>(pbuf + L::PTERM + 2048 * h2, p_rd1));
+                    f.bl[h2] = join(lds_load<v4i>(pbuf + L::PTERM + 2048 * h2, p_rd0),
+                                    lds_load<v4i>(pbuf + L::PTERM + 2048 * h2, p_rd1));
             }
 #pragma unroll
             for (int ct = 0; ct < NCT; ct++) {
-                v8i vt;
 #pragma unroll
                 for (int rho = 0; rho < 4; rho++) {
                     const v2i y = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
                         (SMLA_LDS(v2i) *)(vs + rho * 1024 + voff[ct][rho & 1]));
-                    vt[2 * rho] = y[0];
-                    vt[2 * rho + 1] = y[1];
+                    f.vt[ct][2 * rho] = y[0];
+                    f.vt[ct][2 * rho + 1] = y[1];
                 }
+            }
+        };
+        auto pv_mma = [&](const Frags &f) {
+#pragma unroll
+            for (int ct = 0; ct < NCT; ct++) {
 #pragma unroll
                 for (int h2 = 0; h2 < 2; h2++) {
-                    acc[ct][h2] = mfma32(vt, bh[h2], acc[ct][h2], escw[h2]);
+                    acc[ct][h2] = mfma32(f.vt[ct], f.bh[h2], acc[ct][h2], f.escw[h2]);
                     if constexpr (TWO)  // the second term's 2^-4
-                        acc[ct][h2] = mfma32(vt, bl[h2], acc[ct][h2], escw[h2] - 4);
+                        acc[ct][h2] = mfma32(f.vt[ct], f.bl[h2], acc[ct][h2], f.escw[h2] - 4);
                 }
             }
         };
@@ -645,16 +745,24 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
             }
             for (int c = 0; c <= nch; c++) {
                 lds_barrier();                      // chunk c landed; P of chunk c-1 visible
+                // The loads of chunk c+2 go out before the products of chunk c-1: the QK
+                // waves' products of chunk c then reach the matrix units first, and these run
+                // during the QK waves' softmax.
+                Frags f;
                 if (c > 0)
-                    pv(c - 1);
+                    pv_read(c - 1, f);
                 if (c + 2 < nch) {
                     // the wave's own reads of the slice it refills have completed
                     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
                     issue(c + 2);
-                    wait_dma<NDMA>();               // chunk c+1
-                } else {
-                    wait_dma<0>();
                 }
+                __builtin_amdgcn_sched_barrier(0);  // the products stay after the loads
+                if (c > 0)
+                    pv_mma(f);
+                if (c + 2 < nch)
+                    wait_dma<NDMA>();               // chunk c+1
+                else
+                    wait_dma<0>();
             }
         };
 

@@ -34,6 +34,15 @@ __device__ inline int vsw(int key) { return ((key & 7) << 1) | ((key >> 3) & 1);
 // XOR on the 16-byte piece index of head h's 64-byte P row.
 __device__ inline int psw(int h) { return (h >> 2) & 3; }
 
+// Byte offset of byte `b` of row `row` in a BF16 output tile of 1024-byte rows: the 16-byte
+// granule index is XORed with the row's low four bits, so that the same column of 16
+// consecutive rows (one head per lane, as the accumulators hold them) falls in 16 different
+// bank groups; a row read as 64 consecutive granules stays conflict free.
+__device__ inline int tile_off(int row, int b)
+{
+    return row * 1024 + ((((b >> 4) ^ (row & 15)) << 4) | (b & 15));
+}
+
 __device__ inline v8i join(v4i x, v4i y)
 {
     return v8i{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
