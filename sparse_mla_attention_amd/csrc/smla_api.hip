@@ -51,14 +51,10 @@ bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
 int32_t head_tiles(int32_t H) { return (H + 31) / 32; }
 
 // 32-head tiles per workgroup: 2 (the 64-head kernel, which gathers each row once for 64
-// heads) when the head tiles pair up and its units alone cover at least half of the compute
-// units; 1 (the 32-head kernel) for small batches, where its shorter fixed path wins.
-int default_tiles(int32_t T, int32_t H, int cus)
+// heads) whenever the head tiles pair up; else 1 (the 32-head kernel).
+int default_tiles(int32_t H)
 {
-    const int64_t ht = head_tiles(H);
-    if (ht % 2 != 0)
-        return 1;
-    return (int64_t)T * (ht / 2) * 2 >= cus ? 2 : 1;
+    return head_tiles(H) % 2 == 0 ? 2 : 1;
 }
 
 // Key ranges per (token, head group): one range when a token has at most kFewChunks chunks of
@@ -144,7 +140,7 @@ smla_status smla_decode_plan(int32_t T, int32_t H, int32_t W, int32_t row_bytes,
     int cus = 0;
     if (current_cu_count(&cus) != hipSuccess)
         return SMLA_EHIP;
-    plan->tiles = default_tiles(T, H, cus);
+    plan->tiles = default_tiles(H);
     plan->splits = default_splits(T, head_tiles(H) / plan->tiles, W, cus, plan->tiles);
     plan->chunk = kChunk;
     plan->reserved = 0;

@@ -99,6 +99,13 @@ __device__ inline void wait_dma()
     asm volatile("s_waitcnt vmcnt(%0)" : : "i"(N) : "memory");
 }
 
+// Which 16-byte pieces lane group g of a QK wave holds (the same for Q and K, so the products
+// are unchanged): latent pieces 8 s + qk_pg(g) and 8 s + 4 + qk_pg(g) of step s, rope piece
+// 32 + qk_pr(g).  The two lane groups that share an LDS pass (g = 2h, 2h + 1) then read
+// disjoint bank sets under the slot swizzles, so the K reads run without bank conflicts.
+__device__ inline int qk_pg(int g) { return ((g & 1) << 1) | (g >> 1); }
+__device__ inline int qk_pr(int g) { return g ^ ((g & 1) << 1); }
+
 // LDS byte address (M0 operand) of a pointer into the workgroup's LDS.
 __device__ inline uint32_t lds_addr(const uint8_t *p)
 {
@@ -133,6 +140,7 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
     const int mine = min(min(n - first, per), G64_MAX_RANGE);
     const int nch = (mine + CHUNK - 1) / CHUNK;
     const int32_t *idx_row = a.indices + (int64_t)t * a.W;
+
 
     const uint64_t *addr = reinterpret_cast<const uint64_t *>(lds + L::ADDR);
     int *flag = reinterpret_cast<int *>(lds + L::MISC) + 1;
@@ -437,12 +445,7 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
         const int r = lane & 15, g = lane >> 4;    // row r of a 16-key tile, lane group g
         const int head = 16 * w + r;               // this lane's head within the group
 
-        // Which 16-byte pieces lane group g holds (the same for Q and K, so the products are
-        // unchanged): latent pieces 8 s + pg and 8 s + 4 + pg of step s, rope piece 32 + pr.
-        // The two lane groups that share an LDS pass (g = 2h, 2h + 1) then read disjoint bank
-        // sets under the row swizzles below, so the K reads run without bank conflicts.
-        const int pg = ((g & 1) << 1) | (g >> 1);
-        const int pr = g ^ ((g & 1) << 1);
+        const int pg = qk_pg(g), pr = qk_pr(g);
         // Q fragments, B operand of QK: lane (n, g) holds head 16 w + n.
         v8i qf[4];
         v4i qt = v4i{0, 0, 0, 0};

@@ -198,3 +198,36 @@ def test_g64_graph_replay_matches_eager():
         assert torch.equal(d.out.view(torch.int16), ref_out), f"replay {rep}: out differs"
         assert torch.equal(d.lse.view(torch.int32), ref_lse), f"replay {rep}: lse differs"
         del junk
+
+
+def test_g64_large_batch_split_merge_is_deterministic():
+    """The large-batch launch (T=64, H=128, 2048 columns, two ranges per 64-head group: 256
+    workgroups that all reach the split exchange together): eight calls on one workspace give
+    the first call's bytes, and the output equals the 32-head kernel's (one range, no
+    exchange) on every call."""
+    w = inputs.config_throughput_device("cuda", index_sets=1)
+    T, H = 64, 128
+    idx = w["index_sets"][0]
+    plan = smla.make_plan(2, 2)
+    ws = smla.new_workspace(plan, T, H)
+    out = torch.empty((T, H, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    ref = torch.empty_like(out)
+    ref_lse = torch.empty_like(lse)
+    smla.sparse_mla_decode(w["q"], w["kv_a"], idx, w["lens"], w["bmm1"], w["bmm2"], ref, ref_lse,
+                           plan=smla.make_plan(2, 1), workspace=smla.new_workspace(
+                               smla.make_plan(2, 1), T, H))
+    torch.cuda.synchronize()
+    first = None
+    for i in range(8):
+        out.view(torch.int16).fill_(0x7FC0)
+        smla.sparse_mla_decode(w["q"], w["kv_a"], idx, w["lens"], w["bmm1"], w["bmm2"], out, lse,
+                               plan=plan, workspace=ws)
+        torch.cuda.synchronize()
+        got = out.view(torch.int16).clone()
+        if first is None:
+            first = got
+        bad = int((got != first).sum())
+        assert bad == 0, f"call {i}: {bad} output elements differ from the first call"
+        assert torch.equal(got, ref.view(torch.int16)), f"call {i}: differs from the 32-head kernel"
+        assert torch.equal(lse.view(torch.int32), ref_lse.view(torch.int32))
