@@ -220,10 +220,8 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(DecodeParams a)
                 for (int i = 0; i < 4; i++) {
                     const int col = 32 * (tile0 + ct) + 8 * i + 4 * u;
                     uint2 pk;
-                    pk.x = bf16_bits(acc[ct][4 * i] * inv) |
-                           (bf16_bits(acc[ct][4 * i + 1] * inv) << 16);
-                    pk.y = bf16_bits(acc[ct][4 * i + 2] * inv) |
-                           (bf16_bits(acc[ct][4 * i + 3] * inv) << 16);
+                    pk.x = bf16x2(acc[ct][4 * i] * inv, acc[ct][4 * i + 1] * inv);
+                    pk.y = bf16x2(acc[ct][4 * i + 2] * inv, acc[ct][4 * i + 3] * inv);
                     *reinterpret_cast<uint2 *>(tile + tile_off(hl, 2 * col)) = pk;
                 }
             }

@@ -174,6 +174,15 @@ __device__ inline uint32_t bf16_bits(float x)
     return u >> 16;
 }
 
+// Two floats rounded to BF16 (nearest even) and packed, `lo` in the low half: one
+// v_cvt_pk_bf16_f32.
+typedef __bf16 v2bf16 __attribute__((ext_vector_type(2)));
+__device__ inline uint32_t bf16x2(float lo, float hi)
+{
+    const v2bf16 r = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, r);
+}
+
 // Pad between the last matrix instruction of a chain and the first vector read of its result.
 // A result of the block-scaled 32x32x64 FP8 instruction read 19 wait states after issue was
 // measured to hold the chain's previous partial sum, so fresh results are read behind 24
