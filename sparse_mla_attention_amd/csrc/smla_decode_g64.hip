@@ -433,8 +433,10 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
         for (int x = tid; x < heads_here * 64; x += NT) {
             const int row = x >> 6, part = x & 63;
             const v4i v = lds_load<v4i>(tile, tile_off(row, 16 * part));
-            *reinterpret_cast<v4i *>(a.out + ((int64_t)t * a.H + hg * HG + row) * 512 +
-                                     8 * part) = v;
+            // streaming store: the output is not read again by this kernel
+            __builtin_nontemporal_store(
+                v, reinterpret_cast<v4i *>(a.out + ((int64_t)t * a.H + hg * HG + row) * 512 +
+                                           8 * part));
         }
     };
 
