@@ -450,16 +450,15 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
         v8i qf[4];
         v4i qt = v4i{0, 0, 0, 0};
         {
+            // a padding head (past H) computes with head 0's q: its scores reach no output,
+            // and no instruction between here and the first product waits for these loads
             const int gh = hg * HG + head;
-            const bool live = gh < a.H;
-            const uint8_t *qp = a.q + (int64_t)t * a.q_st + (int64_t)(live ? gh : 0) * a.q_sh;
-            const int keep = live ? -1 : 0;        // padding heads keep zeros
+            const uint8_t *qp = a.q + (int64_t)t * a.q_st + (int64_t)(gh < a.H ? gh : 0) * a.q_sh;
 #pragma unroll
             for (int s = 0; s < 4; s++)
-                qf[s] = join(gload(qp + 16 * (8 * s + pg)) & keep,
-                             gload(qp + 16 * (8 * s + 4 + pg)) & keep);
+                qf[s] = join(gload(qp + 16 * (8 * s + pg)), gload(qp + 16 * (8 * s + 4 + pg)));
             if (TAIL)
-                qt = gload(qp + 16 * (32 + pr)) & keep;
+                qt = gload(qp + 16 * (32 + pr));
         }
 
         // per-lane LDS offsets (loop invariant): pieces pg and 4 + pg of slice s of row 16 kt + r
@@ -738,14 +737,17 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
                     acc[ct][h2] = v16f{};
             if (nch == 0)
                 return;
-            lds_barrier();                          // every slot is free
+            // every slot is free (a second pass starts after the flag barriers), so the first
+            // two chunks go out before the barrier that the QK waves reach once their Q loads
+            // are issued
             issue(0);
-            if (nch > 1) {
+            if (nch > 1)
                 issue(1);
+            lds_barrier();
+            if (nch > 1)
                 wait_dma<NDMA>();                   // chunk 0
-            } else {
+            else
                 wait_dma<0>();
-            }
             for (int c = 0; c <= nch; c++) {
                 lds_barrier();                      // chunk c landed; P of chunk c-1 visible
                 // The loads of chunk c+2 go out before the products of chunk c-1: the QK
