@@ -90,6 +90,7 @@ struct Lds {
     static constexpr int TOTAL = MISC + 16;
     static constexpr int OUT_TILE = HG * 1024;                 // BF16 [32][512], after the loop
     static_assert(OUT_TILE <= P, "output tile must fit in the V slots");
+    static_assert(OUT_TILE + 64 * HG * 8 <= SC, "(G, l) of 64 ranges must fit past the tile");
     static_assert(TOTAL <= 160 * 1024, "LDS budget");
 };
 
@@ -142,64 +143,108 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(DecodeParams a)
         const int head = hg * HG + hl;
         const int64_t tg = (int64_t)t * a.groups + hg;
         const int tile0 = NCT * w;
-        // register-order index of accumulator element r of tile `tile` (one 256-byte run per
-        // register and tile: every store and load instruction of the exchange is one run)
-        auto part_idx = [&](int tile, int r) { return (tile * 16 + r) * 64 + lane; };
         if (a.splits > 1) {
-            // Partial of this range: FP32 accumulators in register order, then (G, l) per
-            // head.  The exchange uses device-scope (write-through) stores and loads, and each
-            // workgroup waits for its stores to complete before taking its ticket: no cache
-            // writeback or invalidation of the whole L2, which other workgroups would pay for.
-            const int64_t ui = tg * a.splits + split;
-            float *po = a.ws_o + ui * (HG * 512);
-            if (!s_wave) {
+            // Split merge.  Every range writes its partial (FP32 accumulators, then (G, l) per
+            // head) with device-scope (write-through) stores, waits for them to complete and
+            // only then takes an arrival ticket; the range holding the last ticket therefore
+            // sees every other partial complete and merges all of them in range order, its own
+            // from registers.  (With few workgroups this beats taking the ticket first: the
+            // stores of all ranges overlap instead of following the ticket round trip.)
+            // Partial layout: accumulator registers 4 j .. 4 j + 3 of tile `tile` at byte
+            // ((tile * 4 + j) * 64 + lane) * 16, one 16-byte access per lane.
+            constexpr int SC1 = 16;  // cache policy of device-scope (write-through) accesses
+            auto part_off = [&](int ct, int j) { return (((tile0 + ct) * 4 + j) * 64 + lane) * 16; };
+            auto part_rsrc = [&](int64_t unit) {
+                return __builtin_amdgcn_make_buffer_rsrc(a.ws_o + unit * (HG * 512), 0,
+                                                         HG * 512 * 4, 0x00020000);
+            };
+            int *ticket = reinterpret_cast<int *>(lds + L::MISC);
+            int *ctr = a.counters + 2 * tg;         // [0] arrival ticket
+            {
+                const int64_t ui = tg * a.splits + split;
+                if (!s_wave) {
+                    const auto rs = part_rsrc(ui);
 #pragma unroll
-                for (int ct = 0; ct < NCT; ct++)
+                    for (int ct = 0; ct < NCT; ct++)
 #pragma unroll
-                    for (int r = 0; r < 16; r++)
-                        store_device(po + part_idx(tile0 + ct, r), acc[ct][r]);
-            }
-            if (wave == 4 && u == 0) {
-                store_device(a.ws_ml + (ui * HG + hl) * 2 + 0, g_h);
-                store_device(a.ws_ml + (ui * HG + hl) * 2 + 1, l_h);
+                        for (int j = 0; j < 4; j++)
+                            __builtin_amdgcn_raw_buffer_store_b128(
+                                v4i{__float_as_int(acc[ct][4 * j]), __float_as_int(acc[ct][4 * j + 1]),
+                                    __float_as_int(acc[ct][4 * j + 2]),
+                                    __float_as_int(acc[ct][4 * j + 3])},
+                                rs, part_off(ct, j), 0, SC1);
+                }
+                if (wave == 4 && u == 0) {
+                    store_device(a.ws_ml + (ui * HG + hl) * 2 + 0, g_h);
+                    store_device(a.ws_ml + (ui * HG + hl) * 2 + 1, l_h);
+                }
             }
             __builtin_amdgcn_s_waitcnt(0);  // this wave's stores have completed
             __syncthreads();
-            int *ticket = reinterpret_cast<int *>(lds + L::MISC);
             if (tid == 0)
-                *ticket = __hip_atomic_fetch_add(a.counters + 2 * tg, 1, __ATOMIC_RELAXED,
+                *ticket = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED,
                                                  __HIP_MEMORY_SCOPE_AGENT);
             __syncthreads();
             if (*ticket != a.splits - 1)
                 return;
-            // last range: merge every range's partial in range order (its own included, read
-            // back from the workspace, so the result does not depend on arrival order)
+            // (G, l) of every range and head, staged in LDS in one round of loads (over the
+            // V slots, past the output tile)
+            float2 *gl = reinterpret_cast<float2 *>(lds + L::OUT_TILE);  // [splits][32]
+            for (int i = tid; i < a.splits * HG; i += NT) {
+                const int s = i / HG, h = i % HG;
+                const float *m = a.ws_ml + ((tg * a.splits + s) * HG + h) * 2;
+                if (s != split)  // this range's own values stay in registers
+                    gl[i] = float2{load_device(m), load_device(m + 1)};
+            }
+            __syncthreads();
             float big_g = -INFINITY;
             for (int s = 0; s < a.splits; s++)
-                big_g = fmaxf(big_g, load_device(a.ws_ml + ((tg * a.splits + s) * HG + hl) * 2));
-            l_h = 0.0f;
-#pragma unroll
-            for (int ct = 0; ct < NCT; ct++)
-                acc[ct] = v16f{};
+                big_g = fmaxf(big_g, s == split ? g_h : gl[s * HG + hl].x);
+            float l_new = 0.0f;
             for (int s = 0; s < a.splits; s++) {
-                const int64_t us = tg * a.splits + s;
-                const float *ps = a.ws_o + us * (HG * 512);
-                const float gs = load_device(a.ws_ml + (us * HG + hl) * 2);
-                const float ls = load_device(a.ws_ml + (us * HG + hl) * 2 + 1);
-                const float wgt = gs == -INFINITY ? 0.0f : exp2f(gs - big_g);
-                l_h += wgt * ls;
-                if (!s_wave) {
+                const float gs = s == split ? g_h : gl[s * HG + hl].x;
+                const float ls = s == split ? l_h : gl[s * HG + hl].y;
+                l_new += (gs == -INFINITY ? 0.0f : exp2f(gs - big_g)) * ls;
+            }
+            if (!s_wave) {
+                // range order, all four column tiles of one range per round of loads
+                v16f sum[NCT];
 #pragma unroll
-                    for (int ct = 0; ct < NCT; ct++)
+                for (int ct = 0; ct < NCT; ct++)
+                    sum[ct] = v16f{};
+                for (int s = 0; s < a.splits; s++) {
+                    const float gs = s == split ? g_h : gl[s * HG + hl].x;
+                    const float wgt = gs == -INFINITY ? 0.0f : exp2f(gs - big_g);
+                    if (s == split) {
 #pragma unroll
-                        for (int r = 0; r < 16; r++)
-                            acc[ct][r] += wgt * load_device(ps + part_idx(tile0 + ct, r));
+                        for (int ct = 0; ct < NCT; ct++)
+#pragma unroll
+                            for (int r = 0; r < 16; r++)
+                                sum[ct][r] += wgt * acc[ct][r];
+                    } else {
+                        const auto rs = part_rsrc(tg * a.splits + s);
+                        v4i v[NCT][4];
+#pragma unroll
+                        for (int ct = 0; ct < NCT; ct++)
+#pragma unroll
+                            for (int j = 0; j < 4; j++)
+                                v[ct][j] = __builtin_amdgcn_raw_buffer_load_b128(
+                                    rs, part_off(ct, j), 0, SC1);
+#pragma unroll
+                        for (int ct = 0; ct < NCT; ct++)
+#pragma unroll
+                            for (int r = 0; r < 16; r++)
+                                sum[ct][r] += wgt * __int_as_float(v[ct][r >> 2][r & 3]);
+                    }
                 }
+#pragma unroll
+                for (int ct = 0; ct < NCT; ct++)
+                    acc[ct] = sum[ct];
             }
             g_h = big_g;
+            l_h = l_new;
             if (tid == 0)  // every range has arrived: ready for the next call
-                __hip_atomic_store(a.counters + 2 * tg, 0, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
 
         // ---- final: sink, normalization, BF16 tile in LDS, coalesced row stores, LSE ------
