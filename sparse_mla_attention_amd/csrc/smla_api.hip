@@ -92,9 +92,9 @@ bool plan_ok(const smla_plan *p, int32_t H)
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Workspace layout under a valid plan: counters [T, groups, 2] int32 (arrival ticket and
-// ready count, zero between calls), then
-// FP32 partials [T, groups, splits, 32 tiles heads, 512], then (frame, sum) [T, groups,
-// splits, 32 tiles heads, 2].
+// ready count, zero between calls), then FP32 partials: one block of 32 tiles x 512 floats per
+// (token, head group, range), in the order the kernel's accumulator registers are stored (16-byte
+// runs per lane), then (frame, sum) [T, groups, splits, 32 tiles heads, 2].
 struct WsLayout {
     size_t counters, partials, ml, total;
 };
