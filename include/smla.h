@@ -62,23 +62,25 @@ typedef int32_t smla_status;
 typedef struct smla_plan {
     int32_t splits; /* 1 .. 64 */
     int32_t tiles;  /* 32-head tiles per workgroup: 1 (32 heads, rows loaded into registers) or
-                       2 (64 heads, rows gathered straight into LDS; needs an even number of
-                       32-head tiles and ranges of at most 2048 columns, ceil(W / splits) <=
-                       2048, else SMLA_EUNSUPPORTED) */
+                       2 (64 heads, rows gathered straight into LDS; the last group is padded
+                       when ceil(H / 32) is odd; ranges of at most 2048 columns,
+                       ceil(W / splits) <= 2048, else SMLA_EUNSUPPORTED) */
     int32_t chunk;  /* columns per gathered chunk (64 in this build; output only) */
     int32_t reserved;
 } smla_plan;
 
-/* The plan sparse_mla_decode uses for these sizes when it is given none: the split count and
- * tiles per workgroup fill the device's compute units (queried once per device).  Returns
- * SMLA_EINVAL for bad sizes, SMLA_EHIP if the device cannot be queried. */
+/* The plan sparse_mla_decode uses for these sizes when it is given none: 64 heads per
+ * workgroup when that needs at most two key ranges, else 32; one range when a token has at
+ * most 6 chunks of columns, else enough ranges to cover the device's compute units (queried
+ * once per device), at most 4.  Returns SMLA_EINVAL for bad sizes, SMLA_EHIP if the device
+ * cannot be queried. */
 smla_status smla_decode_plan(int32_t T, int32_t H, int32_t W, int32_t row_bytes, uint32_t flags,
                              smla_plan *plan);
 
 /* Workspace bytes sparse_mla_decode needs under `plan` (0 when plan->splits == 1): arrival
  * counters (two int32 per token and head group, rounded up to 256 bytes), FP32 partials
  * [T, groups, splits, 32 tiles, 512] and (frame, sum) pairs [T, groups, splits, 32 tiles, 2],
- * groups = ceil(H / 32) / tiles.  0 for a bad plan. */
+ * groups = ceil(ceil(H / 32) / tiles).  0 for a bad plan. */
 size_t smla_decode_workspace_size(const smla_plan *plan, int32_t T, int32_t H);
 
 /*

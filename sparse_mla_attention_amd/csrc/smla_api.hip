@@ -50,12 +50,8 @@ bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
 
 int32_t head_tiles(int32_t H) { return (H + 31) / 32; }
 
-// 32-head tiles per workgroup: 2 (the 64-head kernel, which gathers each row once for 64
-// heads) whenever the head tiles pair up; else 1 (the 32-head kernel).
-int default_tiles(int32_t H)
-{
-    return head_tiles(H) % 2 == 0 ? 2 : 1;
-}
+// Head groups per token: workgroups of `tiles` 32-head tiles, the last one padded.
+int32_t head_groups(int32_t H, int tiles) { return (head_tiles(H) + tiles - 1) / tiles; }
 
 // Key ranges per (token, head group): one range when a token has at most kFewChunks chunks of
 // columns (a split merge costs more than it saves there); else enough workgroups to cover every
@@ -86,7 +82,8 @@ bool plan_ok(const smla_plan *p, int32_t H)
         return false;
     if (p->tiles != 1 && p->tiles != 2)
         return false;
-    return head_tiles(H) % p->tiles == 0;
+    (void)H;
+    return true;
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -101,7 +98,7 @@ struct WsLayout {
 
 WsLayout ws_layout(const smla_plan *plan, int32_t T, int32_t H)
 {
-    const size_t groups = (size_t)(head_tiles(H) / plan->tiles);
+    const size_t groups = (size_t)head_groups(H, plan->tiles);
     const size_t hg = 32 * (size_t)plan->tiles;
     const size_t units = (size_t)T * groups * (size_t)plan->splits;
     WsLayout w;
@@ -140,8 +137,18 @@ smla_status smla_decode_plan(int32_t T, int32_t H, int32_t W, int32_t row_bytes,
     int cus = 0;
     if (current_cu_count(&cus) != hipSuccess)
         return SMLA_EHIP;
-    plan->tiles = default_tiles(H);
-    plan->splits = default_splits(T, head_tiles(H) / plan->tiles, W, cus, plan->tiles);
+    // 64 heads per workgroup (the last group padded when the 32-head tiles do not pair up)
+    // unless that needs more than two key ranges: its split exchange is built for two ranges
+    // at a full grid; more ranges go to the 32-head kernel, whose store-first exchange suits
+    // the few workgroups of small batches.
+    const int s64 = default_splits(T, head_groups(H, 2), W, cus, 2);
+    if (s64 <= 2) {
+        plan->tiles = 2;
+        plan->splits = s64;
+    } else {
+        plan->tiles = 1;
+        plan->splits = default_splits(T, head_groups(H, 1), W, cus, 1);
+    }
     plan->chunk = kChunk;
     plan->reserved = 0;
     return SMLA_OK;
@@ -230,7 +237,7 @@ smla_status sparse_mla_decode(const void *q, int64_t q_stride_t, int64_t q_strid
     p.lse = lse;
     p.lse_log2 = (flags & SMLA_LSE_LOG2) ? 1 : 0;
     p.splits = chosen.splits;
-    p.groups = head_tiles(H) / chosen.tiles;
+    p.groups = head_groups(H, chosen.tiles);
     p.ws_o = nullptr;
     p.ws_ml = nullptr;
     p.counters = nullptr;

@@ -87,7 +87,7 @@ class DeviceProblem:
         nbytes = smla.workspace_size(plan, self.T, self.H)
         if not nbytes:
             return None
-        groups = ((self.H + 31) // 32) // plan.tiles
+        groups = -(-((self.H + 31) // 32) // plan.tiles)
         counters = (self.T * groups * 2 * 4 + 255) // 256 * 256
         ws = torch.empty(nbytes, dtype=torch.uint8, device=self.q.device)
         ws[:counters].zero_()

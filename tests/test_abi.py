@@ -33,18 +33,18 @@ def test_strerror():
 
 def test_workspace_size_formula():
     def expect(T, H, splits, tiles):
-        groups = ((H + 31) // 32) // tiles
+        groups = -(-((H + 31) // 32) // tiles)
         counters = (T * groups * 2 * 4 + 255) // 256 * 256
         return counters + T * groups * splits * 32 * tiles * (512 + 2) * 4
     for splits, tiles, T, H in [(2, 1, 7, 128), (3, 1, 7, 96), (64, 1, 3, 16), (5, 1, 2, 48),
-                                (2, 2, 7, 128), (4, 2, 3, 64), (3, 2, 2, 48)]:
+                                (2, 2, 7, 128), (4, 2, 3, 64), (3, 2, 2, 48), (2, 2, 7, 96),
+                                (2, 2, 1, 16)]:
         plan = smla.make_plan(splits, tiles)
         assert smla.workspace_size(plan, T, H) == expect(T, H, splits, tiles)
     assert smla.workspace_size(smla.make_plan(1, 1), 7, 128) == 0
     # bad plans and sizes report 0
     assert smla.workspace_size(smla.make_plan(0, 1), 7, 128) == 0
     assert smla.workspace_size(smla.make_plan(65, 1), 7, 128) == 0
-    assert smla.workspace_size(smla.make_plan(2, 2), 7, 96) == 0    # 3 tiles: not in pairs
     assert smla.workspace_size(smla.make_plan(2, 4), 7, 128) == 0   # 1 or 2 tiles per WG
     assert smla.workspace_size(smla.make_plan(2, 1), 7, 120) == 0   # H % 16 != 0
 
@@ -68,7 +68,7 @@ def _decode(T=1, H=16, W=64, row_bytes=576, qk_dim=576, flags=0, plan=None, q=16
     dict(T=-1), dict(H=0), dict(H=24), dict(W=0), dict(row_bytes=640), dict(qk_dim=448),
     dict(row_bytes=512, qk_dim=576), dict(flags=0x4), dict(bmm1=float("nan")),
     dict(bmm1=float("inf")), dict(plan=smla.make_plan(0, 1)), dict(plan=smla.make_plan(1, 3)),
-    dict(plan=smla.make_plan(1, 2)),  # 16 heads: one 32-head tile, not a pair
+    dict(plan=smla.make_plan(1, 0)), dict(plan=smla.make_plan(65, 2)),
     dict(q=0), dict(kv=0), dict(idx=0), dict(lens=0), dict(out=0), dict(rows_a=0),
     dict(q=24), dict(kv=8), dict(out=40), dict(idx=18), dict(lens=2), dict(stride_h=8),
     dict(stride_t=-576), dict(kv_b=16, rows_b=0), dict(kv_b=16, rows_b=5, split_col=65),

@@ -73,6 +73,13 @@ CASES = {
     "H128_rows576_qk512": dict(seed=509, T=2, H=128, W=200, qk_dim=512, lens=[200, 71]),
     "H64_long_range": dict(seed=510, T=2, H=64, W=2048, lens=[2048, 1000], neg_frac=0.05,
                            pool_rows=6000),
+    # one 32-head tile, or an odd count of them: the last 64-head group is padded
+    "H16_padded_group": dict(seed=511, T=3, H=16, W=300, lens=[300, 0, 190], neg_frac=0.1,
+                             sinks=True),
+    "H96_three_tiles": dict(seed=512, T=2, H=96, W=200, lens=[200, 133]),
+    "H16_rows512_two_pools": dict(seed=513, T=2, H=16, W=640, row_bytes=512, two_pools=True,
+                                  split_col=128, rows_b=5000, sinks=True, neg_frac=0.1,
+                                  lens=[640, 431]),
 }
 
 
