@@ -58,7 +58,8 @@ typedef int32_t smla_status;
  * contiguous ranges of the token's clamped count (range s = [min(n, s*per), +min(n - first,
  * per)), per = ceil(n / splits), as the attn_sparse page's key split); the ranges run in chunks
  * of `chunk` columns and, when splits > 1, the last range of a (token, head group) to finish
- * merges the FP32 partials of all of them. */
+ * merges the partials of all of them (each range's output normalized by its own sum, exchanged
+ * as FP16, with its frame and sum in FP32). */
 typedef struct smla_plan {
     int32_t splits; /* 1 .. 64 */
     int32_t tiles;  /* 32-head tiles per workgroup: 1 (32 heads, rows loaded into registers) or
@@ -78,8 +79,8 @@ smla_status smla_decode_plan(int32_t T, int32_t H, int32_t W, int32_t row_bytes,
                              smla_plan *plan);
 
 /* Workspace bytes sparse_mla_decode needs under `plan` (0 when plan->splits == 1): arrival
- * counters (two int32 per token and head group, rounded up to 256 bytes), FP32 partials
- * [T, groups, splits, 32 tiles, 512] and (frame, sum) pairs [T, groups, splits, 32 tiles, 2],
+ * counters (two int32 per token and head group, rounded up to 256 bytes), FP16 partials
+ * [T, groups, splits, 32 tiles, 512] and FP32 (frame, sum) pairs [T, groups, splits, 32 tiles, 2],
  * groups = ceil(ceil(H / 32) / tiles).  0 for a bad plan. */
 size_t smla_decode_workspace_size(const smla_plan *plan, int32_t T, int32_t H);
 

@@ -89,9 +89,10 @@ bool plan_ok(const smla_plan *p, int32_t H)
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Workspace layout under a valid plan: counters [T, groups, 2] int32 (arrival ticket and
-// ready count, zero between calls), then FP32 partials: one block of 32 tiles x 512 floats per
-// (token, head group, range), in the order the kernel's accumulator registers are stored (16-byte
-// runs per lane), then (frame, sum) [T, groups, splits, 32 tiles heads, 2].
+// ready count, zero between calls), then partials: one block of 32 tiles x 512 FP16 values per
+// (token, head group, range), each range's output normalized by its own sum, in the order the
+// kernel's accumulator registers are stored (16-byte runs per lane), then (frame, sum)
+// [T, groups, splits, 32 tiles heads, 2].
 struct WsLayout {
     size_t counters, partials, ml, total;
 };
@@ -104,7 +105,7 @@ WsLayout ws_layout(const smla_plan *plan, int32_t T, int32_t H)
     WsLayout w;
     w.counters = 0;
     w.partials = align256((size_t)T * groups * 2 * sizeof(int32_t));
-    w.ml = w.partials + units * hg * 512 * sizeof(float);
+    w.ml = w.partials + units * hg * 512 * sizeof(uint16_t);
     w.total = w.ml + units * hg * 2 * sizeof(float);
     return w;
 }
@@ -245,7 +246,7 @@ smla_status sparse_mla_decode(const void *q, int64_t q_stride_t, int64_t q_strid
         const WsLayout w = ws_layout(&chosen, T, H);
         uint8_t *base = static_cast<uint8_t *>(workspace);
         p.counters = reinterpret_cast<int32_t *>(base + w.counters);
-        p.ws_o = reinterpret_cast<float *>(base + w.partials);
+        p.ws_o = reinterpret_cast<uint16_t *>(base + w.partials);
         p.ws_ml = reinterpret_cast<float *>(base + w.ml);
     }
     const hipError_t e = smla::launch_decode(p, chosen.tiles, row_bytes, qk_dim,

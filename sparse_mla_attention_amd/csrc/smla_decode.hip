@@ -144,20 +144,23 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(DecodeParams a)
         const int64_t tg = (int64_t)t * a.groups + hg;
         const int tile0 = NCT * w;
         if (a.splits > 1) {
-            // Split merge.  Every range writes its partial (FP32 accumulators, then (G, l) per
+            // Split merge.  Every range writes its partial (its output normalized by its own sum,
+            // a weighted mean of V rows bounded by the largest |V|, in FP16; then (G, l) per
             // head) with device-scope (write-through) stores, waits for them to complete and
             // only then takes an arrival ticket; the range holding the last ticket therefore
             // sees every other partial complete and merges all of them in range order, its own
-            // from registers.  (With few workgroups this beats taking the ticket first: the
+            // from registers, rounded as it was stored (so the result does not depend on the
+            // arrival order).  (With few workgroups this beats taking the ticket first: the
             // stores of all ranges overlap instead of following the ticket round trip.)
-            // Partial layout: accumulator registers 4 j .. 4 j + 3 of tile `tile` at byte
-            // ((tile * 4 + j) * 64 + lane) * 16, one 16-byte access per lane.
+            // Partial layout: accumulator registers 8 j .. 8 j + 7 of tile `tile` at byte
+            // ((tile * 2 + j) * 64 + lane) * 16, one 16-byte access per lane.
             constexpr int SC1 = 16;  // cache policy of device-scope (write-through) accesses
-            auto part_off = [&](int ct, int j) { return (((tile0 + ct) * 4 + j) * 64 + lane) * 16; };
+            auto part_off = [&](int ct, int j) { return (((tile0 + ct) * 2 + j) * 64 + lane) * 16; };
             auto part_rsrc = [&](int64_t unit) {
                 return __builtin_amdgcn_make_buffer_rsrc(a.ws_o + unit * (HG * 512), 0,
-                                                         HG * 512 * 4, 0x00020000);
+                                                         HG * 512 * 2, 0x00020000);
             };
+            const float inv_l = l_h > 0.0f ? __builtin_amdgcn_rcpf(l_h) : 0.0f;
             int *ticket = reinterpret_cast<int *>(lds + L::MISC);
             int *ctr = a.counters + 2 * tg;         // [0] arrival ticket
             {
@@ -165,14 +168,13 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(DecodeParams a)
                 if (!s_wave) {
                     const auto rs = part_rsrc(ui);
 #pragma unroll
-                    for (int ct = 0; ct < NCT; ct++)
+                    for (int ct = 0; ct < NCT; ct++) {
+                        v4i pk[2];
+                        f16_pack(acc[ct], inv_l, pk);
 #pragma unroll
-                        for (int j = 0; j < 4; j++)
-                            __builtin_amdgcn_raw_buffer_store_b128(
-                                v4i{__float_as_int(acc[ct][4 * j]), __float_as_int(acc[ct][4 * j + 1]),
-                                    __float_as_int(acc[ct][4 * j + 2]),
-                                    __float_as_int(acc[ct][4 * j + 3])},
-                                rs, part_off(ct, j), 0, SC1);
+                        for (int j = 0; j < 2; j++)
+                            __builtin_amdgcn_raw_buffer_store_b128(pk[j], rs, part_off(ct, j), 0, SC1);
+                    }
                 }
                 if (wave == 4 && u == 0) {
                     store_device(a.ws_ml + (ui * HG + hl) * 2 + 0, g_h);
@@ -214,27 +216,32 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(DecodeParams a)
                     sum[ct] = v16f{};
                 for (int s = 0; s < a.splits; s++) {
                     const float gs = s == split ? g_h : gl[s * HG + hl].x;
-                    const float wgt = gs == -INFINITY ? 0.0f : exp2f(gs - big_g);
+                    const float ls = s == split ? l_h : gl[s * HG + hl].y;
+                    // the values are normalized: weight w l
+                    const float wgt = (gs == -INFINITY ? 0.0f : exp2f(gs - big_g)) * ls;
                     if (s == split) {
 #pragma unroll
-                        for (int ct = 0; ct < NCT; ct++)
+                        for (int ct = 0; ct < NCT; ct++) {
+                            v4i own[2];
+                            f16_pack(acc[ct], inv_l, own);
 #pragma unroll
                             for (int r = 0; r < 16; r++)
-                                sum[ct][r] += wgt * acc[ct][r];
+                                sum[ct][r] += wgt * f16_unpack(own, r);
+                        }
                     } else {
                         const auto rs = part_rsrc(tg * a.splits + s);
-                        v4i v[NCT][4];
+                        v4i v[NCT][2];
 #pragma unroll
                         for (int ct = 0; ct < NCT; ct++)
 #pragma unroll
-                            for (int j = 0; j < 4; j++)
+                            for (int j = 0; j < 2; j++)
                                 v[ct][j] = __builtin_amdgcn_raw_buffer_load_b128(
                                     rs, part_off(ct, j), 0, SC1);
 #pragma unroll
                         for (int ct = 0; ct < NCT; ct++)
 #pragma unroll
                             for (int r = 0; r < 16; r++)
-                                sum[ct][r] += wgt * __int_as_float(v[ct][r >> 2][r & 3]);
+                                sum[ct][r] += wgt * f16_unpack(v[ct], r);
                     }
                 }
 #pragma unroll

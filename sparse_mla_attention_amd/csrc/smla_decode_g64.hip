@@ -184,20 +184,21 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
                              reinterpret_cast<const int *>(fin)[5 * HG + head]);
         }
         const int64_t tg = (int64_t)t * a.groups + hg;
-        // Byte offset of accumulator registers 4 j .. 4 j + 3 of tile (ct, h2) in a range's
-        // partial: 16 bytes per lane, one 1 KB run per (tile, j) across the wave, so every
-        // store and load of the exchange is one 16-byte access per lane.
+        // A range's partial is its output normalized by its own sum (a weighted mean of V
+        // rows, so bounded by the largest |V|), in FP16.  Byte offset of accumulator registers
+        // 8 j .. 8 j + 7 of tile (ct, h2): 16 bytes per lane, one 1 KB run per (tile, j) across
+        // the wave, so every store and load of the exchange is one 16-byte access per lane.
         auto part_off = [&](int ct, int h2, int j) {
-            return ((((NCT * w + ct) * 2 + h2) * 4 + j) * 64 + lane) * 16;
+            return ((((NCT * w + ct) * 2 + h2) * 2 + j) * 64 + lane) * 16;
         };
         constexpr int SC1 = 16;  // cache policy of device-scope (write-through) accesses
         auto part_rsrc = [&](int64_t unit) {
-            return __builtin_amdgcn_make_buffer_rsrc(a.ws_o + unit * (HG * 512), 0, HG * 512 * 4,
+            return __builtin_amdgcn_make_buffer_rsrc(a.ws_o + unit * (HG * 512), 0, HG * 512 * 2,
                                                      0x00020000);
         };
         if (a.splits > 1) {
             // Split merge.  Each range takes an arrival ticket first.  Every range but the last
-            // writes its partial (FP32 accumulators in register order, then (G, l) per head)
+            // writes its partial (normalized FP16 in register order, then (G, l) per head)
             // with device-scope (write-through) stores, waits for them to complete and bumps
             // the ready count; the last range waits until the ready count shows every other
             // partial, then merges all of them in range order, its own from registers.  The
@@ -213,18 +214,21 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
                 const int64_t ui = tg * a.splits + split;
                 if (!qk_wave) {
                     const auto rs = part_rsrc(ui);
+                    float inv_l[2];
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; h2++)
+                        inv_l[h2] = l_h[h2] > 0.0f ? __builtin_amdgcn_rcpf(l_h[h2]) : 0.0f;
 #pragma unroll
                     for (int ct = 0; ct < NCT; ct++)
 #pragma unroll
-                        for (int h2 = 0; h2 < 2; h2++)
+                        for (int h2 = 0; h2 < 2; h2++) {
+                            v4i pk[2];
+                            f16_pack(acc[ct][h2], inv_l[h2], pk);
 #pragma unroll
-                            for (int j = 0; j < 4; j++)
-                                __builtin_amdgcn_raw_buffer_store_b128(
-                                    v4i{__float_as_int(acc[ct][h2][4 * j]),
-                                        __float_as_int(acc[ct][h2][4 * j + 1]),
-                                        __float_as_int(acc[ct][h2][4 * j + 2]),
-                                        __float_as_int(acc[ct][h2][4 * j + 3])},
-                                    rs, part_off(ct, h2, j), 0, SC1);
+                            for (int j = 0; j < 2; j++)
+                                __builtin_amdgcn_raw_buffer_store_b128(pk[j], rs,
+                                                                       part_off(ct, h2, j), 0, SC1);
+                        }
                 }
                 if (wave == 4 && u == 0) {
 #pragma unroll
@@ -248,12 +252,23 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
                 }
             }
             __syncthreads();
-            // merge in range order, own partial from registers, the others' from the workspace
-            float own_g[2], own_l[2];
+            // Merge in range order, own partial from registers, the others' from the workspace.
+            // The own partial is normalized and rounded to FP16 exactly as a writer stores it, so
+            // the result does not depend on which range arrived last.
+            float own_g[2], own_l[2], own_inv[2];
 #pragma unroll
             for (int h2 = 0; h2 < 2; h2++) {
                 own_g[h2] = g_h[h2];
                 own_l[h2] = l_h[h2];
+                own_inv[h2] = l_h[h2] > 0.0f ? __builtin_amdgcn_rcpf(l_h[h2]) : 0.0f;
+            }
+            v4i own[NCT][2][2];  // the own partial as it would have been stored
+            if (!qk_wave) {
+#pragma unroll
+                for (int ct = 0; ct < NCT; ct++)
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; h2++)
+                        f16_pack(acc[ct][h2], own_inv[h2], own[ct][h2]);
             }
             if (a.splits == 2) {
                 // Two ranges: the other range's (G, l) and its first column tile come in one
@@ -262,13 +277,13 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
                 const int other = 1 - split;
                 const int64_t uo = tg * 2 + other;
                 float og[2], ol[2];
-                v4i cur[2][4], nxt[2][4];
+                v4i cur[2][2], nxt[2][2];
                 if (!qk_wave) {
                     const auto rs = part_rsrc(uo);
 #pragma unroll
                     for (int h2 = 0; h2 < 2; h2++)
 #pragma unroll
-                        for (int j = 0; j < 4; j++)
+                        for (int j = 0; j < 2; j++)
                             cur[h2][j] = __builtin_amdgcn_raw_buffer_load_b128(
                                 rs, part_off(0, h2, j), 0, SC1);
                 }
@@ -278,7 +293,7 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
                     og[h2] = load_device(a.ws_ml + m);
                     ol[h2] = load_device(a.ws_ml + m + 1);
                 }
-                float w_s[2][2];  // [range][h2]
+                float c_s[2][2];  // [range][h2]: weight of the range's values in the merged sum
 #pragma unroll
                 for (int h2 = 0; h2 < 2; h2++) {
                     const float gr[2] = {split == 0 ? own_g[h2] : og[h2],
@@ -289,8 +304,9 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
                     l_h[h2] = 0.0f;
 #pragma unroll
                     for (int r = 0; r < 2; r++) {
-                        w_s[r][h2] = gr[r] == -INFINITY ? 0.0f : exp2f(gr[r] - g_h[h2]);
-                        l_h[h2] += w_s[r][h2] * lr[r];
+                        const float w_r = gr[r] == -INFINITY ? 0.0f : exp2f(gr[r] - g_h[h2]);
+                        l_h[h2] += w_r * lr[r];
+                        c_s[r][h2] = w_r * lr[r];  // both ranges' values are normalized
                     }
                 }
                 if (!qk_wave) {
@@ -301,27 +317,29 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
 #pragma unroll
                             for (int h2 = 0; h2 < 2; h2++)
 #pragma unroll
-                                for (int j = 0; j < 4; j++)
+                                for (int j = 0; j < 2; j++)
                                     nxt[h2][j] = __builtin_amdgcn_raw_buffer_load_b128(
                                         rs, part_off(ct + 1, h2, j), 0, SC1);
                         }
 #pragma unroll
-                        for (int h2 = 0; h2 < 2; h2++)
+                        for (int h2 = 0; h2 < 2; h2++) {
 #pragma unroll
                             for (int rr = 0; rr < 16; rr++) {
-                                const float xo = __int_as_float(cur[h2][rr >> 2][rr & 3]);
-                                const float x0 = split == 0 ? acc[ct][h2][rr] : xo;
-                                const float x1 = split == 1 ? acc[ct][h2][rr] : xo;
+                                const float xo = f16_unpack(cur[h2], rr);
+                                const float xs = f16_unpack(own[ct][h2], rr);
+                                const float x0 = split == 0 ? xs : xo;
+                                const float x1 = split == 1 ? xs : xo;
                                 float sum = 0.0f;
-                                sum += w_s[0][h2] * x0;
-                                sum += w_s[1][h2] * x1;
+                                sum += c_s[0][h2] * x0;
+                                sum += c_s[1][h2] * x1;
                                 acc[ct][h2][rr] = sum;
                             }
+                        }
                         if (ct + 1 < NCT) {
 #pragma unroll
                             for (int h2 = 0; h2 < 2; h2++)
 #pragma unroll
-                                for (int j = 0; j < 4; j++)
+                                for (int j = 0; j < 2; j++)
                                     cur[h2][j] = nxt[h2][j];
                         }
                     }
@@ -355,34 +373,34 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
                         v16f sum[2] = {v16f{}, v16f{}};
                         for (int s = 0; s < a.splits; s++) {
                             const int64_t us = tg * a.splits + s;
-                            float w_s[2];
+                            float w_s[2];  // every range's values are normalized: weight w l
 #pragma unroll
                             for (int h2 = 0; h2 < 2; h2++) {
-                                const float gs =
-                                    s == split ? own_g[h2]
-                                               : load_device(a.ws_ml + (us * HG + 32 * h2 + hl) * 2);
-                                w_s[h2] = gs == -INFINITY ? 0.0f : exp2f(gs - g_h[h2]);
+                                const int64_t m = (us * HG + 32 * h2 + hl) * 2;
+                                const float gs = s == split ? own_g[h2] : load_device(a.ws_ml + m);
+                                const float ls = s == split ? own_l[h2] : load_device(a.ws_ml + m + 1);
+                                w_s[h2] = (gs == -INFINITY ? 0.0f : exp2f(gs - g_h[h2])) * ls;
                             }
                             if (s == split) {
 #pragma unroll
                                 for (int h2 = 0; h2 < 2; h2++)
 #pragma unroll
                                     for (int rr = 0; rr < 16; rr++)
-                                        sum[h2][rr] += w_s[h2] * acc[ct][h2][rr];
+                                        sum[h2][rr] += w_s[h2] * f16_unpack(own[ct][h2], rr);
                             } else {
                                 const auto rs = part_rsrc(us);
-                                v4i v[2][4];
+                                v4i v[2][2];
 #pragma unroll
                                 for (int h2 = 0; h2 < 2; h2++)
 #pragma unroll
-                                    for (int j = 0; j < 4; j++)
+                                    for (int j = 0; j < 2; j++)
                                         v[h2][j] = __builtin_amdgcn_raw_buffer_load_b128(
                                             rs, part_off(ct, h2, j), 0, SC1);
 #pragma unroll
                                 for (int h2 = 0; h2 < 2; h2++)
 #pragma unroll
                                     for (int rr = 0; rr < 16; rr++)
-                                        sum[h2][rr] += w_s[h2] * __int_as_float(v[h2][rr >> 2][rr & 3]);
+                                        sum[h2][rr] += w_s[h2] * f16_unpack(v[h2], rr);
                             }
                         }
                         acc[ct][0] = sum[0];

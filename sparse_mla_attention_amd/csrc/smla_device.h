@@ -183,6 +183,33 @@ __device__ inline uint32_t bf16x2(float lo, float hi)
     return __builtin_bit_cast(uint32_t, r);
 }
 
+// A tile's 16 accumulator registers times `scale`, as FP16 pairs in register order: word d of
+// part j holds registers 8 j + 2 d (low half) and 8 j + 2 d + 1.  The conversion instruction is
+// written out so that it rounds the FP32 products to nearest even; left to itself the compiler
+// may fuse a product and its conversion into a mixed-precision instruction that rounds once, and
+// every site that packs the same values must get the same bits.
+__device__ inline void f16_pack(const v16f &x, float scale, v4i (&pk)[2])
+{
+#pragma unroll
+    for (int j = 0; j < 2; j++)
+#pragma unroll
+        for (int d = 0; d < 4; d++) {
+            const float lo = x[8 * j + 2 * d] * scale, hi = x[8 * j + 2 * d + 1] * scale;
+            int r;
+            asm("v_cvt_pk_f16_f32 %0, %1, %2" : "=v"(r) : "v"(lo), "v"(hi));
+            pk[j][d] = r;
+        }
+}
+// register r of a tile packed by f16_pack
+__device__ inline float f16_unpack(const v4i (&pk)[2], int r)
+{
+    typedef _Float16 v2f16 __attribute__((ext_vector_type(2)));
+    // (the element goes through a local: this compiler bit-casts a vector-element lvalue from
+    // element 0 whatever the index)
+    const int word = pk[r >> 3][(r >> 1) & 3];
+    return (float)__builtin_bit_cast(v2f16, word)[r & 1];
+}
+
 // Pad between the last matrix instruction of a chain and the first vector read of its result.
 // A result of the block-scaled 32x32x64 FP8 instruction read 19 wait states after issue was
 // measured to hold the chain's previous partial sum, so fresh results are read behind 24

@@ -22,13 +22,13 @@ struct DecodeParams {
     uint16_t *out;              // BF16 [T, H, 512]
     float *lse;                 // [T, H] or null
     int32_t lse_log2;           // 1: base-2 LSE
-    float *ws_o;                // FP32 partials: a block of (heads per group) x 512 floats per
-                                // (token, group, range), in the kernel's register order
+    uint16_t *ws_o;             // FP16 partials: a block of (heads per group) x 512 values
+                                // per (token, group, range), in the kernel's register order
     float *ws_ml;               // (frame, sum) [T, groups, splits, heads per group, 2]
     int32_t *counters;          // [T, groups, 2]: arrival ticket, ready count; zero between
                                 // calls (splits > 1)
     int32_t splits;             // key ranges per (token, head group)
-    int32_t groups;             // head groups per token = ceil(H / 32) / tiles
+    int32_t groups;             // head groups per token = ceil(ceil(H / 32) / tiles)
 };
 
 // Longest key range (columns) the 64-head kernel takes: its range's row indices are staged in
