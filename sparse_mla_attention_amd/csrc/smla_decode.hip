@@ -47,10 +47,10 @@
 //   chunks c-1 .. c+1.
 //
 // Epilogue: one range (S = 1): merge with the sink, BF16 output through an LDS tile (coalesced
-// row stores) and the LSE.  S > 1: every range writes its FP32 partial (in register order, so
-// reads and writes coalesce) and (G, l); the last range to finish (atomic ticket per token and
-// head group) merges all partials in range order, weights 2^(G_s - M), writes the output and
-// resets the ticket.
+// row stores) and the LSE.  S > 1: every range writes its partial (its output normalized by its
+// own sum, in FP16 and register order, so reads and writes coalesce) and (G, l); the last range
+// to finish (atomic ticket per token and head group) merges all partials in range order,
+// weights 2^(G_s - M) l_s, writes the output and resets the ticket.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
