@@ -58,8 +58,9 @@ typedef int32_t smla_status;
  * contiguous ranges of the token's clamped count (range s = [min(n, s*per), +min(n - first,
  * per)), per = ceil(n / splits), as the attn_sparse page's key split); the ranges run in chunks
  * of `chunk` columns and, when splits > 1, the last range of a (token, head group) to finish
- * merges the partials of all of them (each range's output normalized by its own sum, exchanged
- * as FP16, with its frame and sum in FP32). */
+ * merges the FP32 partials of all of them (each range's FP32 accumulators with its frame and
+ * sum; the attn_sparse page's module docstring, "Precision": the split partials merge in
+ * FP32). */
 typedef struct smla_plan {
     int32_t splits; /* 1 .. 64 */
     int32_t tiles;  /* 32-head tiles per workgroup: 1 (32 heads, rows loaded into registers) or
@@ -78,10 +79,18 @@ typedef struct smla_plan {
 smla_status smla_decode_plan(int32_t T, int32_t H, int32_t W, int32_t row_bytes, uint32_t flags,
                              smla_plan *plan);
 
-/* Workspace bytes sparse_mla_decode needs under `plan` (0 when plan->splits == 1): arrival
- * counters (two int32 per token and head group, rounded up to 256 bytes), FP16 partials
- * [T, groups, splits, 32 tiles, 512] and FP32 (frame, sum) pairs [T, groups, splits, 32 tiles, 2],
- * groups = ceil(ceil(H / 32) / tiles).  0 for a bad plan. */
+/* Workspace bytes sparse_mla_decode needs under `plan` (0 when plan->splits == 1).  The caller
+ * sizes and allocates it once, before any graph capture, and reuses it across calls that are
+ * stream ordered (the dcp page, stock_decode: a split-KV workspace sized before capture, shared
+ * by stream-ordered calls, no per-call allocation).  Layout:
+ *   bytes [0, 4)    status word, int32: the number of (token, head group) split merges that gave
+ *                   up waiting for the other key ranges' partials since the workspace was last
+ *                   zero-filled (0 in normal operation; see sparse_mla_decode);
+ *   bytes [16, ..)  arrival counters, two int32 per token and head group, then padding to a
+ *                   multiple of 256 bytes;
+ *   then            FP32 partials [T, groups, splits, 32 tiles, 512] and FP32 (frame, sum) pairs
+ *                   [T, groups, splits, 32 tiles, 2], groups = ceil(ceil(H / 32) / tiles).
+ * Returns 0 for a bad plan. */
 size_t smla_decode_workspace_size(const smla_plan *plan, int32_t T, int32_t H);
 
 /*
@@ -109,9 +118,15 @@ size_t smla_decode_workspace_size(const smla_plan *plan, int32_t T, int32_t H);
  *                bit-identical from run to run for a fixed plan).
  *   workspace    device scratch of workspace_bytes >= smla_decode_workspace_size(plan, T, H),
  *                16-byte aligned (may be NULL when that size is 0).  Zero-fill it once before
- *                its first use: its first bytes hold arrival counters that must start at zero,
- *                and every call leaves them at zero again (the rest is overwritten before it
- *                is read).  Calls that share a workspace must be stream-ordered.
+ *                its first use: its first bytes hold a status word and arrival counters that
+ *                must start at zero, and every call leaves them at zero again (the partials are
+ *                overwritten before they are read).  Calls that share a workspace must be
+ *                stream-ordered.  With 64 heads per workgroup (plan tiles = 2) the range that
+ *                merges waits for the others' partials with a bounded poll (2^24 polls, about
+ *                half a second); if the bound runs out it adds 1 to the status word, writes NaN
+ *                to its heads' outputs and LSEs and leaves the counters non-zero: a caller that
+ *                finds the status word non-zero must treat those outputs as failed and zero-fill
+ *                the workspace again before its next use.
  *
  * P anchoring: within a key range, the first chunk with an active column fixes the frame G
  * (its running maximum) and each chunk quantizes P = 2^(s2 - F + log2 448) at F = G +
@@ -161,8 +176,17 @@ smla_status sparse_mla_decode(const void *q, int64_t q_stride_t, int64_t q_strid
 smla_status lse_merge(const void *partials, const float *lse2, int32_t S, int32_t T, int32_t H,
                       int32_t D, void *out, float *lse_out, uint32_t flags, hipStream_t stream);
 
-/* A static string describing a status code. */
+/* A static string describing a status code (the pages raise RuntimeError or assert on bad
+ * arguments; a C caller gets a status code and this text instead). */
 const char *smla_strerror(smla_status status);
+
+/* Test hook, not for production callers: bounds the 64-head kernel's split-merge wait to
+ * max_polls polls (0 restores the default, 2^24) and, with unreachable = 1, makes the merging
+ * range wait for one partial more than exists, so every such wait gives up after max_polls polls
+ * and takes the failure path described under sparse_mla_decode while every kernel still exits
+ * normally.  Process-wide; not thread-safe against concurrent calls.  SMLA_EINVAL for
+ * max_polls < 0 or unreachable not in {0, 1}. */
+smla_status smla_testing_set_merge_wait(int32_t max_polls, int32_t unreachable);
 
 #ifdef __cplusplus
 }

@@ -62,7 +62,7 @@ def lib():
         common = [P, I64, I64, P, I64, P, I64, I32, I32, I32, P, P, I32, I32, I32, D, D, P, U32]
         L.oracle_decode_exact.argtypes = common + [P, I32, P, P]
         L.oracle_decode_exact.restype = ctypes.c_int
-        L.oracle_decode_mimic.argtypes = common + [I32, I32, D, I32, I32, I32, P, I32, P, P]
+        L.oracle_decode_mimic.argtypes = common + [I32, I32, D, I32, I32, P, I32, P, P]
         L.oracle_decode_mimic.restype = ctypes.c_int
         L.oracle_lse_merge.argtypes = [P, P, I32, I32, I32, I32, U32, P, P]
         L.oracle_lse_merge.restype = ctypes.c_int
@@ -133,11 +133,9 @@ def decode_exact(p, lse_log2=False, units=None):
 
 
 def decode_mimic(p, splits, chunk, anchor=448.0, terms=1, quantize=True, lse_log2=False,
-                 units=None, frame_limit=0):
-    """Mimic mode (the E4M3-P recipe with the given split count and chunk size).
-    frame_limit > 0: frame anchoring (P anchored at G + ceil(m - G); a range whose offset
-    exceeds frame_limit reruns with G preset to its maximum); 0: the recipe's exact
-    running-max anchor."""
+                 units=None):
+    """Mimic mode: the E4M3-P recipe (P anchored at the running maximum, accumulators and sums
+    rescaled when it rises) with the given split count and chunk size."""
     args, keep, T, H = _problem_args(p)
     u, n = _units_array(units)
     count = n if u is not None else T * H
@@ -145,7 +143,7 @@ def decode_mimic(p, splits, chunk, anchor=448.0, terms=1, quantize=True, lse_log
     lse = np.empty((count,), dtype=np.float64)
     _check(lib().oracle_decode_mimic(*args, LSE_LOG2 if lse_log2 else 0, int(splits), int(chunk),
                                      float(anchor), int(terms), 1 if quantize else 0,
-                                     int(frame_limit), _ptr(u), n, _ptr(out), _ptr(lse)))
+                                     _ptr(u), n, _ptr(out), _ptr(lse)))
     del keep
     return out, lse
 

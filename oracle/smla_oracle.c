@@ -196,7 +196,6 @@ static int check_problem(const problem *p)
 }
 
 #define V_DIM 512 /* V is the first 512 bytes of a row on every page */
-#define E_FLOOR (-120.0) /* frame mode: smallest offset e of a second pass */
 
 /* ---------------------------------------------------------------------------
  * C1: exact mode, the formula of the sparse_mla_cute page, with the LSE
@@ -298,19 +297,6 @@ int oracle_decode_exact(
  * base-2 sink), w = 2^(m - M), L = sum w l (+ anchor * 2^(sink2 - M)),
  * out = bmm2 * sum w acc / L, LSE2 = M - log2 anchor + log2 L.
  * With `quantize` = 0, p_hat = p (no rounding), which reduces to exact mode.
- *
- * frame_limit > 0 selects frame anchoring, a variant of the recipe in which the
- * anchor moves in whole powers of two (the reading used by the GPU path, whose
- * matrix instructions apply power-of-two block scales): per range, G is the
- * running max after the first chunk that has one, each later chunk anchors P
- * at F = G + e with e = ceil(m_new - G), so P <= anchor still holds; the
- * chunk's p_hat v and p enter acc and l in frame G with weight 2^e, and acc and
- * l are never rescaled.  If some chunk's e exceeds frame_limit (the scores grew
- * by that many binades), the range is run a second time with G fixed in advance
- * at the range's maximum: then e = ceil(m_new - G) <= 0, raised to E_FLOOR when
- * lower (P <= anchor still holds), and 0 while the range has no active column.
- * The range reports m = G.  A single chunk gives e = 0, i.e. the recipe itself;
- * without quantization either pass is exact mode.
  * ------------------------------------------------------------------------- */
 int oracle_decode_mimic(
     const uint8_t *q, int64_t q_stride_t, int64_t q_stride_h,
@@ -321,7 +307,6 @@ int oracle_decode_mimic(
     int32_t T, int32_t H, int32_t W,
     double bmm1, double bmm2, const float *sinks, uint32_t flags,
     int32_t splits, int32_t chunk, double anchor, int32_t terms, int32_t quantize,
-    int32_t frame_limit,
     const int32_t *units, int32_t n_units,
     double *out, double *lse)
 {
@@ -333,7 +318,7 @@ int oracle_decode_mimic(
     double *m_s, *l_s, *acc_s, *s2, *phat;
     if (status != ORACLE_OK)
         return status;
-    if (splits < 1 || chunk < 1 || !(anchor > 0) || terms < 1 || terms > 2 || frame_limit < 0)
+    if (splits < 1 || chunk < 1 || !(anchor > 0) || terms < 1 || terms > 2)
         return ORACLE_EBADARG;
     m_s = (double *)malloc(sizeof(double) * (size_t)splits);
     l_s = (double *)malloc(sizeof(double) * (size_t)splits);
@@ -360,11 +345,7 @@ int oracle_decode_mimic(
             int first = s * per < n ? s * per : n;
             int mine = n - first < per ? n - first : per;
             double m_run = -INFINITY, l_run = 0.0;
-            double frame = -INFINITY; /* frame mode: the base G of acc and l_run */
-            int preset = 0;           /* frame mode, second pass: G fixed in advance */
-            double e_max = 0.0;       /* frame mode: largest offset e of the pass */
             double *acc = acc_s + (int64_t)s * V_DIM;
-        range_pass:
             for (int j = 0; j < V_DIM; j++)
                 acc[j] = 0.0;
             for (int base = first; base < first + mine && status == ORACLE_OK; base += chunk) {
@@ -385,27 +366,10 @@ int oracle_decode_mimic(
                 }
                 if (status != ORACLE_OK)
                     break;
+                /* the running maximum and the rescale of what came before it */
                 m_new = m_run > chunk_max ? m_run : chunk_max;
-                if (frame_limit > 0) {
-                    /* frame mode: P is anchored at F = G + e, e = ceil(m_new - G) >= 0, so
-                     * that P <= anchor; acc and l_run stay in frame G and this chunk's
-                     * terms enter scaled by 2^e (exact).  When e exceeds the limit the frame
-                     * moves up by e: acc and l_run are scaled by 2^-e and e becomes 0. */
-                    double e = 0.0;
-                    if (frame == -INFINITY)
-                        frame = m_new; /* first chunk with an active column (or still -inf) */
-                    else if (m_new != -INFINITY)
-                        e = ceil(m_new - frame);
-                    if (preset && e < E_FLOOR)
-                        e = E_FLOOR;
-                    if (e > e_max)
-                        e_max = e;
-                    alpha = ldexp(1.0, (int)e); /* weight of this chunk's terms in frame G */
-                    bias = (frame == -INFINITY) ? 0.0 : frame + e - log2(anchor);
-                } else {
-                    alpha = (m_run == -INFINITY) ? 1.0 : exp2(m_run - m_new);
-                    bias = m_new - log2(anchor);
-                }
+                alpha = (m_run == -INFINITY) ? 1.0 : exp2(m_run - m_new);
+                bias = (m_new == -INFINITY) ? 0.0 : m_new - log2(anchor);
                 for (int i = 0; i < cnt; i++) {
                     double pv = 0.0, hi;
                     if (s2[i] != -INFINITY)
@@ -420,34 +384,20 @@ int oracle_decode_mimic(
                     if (terms == 2)
                         phat[i] += oracle_e4m3_value(oracle_e4m3_encode(16.0 * (pv - hi))) / 16.0;
                 }
-                if (frame_limit > 0) {
-                    l_run += alpha * sum_p;
-                } else {
-                    l_run = l_run * alpha + sum_p;
-                    for (int j = 0; j < V_DIM; j++)
-                        acc[j] *= alpha;
-                }
+                l_run = l_run * alpha + sum_p;
+                for (int j = 0; j < V_DIM; j++)
+                    acc[j] *= alpha;
                 for (int i = 0; i < cnt; i++) {
                     const uint8_t *row;
-                    double w = frame_limit > 0 ? phat[i] * alpha : phat[i];
                     if (phat[i] == 0.0)
                         continue; /* inactive, or P rounded to zero */
                     row = row_of(&p, t, base + i, &status);
                     for (int j = 0; j < V_DIM; j++)
-                        acc[j] += w * oracle_e4m3_value(row[j]);
+                        acc[j] += phat[i] * oracle_e4m3_value(row[j]);
                 }
                 m_run = m_new;
             }
-            if (status == ORACLE_OK && frame_limit > 0 && !preset && e_max > frame_limit) {
-                /* second pass: G = the range's maximum, known now */
-                preset = 1;
-                frame = m_run;
-                m_run = -INFINITY;
-                l_run = 0.0;
-                e_max = 0.0;
-                goto range_pass;
-            }
-            m_s[s] = frame_limit > 0 ? frame : m_run;
+            m_s[s] = m_run;
             l_s[s] = l_run;
         }
         if (status != ORACLE_OK)

@@ -59,6 +59,8 @@ def _load():
     L.sparse_mla_decode.restype = I32
     L.lse_merge.argtypes = [P, P, I32, I32, I32, I32, P, P, U32, P]
     L.lse_merge.restype = I32
+    L.smla_testing_set_merge_wait.argtypes = [I32, I32]
+    L.smla_testing_set_merge_wait.restype = I32
     _lib = L
     return L
 
@@ -103,6 +105,28 @@ def new_workspace(plan: Plan, T: int, H: int, device="cuda"):
     import torch
     n = workspace_size(plan, T, H)
     return torch.zeros(n, dtype=torch.uint8, device=device) if n else None
+
+
+def workspace_header_bytes(plan: Plan, T: int, H: int) -> int:
+    """Bytes at the start of a workspace that must be zero before a call: the status word and
+    the arrival counters, padded to 256 (the layout include/smla.h states)."""
+    groups = -(-((H + 31) // 32) // plan.tiles)
+    return (16 + T * groups * 2 * 4 + 255) // 256 * 256
+
+
+def workspace_status(workspace) -> int:
+    """The workspace's status word (split merges that gave up waiting); synchronizes."""
+    if workspace is None:
+        return 0
+    return int(workspace[:4].view(__import__("torch").int32).item())
+
+
+def testing_set_merge_wait(max_polls: int = 0, unreachable: bool = False) -> None:
+    """Test hook: bound (and optionally make unreachable) the split-merge wait of the 64-head
+    kernel; testing_set_merge_wait() restores the default."""
+    st = _load().smla_testing_set_merge_wait(int(max_polls), 1 if unreachable else 0)
+    if st != SMLA_OK:
+        raise SmlaError(st, "smla_testing_set_merge_wait")
 
 
 def make_plan(splits: int, tiles: int) -> Plan:

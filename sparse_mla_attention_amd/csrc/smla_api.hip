@@ -17,7 +17,11 @@ constexpr int kMaxSplits = 64;
 constexpr int kChunk = 64;
 constexpr int kDefaultMaxSplits = 4;
 constexpr int kFewChunks = 6;
+constexpr int32_t kDefaultWaitPolls = 1 << 24;
 std::atomic<int> g_cu_count[kMaxDevices];
+// bound of the 64-head kernel's split-merge wait, and the test hook that makes it unreachable
+std::atomic<int32_t> g_wait_polls{kDefaultWaitPolls};
+std::atomic<int32_t> g_wait_extra{0};
 
 // Compute units of the current device, queried once per device.
 hipError_t current_cu_count(int *cus)
@@ -88,13 +92,13 @@ bool plan_ok(const smla_plan *p, int32_t H)
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Workspace layout under a valid plan: counters [T, groups, 2] int32 (arrival ticket and
-// ready count, zero between calls), then partials: one block of 32 tiles x 512 FP16 values per
-// (token, head group, range), each range's output normalized by its own sum, in the order the
-// kernel's accumulator registers are stored (16-byte runs per lane), then (frame, sum)
-// [T, groups, splits, 32 tiles heads, 2].
+// Workspace layout under a valid plan: a status word (int32: split merges that gave up
+// waiting), counters [T, groups, 2] int32 from byte 16 (arrival ticket and ready count, zero
+// between calls), padded to 256 bytes; then FP32 partials: one block of 32 tiles x 512 floats per
+// (token, head group, range), in the order the kernel's accumulator registers are stored (16-byte
+// runs per lane); then (frame, sum) [T, groups, splits, 32 tiles heads, 2].
 struct WsLayout {
-    size_t counters, partials, ml, total;
+    size_t status, counters, partials, ml, total;
 };
 
 WsLayout ws_layout(const smla_plan *plan, int32_t T, int32_t H)
@@ -103,9 +107,10 @@ WsLayout ws_layout(const smla_plan *plan, int32_t T, int32_t H)
     const size_t hg = 32 * (size_t)plan->tiles;
     const size_t units = (size_t)T * groups * (size_t)plan->splits;
     WsLayout w;
-    w.counters = 0;
-    w.partials = align256((size_t)T * groups * 2 * sizeof(int32_t));
-    w.ml = w.partials + units * hg * 512 * sizeof(uint16_t);
+    w.status = 0;
+    w.counters = 16;
+    w.partials = align256(w.counters + (size_t)T * groups * 2 * sizeof(int32_t));
+    w.ml = w.partials + units * hg * 512 * sizeof(float);
     w.total = w.ml + units * hg * 2 * sizeof(float);
     return w;
 }
@@ -242,16 +247,29 @@ smla_status sparse_mla_decode(const void *q, int64_t q_stride_t, int64_t q_strid
     p.ws_o = nullptr;
     p.ws_ml = nullptr;
     p.counters = nullptr;
+    p.status = nullptr;
+    p.wait_polls = g_wait_polls.load(std::memory_order_relaxed);
+    p.wait_extra = g_wait_extra.load(std::memory_order_relaxed);
     if (need > 0) {
         const WsLayout w = ws_layout(&chosen, T, H);
         uint8_t *base = static_cast<uint8_t *>(workspace);
+        p.status = reinterpret_cast<int32_t *>(base + w.status);
         p.counters = reinterpret_cast<int32_t *>(base + w.counters);
-        p.ws_o = reinterpret_cast<uint16_t *>(base + w.partials);
+        p.ws_o = reinterpret_cast<float *>(base + w.partials);
         p.ws_ml = reinterpret_cast<float *>(base + w.ml);
     }
     const hipError_t e = smla::launch_decode(p, chosen.tiles, row_bytes, qk_dim,
                                              (flags & SMLA_P_ONE_TERM) == 0, stream);
     return e == hipSuccess ? SMLA_OK : SMLA_EHIP;
+}
+
+smla_status smla_testing_set_merge_wait(int32_t max_polls, int32_t unreachable)
+{
+    if (max_polls < 0 || (unreachable != 0 && unreachable != 1))
+        return SMLA_EINVAL;
+    g_wait_polls.store(max_polls == 0 ? kDefaultWaitPolls : max_polls, std::memory_order_relaxed);
+    g_wait_extra.store(unreachable, std::memory_order_relaxed);
+    return SMLA_OK;
 }
 
 smla_status lse_merge(const void *partials, const float *lse2, int32_t S, int32_t T, int32_t H,

@@ -28,15 +28,12 @@
 //     lane order, with this wave's 16-key maximum per head.
 //   P.V waves (4..7): wave 4 + j owns latent columns 128 j .. 128 j + 127 and, for the
 //     softmax, the keys 16 j .. 16 j + 15 of every chunk (the same lanes as the QK wave that
-//     computed their scores).  Softmax: chunk maximum over the four key quarters, running
-//     maximum m.  P is anchored at F = G + e, e = ceil(m - G) (G: the running maximum after the
-//     first chunk that has one): P = 2^(s2 - F + log2 448) <= 448, rounded to E4M3 by
-//     v_cvt_pk_fp8_f32 (two-term default: P = hi + lo/16, lo = E4M3(16 (P - hi))).  The
-//     accumulators stay in frame G and the chunk enters with weight 2^e through the P.V
-//     instruction's per-lane E8M0 B scale, so they are never rescaled; a head whose offset
-//     would exceed FRAME_LIMIT makes the workgroup compute its range again with that head's G
-//     preset to its maximum.  FP32 sums of the unquantized P are kept per lane in frame F.
-//     P.V: O^T (32 columns x 32 heads) += V^T (32 columns x 64 keys, ds_read_b64_tr_b8 from
+//     computed their scores).  Softmax (the attn_sparse page's recipe): chunk maximum over the
+//     four key quarters, running maximum m, alpha = 2^(m_old - m); P = 2^(s2 - m + log2 448)
+//     <= 448, rounded to E4M3 by v_cvt_pk_fp8_f32 (two-term default: P = hi + lo/16, lo =
+//     E4M3(16 (P - hi))); FP32 sums of the unquantized P kept per lane, rescaled by alpha.
+//     P.V: O^T *= alpha (per head), then
+//     O^T (32 columns x 32 heads) += V^T (32 columns x 64 keys, ds_read_b64_tr_b8 from
 //     the slot) P^T (64 keys x 32 heads, from the P buffer) on
 //     v_mfma_scale_f32_32x32x64_f8f6f4, 4 tiles per chunk (8 instructions with two-term P).
 //     One of these waves also loads the row indices, eight chunks at a time and at least
@@ -47,10 +44,10 @@
 //   chunks c-1 .. c+1.
 //
 // Epilogue: one range (S = 1): merge with the sink, BF16 output through an LDS tile (coalesced
-// row stores) and the LSE.  S > 1: every range writes its partial (its output normalized by its
-// own sum, in FP16 and register order, so reads and writes coalesce) and (G, l); the last range
-// to finish (atomic ticket per token and head group) merges all partials in range order,
-// weights 2^(G_s - M) l_s, writes the output and resets the ticket.
+// row stores) and the LSE.  S > 1: every range writes its partial (its FP32 accumulators in
+// register order, so reads and writes coalesce) and (m, l); the last range to finish (atomic
+// ticket per token and head group) merges all partials in range order, weights 2^(m_s - M),
+// writes the output and resets the ticket.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -81,16 +78,16 @@ struct Lds {
     static constexpr int P = SC + 2 * 4 * 64 * 8 * 4;          // [2 buf][2 term][32][64]
     static constexpr int PTERM = HG * 64;
     static constexpr int PBUF = 2 * PTERM;
-    static constexpr int ESC = P + 2 * PBUF;                   // [2 buf][32] int: E8M0 byte
-    static constexpr int MX = ESC + 2 * HG * 4;                // [2 buf][32 heads][4 key quarters]
+    static constexpr int SCL = P + 2 * PBUF;                   // [2 buf][32] float: alpha
+    static constexpr int MX = SCL + 2 * HG * 4;                // [2 buf][32 heads][4 key quarters]
     static constexpr int FIN = MX + 2 * HG * 4 * 4;            // [4 key quarters][32] l, [32] G, e
     static constexpr int IDX = FIN + 6 * HG * 4;               // [16 chunks][64] int indices
     static constexpr int QR = IDX + IRING * CHUNK * 4;         // [4 QK waves][32][64] q rope
-    static constexpr int MISC = QR + 4 * HG * 64;              // ticket, overflow flag
+    static constexpr int MISC = QR + 4 * HG * 64;              // ticket
     static constexpr int TOTAL = MISC + 16;
     static constexpr int OUT_TILE = HG * 1024;                 // BF16 [32][512], after the loop
     static_assert(OUT_TILE <= P, "output tile must fit in the V slots");
-    static_assert(OUT_TILE + 64 * HG * 8 <= SC, "(G, l) of 64 ranges must fit past the tile");
+    static_assert(OUT_TILE + 64 * HG * 8 <= SC, "(m, l) of 64 ranges must fit past the tile");
     static_assert(TOTAL <= 160 * 1024, "LDS budget");
 };
 
@@ -125,10 +122,7 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(DecodeParams a)
     const int nch = (mine + CHUNK - 1) / CHUNK;
     const int32_t *idx_row = a.indices + (int64_t)t * a.W;
 
-    int *flag = reinterpret_cast<int *>(lds + L::MISC) + 1;
-    float *fin = reinterpret_cast<float *>(lds + L::FIN);  // [4][32] l, [32] G, [32] e (int)
-    if (tid == 0)
-        *flag = 0;
+    float *fin = reinterpret_cast<float *>(lds + L::FIN);  // [4][32] l, [32] m
 
     // ---- epilogue (every wave; `acc` holds the P.V waves' accumulators) ---------------------
     // acc[ct]: O^T tile of columns 32 (4 w + ct) + .. x 32 heads; lane l holds head l % 32,
@@ -136,31 +130,28 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(DecodeParams a)
     auto epilogue = [&](v16f(&acc)[NCT]) __attribute__((always_inline)) {
         lds_barrier();
         const int hl = lane & 31, u = lane >> 5;
-        // head hl of this lane: frame G and the sum l in frame G
+        // head hl of this lane: the running maximum m (g_h) and the sum l at 448 of it
         float g_h = fin[4 * HG + hl];
-        float l_h = ldexpf(fin[hl] + fin[HG + hl] + fin[2 * HG + hl] + fin[3 * HG + hl],
-                           reinterpret_cast<const int *>(fin)[5 * HG + hl]);
+        float l_h = ((fin[hl] + fin[HG + hl]) + fin[2 * HG + hl]) + fin[3 * HG + hl];
         const int head = hg * HG + hl;
         const int64_t tg = (int64_t)t * a.groups + hg;
         const int tile0 = NCT * w;
         if (a.splits > 1) {
-            // Split merge.  Every range writes its partial (its output normalized by its own sum,
-            // a weighted mean of V rows bounded by the largest |V|, in FP16; then (G, l) per
-            // head) with device-scope (write-through) stores, waits for them to complete and
-            // only then takes an arrival ticket; the range holding the last ticket therefore
-            // sees every other partial complete and merges all of them in range order, its own
-            // from registers, rounded as it was stored (so the result does not depend on the
-            // arrival order).  (With few workgroups this beats taking the ticket first: the
+            // Split merge.  Every range writes its partial (FP32 accumulators as they stand, at
+            // 448 of the range's running maximum m; then (m, l) per head) with device-scope
+            // (write-through) stores, waits for them to complete and only then takes an arrival
+            // ticket; the range holding the last ticket therefore sees every other partial
+            // complete and merges all of them in range order, its own from registers (FP32 throughout, so the result does not depend on
+            // the arrival order).  (With few workgroups this beats taking the ticket first: the
             // stores of all ranges overlap instead of following the ticket round trip.)
-            // Partial layout: accumulator registers 8 j .. 8 j + 7 of tile `tile` at byte
-            // ((tile * 2 + j) * 64 + lane) * 16, one 16-byte access per lane.
+            // Partial layout: accumulator registers 4 j .. 4 j + 3 of tile `tile` at byte
+            // ((tile * 4 + j) * 64 + lane) * 16, one 16-byte access per lane.
             constexpr int SC1 = 16;  // cache policy of device-scope (write-through) accesses
-            auto part_off = [&](int ct, int j) { return (((tile0 + ct) * 2 + j) * 64 + lane) * 16; };
+            auto part_off = [&](int ct, int j) { return (((tile0 + ct) * 4 + j) * 64 + lane) * 16; };
             auto part_rsrc = [&](int64_t unit) {
                 return __builtin_amdgcn_make_buffer_rsrc(a.ws_o + unit * (HG * 512), 0,
-                                                         HG * 512 * 2, 0x00020000);
+                                                         HG * 512 * 4, 0x00020000);
             };
-            const float inv_l = l_h > 0.0f ? __builtin_amdgcn_rcpf(l_h) : 0.0f;
             int *ticket = reinterpret_cast<int *>(lds + L::MISC);
             int *ctr = a.counters + 2 * tg;         // [0] arrival ticket
             {
@@ -168,13 +159,14 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(DecodeParams a)
                 if (!s_wave) {
                     const auto rs = part_rsrc(ui);
 #pragma unroll
-                    for (int ct = 0; ct < NCT; ct++) {
-                        v4i pk[2];
-                        f16_pack(acc[ct], inv_l, pk);
+                    for (int ct = 0; ct < NCT; ct++)
 #pragma unroll
-                        for (int j = 0; j < 2; j++)
-                            __builtin_amdgcn_raw_buffer_store_b128(pk[j], rs, part_off(ct, j), 0, SC1);
-                    }
+                        for (int j = 0; j < 4; j++)
+                            __builtin_amdgcn_raw_buffer_store_b128(
+                                v4i{__float_as_int(acc[ct][4 * j]), __float_as_int(acc[ct][4 * j + 1]),
+                                    __float_as_int(acc[ct][4 * j + 2]),
+                                    __float_as_int(acc[ct][4 * j + 3])},
+                                rs, part_off(ct, j), 0, SC1);
                 }
                 if (wave == 4 && u == 0) {
                     store_device(a.ws_ml + (ui * HG + hl) * 2 + 0, g_h);
@@ -189,7 +181,7 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(DecodeParams a)
             __syncthreads();
             if (*ticket != a.splits - 1)
                 return;
-            // (G, l) of every range and head, staged in LDS in one round of loads (over the
+            // (m, l) of every range and head, staged in LDS in one round of loads (over the
             // V slots, past the output tile)
             float2 *gl = reinterpret_cast<float2 *>(lds + L::OUT_TILE);  // [splits][32]
             for (int i = tid; i < a.splits * HG; i += NT) {
@@ -216,32 +208,27 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(DecodeParams a)
                     sum[ct] = v16f{};
                 for (int s = 0; s < a.splits; s++) {
                     const float gs = s == split ? g_h : gl[s * HG + hl].x;
-                    const float ls = s == split ? l_h : gl[s * HG + hl].y;
-                    // the values are normalized: weight w l
-                    const float wgt = (gs == -INFINITY ? 0.0f : exp2f(gs - big_g)) * ls;
+                    const float wgt = gs == -INFINITY ? 0.0f : exp2f(gs - big_g);
                     if (s == split) {
-#pragma unroll
-                        for (int ct = 0; ct < NCT; ct++) {
-                            v4i own[2];
-                            f16_pack(acc[ct], inv_l, own);
-#pragma unroll
-                            for (int r = 0; r < 16; r++)
-                                sum[ct][r] += wgt * f16_unpack(own, r);
-                        }
-                    } else {
-                        const auto rs = part_rsrc(tg * a.splits + s);
-                        v4i v[NCT][2];
 #pragma unroll
                         for (int ct = 0; ct < NCT; ct++)
 #pragma unroll
-                            for (int j = 0; j < 2; j++)
+                            for (int r = 0; r < 16; r++)
+                                sum[ct][r] += wgt * acc[ct][r];
+                    } else {
+                        const auto rs = part_rsrc(tg * a.splits + s);
+                        v4i v[NCT][4];
+#pragma unroll
+                        for (int ct = 0; ct < NCT; ct++)
+#pragma unroll
+                            for (int j = 0; j < 4; j++)
                                 v[ct][j] = __builtin_amdgcn_raw_buffer_load_b128(
                                     rs, part_off(ct, j), 0, SC1);
 #pragma unroll
                         for (int ct = 0; ct < NCT; ct++)
 #pragma unroll
                             for (int r = 0; r < 16; r++)
-                                sum[ct][r] += wgt * f16_unpack(v[ct], r);
+                                sum[ct][r] += wgt * __int_as_float(v[ct][r >> 2][r & 3]);
                     }
                 }
 #pragma unroll
@@ -456,10 +443,6 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(DecodeParams a)
         };
 
         run_range();
-        lds_barrier();                              // the P.V waves decide on a second pass
-        lds_barrier();
-        if (*flag != 0)
-            run_range();
         v16f none[NCT];
 #pragma unroll
         for (int ct = 0; ct < NCT; ct++)
@@ -486,16 +469,13 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(DecodeParams a)
 
         // ---- softmax state: lane (nh, kq) owns heads nh and 16 + nh, keys 16 w + 4 kq + i --
         const int kq = lane >> 4, nh = lane & 15;
-        float m_run[2] = {-INFINITY, -INFINITY}, frame[2], l_lane[2];
-        int ecur[2];
-        bool preset[2] = {false, false};
-        bool ovf[2];                               // this head overflowed (first pass)
+        float m_run[2] = {-INFINITY, -INFINITY}, l_lane[2] = {0.0f, 0.0f};
 
-        // softmax of chunk x (branch-free): frame, P (to the chunk's P buffer) and E8M0 scales.
-        // First pass: G is the running maximum after the first chunk with an active column and
-        // e = ceil(m - G) >= 0; an offset beyond FRAME_LIMIT marks the head for the second
-        // pass, which fixes G at the head's final maximum before the range starts (e = ceil(m -
-        // G) <= 0, at least E_MIN), so no pass ever rescales the accumulators.
+        // softmax of chunk x (branch-free; the attn_sparse page's recipe): the chunk maximum over
+        // the four key quarters, the running maximum m, the rescale factor alpha = 2^(m_old - m)
+        // of everything accumulated so far (into LDS beside P, for the accumulators), and
+        // P = 2^(s2 - m + log2 448) <= 448 as E4M3 (two-term by default) into the chunk's P
+        // buffer; the sums of the unquantized P are rescaled and extended here.
         auto softmax = [&](int x) {
             const uint8_t *mxb = lds + L::MX + (x & 1) * HG * 16;
             const float *sc = reinterpret_cast<const float *>(lds + L::SC) +
@@ -509,25 +489,16 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(DecodeParams a)
                 const v4f m4 = lds_load<v4f>(mxb, head * 16);
                 const float m_chunk = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
                 const float m_new = fmaxf(m_run[ht], m_chunk);
-                const bool fresh = frame[ht] == -INFINITY;
-                const float diff = fresh || m_new == -INFINITY ? 0.0f : m_new - frame[ht];
-                int e = (int)ceilf(fmaxf(diff, (float)E_MIN));
-                ovf[ht] = ovf[ht] || e > FRAME_LIMIT;
-                e = min(e, FRAME_LIMIT);            // first pass after an overflow: unused
-                const int shift = fresh ? 0 : ecur[ht] - e;
-                frame[ht] = fresh ? m_new : frame[ht];
-                ecur[ht] = e;
+                const float alpha =
+                    m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run[ht] - m_new);
                 m_run[ht] = m_new;
-                const float fb =
-                    frame[ht] == -INFINITY ? 0.0f : (frame[ht] + (float)e) - LOG2_ANCHOR;
+                const float fb = m_new == -INFINITY ? 0.0f : m_new - LOG2_ANCHOR;
                 float p[4];
-                float lsum = 0.0f;
 #pragma unroll
-                for (int i = 0; i < 4; i++) {
+                for (int i = 0; i < 4; i++)
                     p[i] = __builtin_amdgcn_exp2f(sv[ht][i] - fb);  // exp2(-inf) = 0
-                    lsum += p[i];
-                }
-                l_lane[ht] = ldexpf(l_lane[ht], shift) + lsum;
+                const float lsum = ((p[0] + p[1]) + p[2]) + p[3];
+                l_lane[ht] = __builtin_fmaf(l_lane[ht], alpha, lsum);
                 int hi = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
                 hi = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], hi, true);
                 const int off = head * 64 + 16 * (w ^ psw(head)) + 4 * kq;
@@ -544,15 +515,16 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(DecodeParams a)
                     *reinterpret_cast<int *>(pbase + L::PTERM + off) = lo;
                 }
                 if (w == 0 && kq == ht)
-                    reinterpret_cast<int *>(lds + L::ESC)[(x & 1) * HG + head] = 127 + e;
+                    reinterpret_cast<float *>(lds + L::SCL)[(x & 1) * HG + head] = alpha;
             }
         };
 
-        // P.V of chunk x over this wave's 4 column tiles
+        // P.V of chunk x over this wave's 4 column tiles: the accumulators rescaled to the
+        // chunk's running maximum, then its products
         auto pv = [&](int x) {
             const uint8_t *vs = lds + L::V + vslot(x) * L::VSLOT;
             const uint8_t *pbuf = lds + L::P + (x & 1) * L::PBUF;
-            const int escw = reinterpret_cast<const int *>(lds + L::ESC)[(x & 1) * HG + hl];
+            const float alpha = reinterpret_cast<const float *>(lds + L::SCL)[(x & 1) * HG + hl];
             const v8i bh = join(lds_load<v4i>(pbuf, p_off0), lds_load<v4i>(pbuf, p_off1));
             v8i bl = bh;
             if constexpr (TWO)
@@ -570,14 +542,18 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(DecodeParams a)
                 return vt;
             };
             v8i vcur = read_vt(0);
+            mfma_result_pad();                     // the previous chunk's products have landed
+#pragma unroll
+            for (int ct = 0; ct < NCT; ct++)
+                acc[ct] *= alpha;
 #pragma unroll
             for (int ct = 0; ct < NCT; ct++) {
                 v8i vnext = vcur;
                 if (ct + 1 < NCT)
                     vnext = read_vt(ct + 1);  // next tile's V^T in flight during these products
-                acc[ct] = mfma32(vcur, bh, acc[ct], escw);
+                acc[ct] = mfma32(vcur, bh, acc[ct], 127);
                 if constexpr (TWO)
-                    acc[ct] = mfma32(vcur, bl, acc[ct], escw - 4);  // the second term's 2^-4
+                    acc[ct] = mfma32(vcur, bl, acc[ct], 127 - 4);  // the second term's 2^-4
                 vcur = vnext;
             }
         };
@@ -610,19 +586,11 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(DecodeParams a)
 
         auto run_range = [&]() __attribute__((always_inline)) {
 #pragma unroll
-            for (int ht = 0; ht < 2; ht++) {
-                frame[ht] = preset[ht] ? m_run[ht] : -INFINITY;
-                m_run[ht] = -INFINITY;
-                l_lane[ht] = 0.0f;
-                ecur[ht] = 0;
-                ovf[ht] = false;
-            }
-#pragma unroll
             for (int ct = 0; ct < NCT; ct++)
                 acc[ct] = v16f{};
             if (nch == 0)
                 return;
-            // chunk -1 (read by P.V in iteration 0): a zero V slot, zero P and a unit scale
+            // chunk -1 (read by P.V in iteration 0): a zero V slot, zero P and alpha 1
             {
                 const int ot = tid - 256;
                 uint8_t *z = lds + L::V + vslot(-1) * L::VSLOT;
@@ -631,7 +599,7 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(DecodeParams a)
                 for (int x = ot; x < L::PBUF / 16; x += 256)
                     *reinterpret_cast<v4i *>(lds + L::P + L::PBUF + 16 * x) = v4i{0, 0, 0, 0};
                 if (ot < HG)
-                    reinterpret_cast<int *>(lds + L::ESC)[HG + ot] = 127;
+                    reinterpret_cast<float *>(lds + L::SCL)[HG + ot] = 1.0f;
             }
             if (w == 0) {
 #pragma unroll
@@ -658,19 +626,9 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(DecodeParams a)
         };
 
         run_range();
-        // second pass for the heads whose offset overflowed (rare): restart the range with
-        // their frames fixed at their final maxima
-        lds_barrier();
-        if (__any(ovf[0] || ovf[1]) && lane == 0)
-            *flag = 1;
-        lds_barrier();
-        if (*flag != 0) {
-            preset[0] = ovf[0];
-            preset[1] = ovf[1];
-            run_range();
-        }
+        mfma_result_pad();                          // the last products have landed
 
-        // ---- per-head results: l (per wave), G and e ---------------------------------------
+        // ---- per-head results: l (per wave) and the running maximum --------------------------
 #pragma unroll
         for (int ht = 0; ht < 2; ht++) {
             float lt = l_lane[ht];
@@ -679,10 +637,8 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(DecodeParams a)
             const int head = 16 * ht + nh;
             if (kq == ht) {
                 fin[w * HG + head] = lt;
-                if (w == 0) {
-                    fin[4 * HG + head] = frame[ht];
-                    reinterpret_cast<int *>(fin)[5 * HG + head] = ecur[ht];
-                }
+                if (w == 0)
+                    fin[4 * HG + head] = m_run[ht];
             }
         }
         epilogue(acc);

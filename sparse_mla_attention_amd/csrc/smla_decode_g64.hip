@@ -5,10 +5,10 @@
 // computes"; the E4M3-P recipe, the contiguous key split and the split merge are the
 // attn_sparse page's module docstring and its SparseDcpDecode.kernel / merge methods.  The
 // arithmetic is that of the 32-head kernel (smla_decode.hip), operation for operation: the
-// same QK instruction chains, the same integer-offset softmax frames, E4M3 P (two-term by
-// default) at the 448 anchor, the same E8M0 chunk weights on the P.V instruction, the same
-// order of the FP32 sums of the unquantized P and the same fused split merge, so under one
-// split plan the two kernels agree bit for bit.
+// same QK instruction chains, the same running maxima and rescale factors, E4M3 P (two-term
+// by default) at 448 of the running maximum, the same accumulator rescales, the same order of
+// the FP32 sums of the unquantized P and the same fused split merge, so under one split plan
+// the two kernels agree bit for bit.
 //
 // Why this decomposition.  The 32-head kernel pays a chunk's fixed costs (row-load issue,
 // index reads, score exchange, barriers) once per 32 heads, and its scattered row loads into
@@ -20,10 +20,11 @@
 //   QK waves (0..3): wave w takes head tile w (16 heads) over all 64 keys of a chunk:
 //     S^T tiles of 16 keys x 16 heads on v_mfma_scale_f32_16x16x128_f8f6f4 (K read from the
 //     slot, Q fragments held in registers, the rope step on two 16x16x32 FP8 instructions),
-//     then the softmax of its heads over the whole chunk (no exchange of maxima): integer-
-//     offset frames, E4M3 P (two-term by default) and the E8M0 scale into a P buffer.
+//     then the softmax of its heads over the whole chunk (no exchange of maxima): running
+//     maximum, rescale factor, E4M3 P (two-term by default) and the factor into a P buffer.
 //   P.V waves (4..7): wave 4 + j owns output columns 128 j .. 128 j + 127 of all 64 heads:
-//     O^T (32 columns x 32 heads) += V^T (ds_read_b64_tr_b8 from the slot) P^T on
+//     O^T *= alpha (per head), then O^T (32 columns x 32 heads) += V^T (ds_read_b64_tr_b8 from
+//     the slot) P^T on
 //     v_mfma_scale_f32_32x32x64_f8f6f4, 4 column tiles x 2 head tiles (x 2 with two-term P).
 //     It also gathers its own column slice of every chunk (and a quarter of the rope rows).
 // Slot (one gathered chunk): four slices of 8 KB, slice j holding latent pieces 8 j .. 8 j + 7
@@ -72,10 +73,10 @@ struct LdsG {
     static constexpr int P = SLOTS * SLOTB;                    // [2 buf][2 term][64][64 keys]
     static constexpr int PTERM = HG * 64;
     static constexpr int PBUF = 2 * PTERM;
-    static constexpr int ESC = P + 2 * PBUF;                   // [2 buf][64] int: E8M0 byte
-    static constexpr int FIN = ESC + 2 * HG * 4;               // [4 key quarters][64] l, G, e
+    static constexpr int SCL = P + 2 * PBUF;                   // [2 buf][64] float: alpha
+    static constexpr int FIN = SCL + 2 * HG * 4;               // [4 key quarters][64] l, [64] m
     static constexpr int ADDR = FIN + 6 * HG * 4;              // [G64_MAX_RANGE] row addresses
-    static constexpr int MISC = ADDR + G64_MAX_RANGE * 8;      // ticket, overflow flag
+    static constexpr int MISC = ADDR + G64_MAX_RANGE * 8;      // ticket, spare, wait outcome
     static constexpr int TOTAL = MISC + 16;
     static constexpr int OUT_TILE = HG * 1024;                 // BF16 [64][512], after the loop
     static_assert(OUT_TILE <= P, "output tile must fit in the slots");
@@ -143,9 +144,8 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
 
 
     const uint64_t *addr = reinterpret_cast<const uint64_t *>(lds + L::ADDR);
-    int *flag = reinterpret_cast<int *>(lds + L::MISC) + 1;
-    float *fin = reinterpret_cast<float *>(lds + L::FIN);  // [4][64] l, [64] G, [64] e (int)
-    int *esc = reinterpret_cast<int *>(lds + L::ESC);
+    float *fin = reinterpret_cast<float *>(lds + L::FIN);  // [4][64] l, [64] m
+    float *scl = reinterpret_cast<float *>(lds + L::SCL);  // [2][64] alpha per chunk
     const uint64_t zero = (uint64_t)(uintptr_t)g_zero_row_g64;
 
     // ---- source address of every column of the range: its row, or the zero row when the
@@ -165,8 +165,6 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
             ad[i] = src;
         }
     }
-    if (tid == 0)
-        *flag = 0;
     __syncthreads();                               // the only full fence before the loop
 
     // ---- epilogue (every wave; `acc` holds the P.V waves' accumulators) ---------------------
@@ -180,55 +178,54 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
         for (int h2 = 0; h2 < 2; h2++) {
             const int head = 32 * h2 + hl;
             g_h[h2] = fin[4 * HG + head];
-            l_h[h2] = ldexpf(fin[head] + fin[HG + head] + fin[2 * HG + head] + fin[3 * HG + head],
-                             reinterpret_cast<const int *>(fin)[5 * HG + head]);
+            l_h[h2] = ((fin[head] + fin[HG + head]) + fin[2 * HG + head]) + fin[3 * HG + head];
         }
         const int64_t tg = (int64_t)t * a.groups + hg;
-        // A range's partial is its output normalized by its own sum (a weighted mean of V
-        // rows, so bounded by the largest |V|), in FP16.  Byte offset of accumulator registers
-        // 8 j .. 8 j + 7 of tile (ct, h2): 16 bytes per lane, one 1 KB run per (tile, j) across
-        // the wave, so every store and load of the exchange is one 16-byte access per lane.
+        // A range's partial: its FP32 accumulators as they stand (at 448 of the range's running
+        // maximum m, not normalized) and (m, l) per head (g_h holds m).  Byte offset of accumulator registers 4 j .. 4 j + 3 of tile
+        // (ct, h2): 16 bytes per lane, one 1 KB run per (tile, j) across the wave, so every store
+        // and load of the exchange is one 16-byte access per lane.
         auto part_off = [&](int ct, int h2, int j) {
-            return ((((NCT * w + ct) * 2 + h2) * 2 + j) * 64 + lane) * 16;
+            return ((((NCT * w + ct) * 2 + h2) * 4 + j) * 64 + lane) * 16;
         };
         constexpr int SC1 = 16;  // cache policy of device-scope (write-through) accesses
         auto part_rsrc = [&](int64_t unit) {
-            return __builtin_amdgcn_make_buffer_rsrc(a.ws_o + unit * (HG * 512), 0, HG * 512 * 2,
+            return __builtin_amdgcn_make_buffer_rsrc(a.ws_o + unit * (HG * 512), 0, HG * 512 * 4,
                                                      0x00020000);
         };
+        bool failed = false;
         if (a.splits > 1) {
             // Split merge.  Each range takes an arrival ticket first.  Every range but the last
-            // writes its partial (normalized FP16 in register order, then (G, l) per head)
+            // writes its partial (FP32 accumulators in register order, then (m, l) per head)
             // with device-scope (write-through) stores, waits for them to complete and bumps
             // the ready count; the last range waits until the ready count shows every other
             // partial, then merges all of them in range order, its own from registers.  The
             // writers are running when the last range waits (they hold earlier tickets and
-            // wait on nothing), so the wait ends; it is also bounded.
-            int *ticket = reinterpret_cast<int *>(lds + L::MISC);
+            // wait on nothing), so the wait ends; it is also bounded: a range that gives up
+            // counts itself in the workspace's status word, writes NaN for its heads and
+            // leaves the counters as they are.
+            int *misc = reinterpret_cast<int *>(lds + L::MISC);  // ticket, spare, wait outcome
             int *ctr = a.counters + 2 * tg;         // [0] arrival ticket, [1] ready count
             if (tid == 0)
-                *ticket = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED,
+                misc[0] = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED,
                                                  __HIP_MEMORY_SCOPE_AGENT);
             __syncthreads();
-            if (*ticket != a.splits - 1) {
+            if (misc[0] != a.splits - 1) {
                 const int64_t ui = tg * a.splits + split;
                 if (!qk_wave) {
                     const auto rs = part_rsrc(ui);
-                    float inv_l[2];
-#pragma unroll
-                    for (int h2 = 0; h2 < 2; h2++)
-                        inv_l[h2] = l_h[h2] > 0.0f ? __builtin_amdgcn_rcpf(l_h[h2]) : 0.0f;
 #pragma unroll
                     for (int ct = 0; ct < NCT; ct++)
 #pragma unroll
-                        for (int h2 = 0; h2 < 2; h2++) {
-                            v4i pk[2];
-                            f16_pack(acc[ct][h2], inv_l[h2], pk);
+                        for (int h2 = 0; h2 < 2; h2++)
 #pragma unroll
-                            for (int j = 0; j < 2; j++)
-                                __builtin_amdgcn_raw_buffer_store_b128(pk[j], rs,
-                                                                       part_off(ct, h2, j), 0, SC1);
-                        }
+                            for (int j = 0; j < 4; j++)
+                                __builtin_amdgcn_raw_buffer_store_b128(
+                                    v4i{__float_as_int(acc[ct][h2][4 * j]),
+                                        __float_as_int(acc[ct][h2][4 * j + 1]),
+                                        __float_as_int(acc[ct][h2][4 * j + 2]),
+                                        __float_as_int(acc[ct][h2][4 * j + 3])},
+                                    rs, part_off(ct, h2, j), 0, SC1);
                 }
                 if (wave == 4 && u == 0) {
 #pragma unroll
@@ -244,46 +241,48 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
                 return;
             }
             if (tid == 0) {
-                for (int spin = 0; spin < (1 << 24); spin++) {
+                const int need = a.splits - 1 + a.wait_extra;
+                int ready = 0;
+                for (int spin = 0;; spin++) {
                     if (__hip_atomic_load(ctr + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >=
-                        a.splits - 1)
+                        need) {
+                        ready = 1;
+                        break;
+                    }
+                    if (spin >= a.wait_polls)
                         break;
                     __builtin_amdgcn_s_sleep(1);
                 }
+                misc[2] = ready;
+                if (!ready)
+                    __hip_atomic_fetch_add(a.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
             __syncthreads();
-            // Merge in range order, own partial from registers, the others' from the workspace.
-            // The own partial is normalized and rounded to FP16 exactly as a writer stores it, so
-            // the result does not depend on which range arrived last.
-            float own_g[2], own_l[2], own_inv[2];
+            // A range that gave up writes NaN rows and LSEs (final part); what it merges then is
+            // never used, and every workspace address it reads is in bounds either way.
+            failed = misc[2] == 0;
+            // Merge in range order, own partial from registers, the others' from the workspace
+            // (FP32 throughout: the result does not depend on which range arrived last).
+            float own_g[2], own_l[2];
 #pragma unroll
             for (int h2 = 0; h2 < 2; h2++) {
                 own_g[h2] = g_h[h2];
                 own_l[h2] = l_h[h2];
-                own_inv[h2] = l_h[h2] > 0.0f ? __builtin_amdgcn_rcpf(l_h[h2]) : 0.0f;
-            }
-            v4i own[NCT][2][2];  // the own partial as it would have been stored
-            if (!qk_wave) {
-#pragma unroll
-                for (int ct = 0; ct < NCT; ct++)
-#pragma unroll
-                    for (int h2 = 0; h2 < 2; h2++)
-                        f16_pack(acc[ct][h2], own_inv[h2], own[ct][h2]);
             }
             if (a.splits == 2) {
-                // Two ranges: the other range's (G, l) and its first column tile come in one
+                // Two ranges: the other range's (m, l) and its first column tile come in one
                 // round trip, and each column tile's loads go out before the previous one is
                 // summed.
                 const int other = 1 - split;
                 const int64_t uo = tg * 2 + other;
                 float og[2], ol[2];
-                v4i cur[2][2], nxt[2][2];
+                v4i cur[2][4], nxt[2][4];
                 if (!qk_wave) {
                     const auto rs = part_rsrc(uo);
 #pragma unroll
                     for (int h2 = 0; h2 < 2; h2++)
 #pragma unroll
-                        for (int j = 0; j < 2; j++)
+                        for (int j = 0; j < 4; j++)
                             cur[h2][j] = __builtin_amdgcn_raw_buffer_load_b128(
                                 rs, part_off(0, h2, j), 0, SC1);
                 }
@@ -293,7 +292,7 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
                     og[h2] = load_device(a.ws_ml + m);
                     ol[h2] = load_device(a.ws_ml + m + 1);
                 }
-                float c_s[2][2];  // [range][h2]: weight of the range's values in the merged sum
+                float w_s[2][2];  // [range][h2]: weight 2^(m_s - M) of the range's accumulators
 #pragma unroll
                 for (int h2 = 0; h2 < 2; h2++) {
                     const float gr[2] = {split == 0 ? own_g[h2] : og[h2],
@@ -304,9 +303,8 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
                     l_h[h2] = 0.0f;
 #pragma unroll
                     for (int r = 0; r < 2; r++) {
-                        const float w_r = gr[r] == -INFINITY ? 0.0f : exp2f(gr[r] - g_h[h2]);
-                        l_h[h2] += w_r * lr[r];
-                        c_s[r][h2] = w_r * lr[r];  // both ranges' values are normalized
+                        w_s[r][h2] = gr[r] == -INFINITY ? 0.0f : exp2f(gr[r] - g_h[h2]);
+                        l_h[h2] += w_s[r][h2] * lr[r];
                     }
                 }
                 if (!qk_wave) {
@@ -317,7 +315,7 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
 #pragma unroll
                             for (int h2 = 0; h2 < 2; h2++)
 #pragma unroll
-                                for (int j = 0; j < 2; j++)
+                                for (int j = 0; j < 4; j++)
                                     nxt[h2][j] = __builtin_amdgcn_raw_buffer_load_b128(
                                         rs, part_off(ct + 1, h2, j), 0, SC1);
                         }
@@ -325,13 +323,13 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
                         for (int h2 = 0; h2 < 2; h2++) {
 #pragma unroll
                             for (int rr = 0; rr < 16; rr++) {
-                                const float xo = f16_unpack(cur[h2], rr);
-                                const float xs = f16_unpack(own[ct][h2], rr);
+                                const float xo = __int_as_float(cur[h2][rr >> 2][rr & 3]);
+                                const float xs = acc[ct][h2][rr];
                                 const float x0 = split == 0 ? xs : xo;
                                 const float x1 = split == 1 ? xs : xo;
                                 float sum = 0.0f;
-                                sum += c_s[0][h2] * x0;
-                                sum += c_s[1][h2] * x1;
+                                sum += w_s[0][h2] * x0;
+                                sum += w_s[1][h2] * x1;
                                 acc[ct][h2][rr] = sum;
                             }
                         }
@@ -339,7 +337,7 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
 #pragma unroll
                             for (int h2 = 0; h2 < 2; h2++)
 #pragma unroll
-                                for (int j = 0; j < 2; j++)
+                                for (int j = 0; j < 4; j++)
                                     cur[h2][j] = nxt[h2][j];
                         }
                     }
@@ -373,34 +371,34 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
                         v16f sum[2] = {v16f{}, v16f{}};
                         for (int s = 0; s < a.splits; s++) {
                             const int64_t us = tg * a.splits + s;
-                            float w_s[2];  // every range's values are normalized: weight w l
+                            float w_s[2];
 #pragma unroll
                             for (int h2 = 0; h2 < 2; h2++) {
-                                const int64_t m = (us * HG + 32 * h2 + hl) * 2;
-                                const float gs = s == split ? own_g[h2] : load_device(a.ws_ml + m);
-                                const float ls = s == split ? own_l[h2] : load_device(a.ws_ml + m + 1);
-                                w_s[h2] = (gs == -INFINITY ? 0.0f : exp2f(gs - g_h[h2])) * ls;
+                                const float gs =
+                                    s == split ? own_g[h2]
+                                               : load_device(a.ws_ml + (us * HG + 32 * h2 + hl) * 2);
+                                w_s[h2] = gs == -INFINITY ? 0.0f : exp2f(gs - g_h[h2]);
                             }
                             if (s == split) {
 #pragma unroll
                                 for (int h2 = 0; h2 < 2; h2++)
 #pragma unroll
                                     for (int rr = 0; rr < 16; rr++)
-                                        sum[h2][rr] += w_s[h2] * f16_unpack(own[ct][h2], rr);
+                                        sum[h2][rr] += w_s[h2] * acc[ct][h2][rr];
                             } else {
                                 const auto rs = part_rsrc(us);
-                                v4i v[2][2];
+                                v4i v[2][4];
 #pragma unroll
                                 for (int h2 = 0; h2 < 2; h2++)
 #pragma unroll
-                                    for (int j = 0; j < 2; j++)
+                                    for (int j = 0; j < 4; j++)
                                         v[h2][j] = __builtin_amdgcn_raw_buffer_load_b128(
                                             rs, part_off(ct, h2, j), 0, SC1);
 #pragma unroll
                                 for (int h2 = 0; h2 < 2; h2++)
 #pragma unroll
                                     for (int rr = 0; rr < 16; rr++)
-                                        sum[h2][rr] += w_s[h2] * f16_unpack(v[h2], rr);
+                                        sum[h2][rr] += w_s[h2] * __int_as_float(v[h2][rr >> 2][rr & 3]);
                             }
                         }
                         acc[ct][0] = sum[0];
@@ -408,7 +406,8 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
                     }
                 }
             }
-            if (tid == 0) {  // every range has arrived and been merged: ready for the next call
+            if (tid == 0 && !failed) {  // every range has arrived and been merged: ready for
+                                        // the next call
                 __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 __hip_atomic_store(ctr + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
@@ -427,7 +426,7 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
                 wgt = any ? exp2f(g_h[h2] - big_m) : 0.0f;
                 big_l = wgt * l_h[h2] + ANCHOR * exp2f(sk - big_m);
             }
-            const float inv = any ? a.bmm2 * wgt / big_l : 0.0f;
+            const float inv = failed ? __int_as_float(0x7FC00000) : any ? a.bmm2 * wgt / big_l : 0.0f;
             if (!qk_wave) {
 #pragma unroll
                 for (int ct = 0; ct < NCT; ct++) {
@@ -442,7 +441,9 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
                 }
             }
             if (wave == 4 && u == 0 && head < a.H && a.lse != nullptr) {
-                const float lse2 = any ? big_m - LOG2_ANCHOR + log2f(big_l) : -INFINITY;
+                const float lse2 = failed ? __int_as_float(0x7FC00000)
+                                   : any  ? big_m - LOG2_ANCHOR + log2f(big_l)
+                                          : -INFINITY;
                 a.lse[(int64_t)t * a.H + head] = a.lse_log2 ? lse2 : lse2 * LN2;
             }
         }
@@ -489,16 +490,14 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
         for (int kt = 0; kt < 4; kt++)
             pw[kt] = head * 64 + 16 * (kt ^ psw(head)) + 4 * g;
 
-        float m_run = -INFINITY, frame = -INFINITY, l_lane[4];
-        int ecur = 0;
-        bool preset = false, ovf = false;
+        float m_run = -INFINITY, l_lane[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 
-        // QK and softmax of chunk x: scores of this lane's head (keys 16 kt + 4 g + i), the
-        // chunk maximum over all 64 keys, then frame, P and the E8M0 scale.  First pass: G is
-        // the running maximum after the first chunk with an active column and e = ceil(m - G)
-        // >= 0; an offset beyond FRAME_LIMIT marks the head for the second pass, which fixes G
-        // at the head's final maximum before the range starts (e = ceil(m - G) <= 0, at least
-        // E_MIN), so no pass ever rescales the accumulators.
+        // QK and softmax of chunk x (the attn_sparse page's recipe): scores of this lane's head
+        // (keys 16 kt + 4 g + i), the chunk maximum over all 64 keys, the running maximum m, the
+        // rescale factor alpha = 2^(m_old - m) of everything accumulated so far, P = 2^(s2 - m +
+        // log2 448) <= 448 as E4M3 (two-term by default) into the P buffer and alpha beside it;
+        // the sums of the unquantized P are rescaled and extended here, the P.V waves rescale
+        // their accumulators by alpha before adding the chunk.
         auto qk_softmax = [&](int x) {
             // the K reads and products of the QK waves go ahead of the P.V waves' work on
             // the same SIMD; the softmax then runs at normal priority
@@ -570,16 +569,11 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
                 mx = fmaxf(__uint_as_float(p32[0]), __uint_as_float(p32[1]));
             }
             const float m_new = fmaxf(m_run, mx);
-            const bool fresh = frame == -INFINITY;
-            const float diff = fresh || m_new == -INFINITY ? 0.0f : m_new - frame;
-            int e = (int)ceilf(fmaxf(diff, (float)E_MIN));
-            ovf = ovf || e > FRAME_LIMIT;
-            e = min(e, FRAME_LIMIT);                // first pass after an overflow: unused
-            const int shift = fresh ? 0 : ecur - e;
-            frame = fresh ? m_new : frame;
-            ecur = e;
+            // alpha = 1 while the range has no active column yet (m_new = -inf), 0 on the first
+            // chunk that has one (nothing accumulated)
+            const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
             m_run = m_new;
-            const float fb = frame == -INFINITY ? 0.0f : (frame + (float)e) - LOG2_ANCHOR;
+            const float fb = m_new == -INFINITY ? 0.0f : m_new - LOG2_ANCHOR;
             uint8_t *pbase = lds + L::P + (x & 1) * L::PBUF;
 #pragma unroll
             for (int kt = 0; kt < 4; kt++) {
@@ -588,7 +582,7 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
                 for (int i = 0; i < 4; i++)
                     p[i] = __builtin_amdgcn_exp2f(sc[kt][i] - fb);  // exp2(-inf) = 0
                 const float lsum = ((p[0] + p[1]) + p[2]) + p[3];
-                l_lane[kt] = ldexpf(l_lane[kt], shift) + lsum;
+                l_lane[kt] = __builtin_fmaf(l_lane[kt], alpha, lsum);
                 int hi = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
                 hi = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], hi, true);
                 *reinterpret_cast<int *>(pbase + pw[kt]) = hi;
@@ -603,38 +597,19 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
                 }
             }
             if (g == 0)
-                esc[(x & 1) * HG + head] = 127 + e;
+                scl[(x & 1) * HG + head] = alpha;
         };
 
-        auto run_range = [&]() __attribute__((always_inline)) {
-            frame = preset ? m_run : -INFINITY;
-            m_run = -INFINITY;
-#pragma unroll
-            for (int kt = 0; kt < 4; kt++)
-                l_lane[kt] = 0.0f;
-            ecur = 0;
-            ovf = false;
-            if (nch == 0)
-                return;
+        if (nch > 0) {
             lds_barrier();                          // the P.V waves issue chunks 0 and 1
             for (int c = 0; c <= nch; c++) {
                 lds_barrier();                      // chunk c landed; P buffer c & 1 free
                 if (c < nch)
                     qk_softmax(c);
             }
-        };
-
-        run_range();
-        lds_barrier();                              // second pass for overflowed heads?
-        if (__any(ovf) && lane == 0)
-            *flag = 1;
-        lds_barrier();
-        if (*flag != 0) {
-            preset = ovf;
-            run_range();
         }
 
-        // ---- per-head results: l per key quarter, G and e -----------------------------------
+        // ---- per-head results: l per key quarter and the running maximum ------------------------
 #pragma unroll
         for (int kt = 0; kt < 4; kt++) {
             float lt = l_lane[kt];
@@ -642,10 +617,8 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
             lt += __shfl_xor(lt, 32);
             if (g == 0) {
                 fin[kt * HG + head] = lt;
-                if (kt == 0) {
-                    fin[4 * HG + head] = frame;
-                    reinterpret_cast<int *>(fin)[5 * HG + head] = ecur;
-                }
+                if (kt == 0)
+                    fin[4 * HG + head] = m_run;
             }
         }
         v16f none[NCT][2];
@@ -709,14 +682,14 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
         struct Frags {
             v8i vt[NCT];
             v8i bh[2], bl[2];
-            int escw[2];
+            float alpha[2];
         };
         auto pv_read = [&](int x, Frags &f) {
             const uint8_t *vs = lds + (x % SLOTS) * L::SLOTB;
             const uint8_t *pbuf = lds + L::P + (x & 1) * L::PBUF;
 #pragma unroll
             for (int h2 = 0; h2 < 2; h2++) {
-                f.escw[h2] = esc[(x & 1) * HG + 32 * h2 + hl];
+                f.alpha[h2] = scl[(x & 1) * HG + 32 * h2 + hl];
                 f.bh[h2] = join(lds_load<v4i>(pbuf + 2048 * h2, p_rd0),
                                 lds_load<v4i>(pbuf + 2048 * h2, p_rd1));
                 f.bl[h2] = f.bh[h2];
@@ -735,29 +708,33 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
                 }
             }
         };
+        // the accumulators rescaled to the chunk's running maximum, then its products
         auto pv_mma = [&](const Frags &f) {
-#pragma unroll
-            for (int ct = 0; ct < NCT; ct++) {
-#pragma unroll
-                for (int h2 = 0; h2 < 2; h2++) {
-                    acc[ct][h2] = mfma32(f.vt[ct], f.bh[h2], acc[ct][h2], f.escw[h2]);
-                    if constexpr (TWO)  // the second term's 2^-4
-                        acc[ct][h2] = mfma32(f.vt[ct], f.bl[h2], acc[ct][h2], f.escw[h2] - 4);
-                }
-            }
-        };
-
-        auto run_range = [&]() __attribute__((always_inline)) {
+            mfma_result_pad();                     // the previous chunk's products have landed
 #pragma unroll
             for (int ct = 0; ct < NCT; ct++)
 #pragma unroll
                 for (int h2 = 0; h2 < 2; h2++)
-                    acc[ct][h2] = v16f{};
-            if (nch == 0)
-                return;
-            // every slot is free (a second pass starts after the flag barriers), so the first
-            // two chunks go out before the barrier that the QK waves reach once their Q loads
-            // are issued
+                    acc[ct][h2] *= f.alpha[h2];
+#pragma unroll
+            for (int ct = 0; ct < NCT; ct++) {
+#pragma unroll
+                for (int h2 = 0; h2 < 2; h2++) {
+                    acc[ct][h2] = mfma32(f.vt[ct], f.bh[h2], acc[ct][h2], 127);
+                    if constexpr (TWO)  // the second term's 2^-4
+                        acc[ct][h2] = mfma32(f.vt[ct], f.bl[h2], acc[ct][h2], 127 - 4);
+                }
+            }
+        };
+
+#pragma unroll
+        for (int ct = 0; ct < NCT; ct++)
+#pragma unroll
+            for (int h2 = 0; h2 < 2; h2++)
+                acc[ct][h2] = v16f{};
+        if (nch > 0) {
+            // every slot is free, so the first two chunks go out before the barrier that the
+            // QK waves reach once their Q loads are issued
             issue(0);
             if (nch > 1)
                 issue(1);
@@ -787,13 +764,8 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
                 else
                     wait_dma<0>();
             }
-        };
-
-        run_range();
-        lds_barrier();                              // the QK waves decide on a second pass
-        lds_barrier();
-        if (*flag != 0)
-            run_range();
+        }
+        mfma_result_pad();                          // the last products have landed
         epilogue(acc);
     }
 }

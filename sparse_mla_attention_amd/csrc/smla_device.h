@@ -23,8 +23,6 @@ constexpr float ANCHOR = 448.0f;                   // P anchor: E4M3's largest f
 constexpr float LOG2_ANCHOR = 8.807354922057604f;  // log2(448)
 constexpr float LN2 = 0.6931471805599453f;
 constexpr float LOG2E = 1.4426950408889634f;
-constexpr int FRAME_LIMIT = 96;                    // largest frame offset e of the first pass
-constexpr int E_MIN = -120;                        // smallest offset (preset frames)
 
 // XOR on the 16-byte piece index of latent row `key` in a V slot: eight consecutive keys put
 // a 32-byte column pair on eight distinct bank groups (the transposed reads of P.V) and
@@ -159,8 +157,8 @@ __device__ inline v4f mfma16k32(v2i a, v2i b, v4f c)
                                                       __builtin_bit_cast(long, b), c, 0, 0, 0);
 }
 
-// 32x32x64 FP8, unit A scale and the per-lane B scale byte sb (lane l scales column l % 32 of
-// its own 32-key block; both blocks of a chunk carry the same byte).
+// 32x32x64 FP8, unit A scale and the per-lane B scale byte sb (E8M0: lane l scales column
+// l % 32 of its own 32-key block): 127 (2^0) for P's first term, 123 (2^-4) for its second.
 __device__ inline v16f mfma32(v8i a, v8i b, v16f c, int sb)
 {
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, sb);
@@ -181,33 +179,6 @@ __device__ inline uint32_t bf16x2(float lo, float hi)
 {
     const v2bf16 r = {(__bf16)lo, (__bf16)hi};
     return __builtin_bit_cast(uint32_t, r);
-}
-
-// A tile's 16 accumulator registers times `scale`, as FP16 pairs in register order: word d of
-// part j holds registers 8 j + 2 d (low half) and 8 j + 2 d + 1.  The conversion instruction is
-// written out so that it rounds the FP32 products to nearest even; left to itself the compiler
-// may fuse a product and its conversion into a mixed-precision instruction that rounds once, and
-// every site that packs the same values must get the same bits.
-__device__ inline void f16_pack(const v16f &x, float scale, v4i (&pk)[2])
-{
-#pragma unroll
-    for (int j = 0; j < 2; j++)
-#pragma unroll
-        for (int d = 0; d < 4; d++) {
-            const float lo = x[8 * j + 2 * d] * scale, hi = x[8 * j + 2 * d + 1] * scale;
-            int r;
-            asm("v_cvt_pk_f16_f32 %0, %1, %2" : "=v"(r) : "v"(lo), "v"(hi));
-            pk[j][d] = r;
-        }
-}
-// register r of a tile packed by f16_pack
-__device__ inline float f16_unpack(const v4i (&pk)[2], int r)
-{
-    typedef _Float16 v2f16 __attribute__((ext_vector_type(2)));
-    // (the element goes through a local: this compiler bit-casts a vector-element lvalue from
-    // element 0 whatever the index)
-    const int word = pk[r >> 3][(r >> 1) & 3];
-    return (float)__builtin_bit_cast(v2f16, word)[r & 1];
 }
 
 // Pad between the last matrix instruction of a chain and the first vector read of its result.

@@ -22,11 +22,14 @@ struct DecodeParams {
     uint16_t *out;              // BF16 [T, H, 512]
     float *lse;                 // [T, H] or null
     int32_t lse_log2;           // 1: base-2 LSE
-    uint16_t *ws_o;             // FP16 partials: a block of (heads per group) x 512 values
-                                // per (token, group, range), in the kernel's register order
+    float *ws_o;                // FP32 partials: a block of (heads per group) x 512 floats per
+                                // (token, group, range), in the kernel's register order
     float *ws_ml;               // (frame, sum) [T, groups, splits, heads per group, 2]
     int32_t *counters;          // [T, groups, 2]: arrival ticket, ready count; zero between
                                 // calls (splits > 1)
+    int32_t *status;            // workspace status word: merges that gave up waiting
+    int32_t wait_polls;         // bound of the 64-head kernel's merge wait (polls)
+    int32_t wait_extra;         // 0; 1 makes that wait unreachable (a test hook)
     int32_t splits;             // key ranges per (token, head group)
     int32_t groups;             // head groups per token = ceil(ceil(H / 32) / tiles)
 };

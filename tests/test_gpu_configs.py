@@ -7,9 +7,9 @@ import torch
 import oracle
 import sparse_mla_attention_amd as smla
 from sparse_mla_attention_amd import inputs
-from smla_testlib import (EXACT_MAX_ABS, EXACT_REL_L2, FRAME_LIMIT, LSE_ABS, MIMIC_MAX_ABS,
-                          MIMIC_REL_L2, DeviceProblem, bf16_to_f64, check_empty_rows_exact, dev,
-                          log, lse_err, rel_l2)
+from smla_testlib import (EXACT_MAX_ABS, EXACT_REL_L2, LSE_ABS, MIMIC_MAX_ABS, MIMIC_REL_L2,
+                          DeviceProblem, bf16_to_f64, check_empty_rows_exact, dev, flip_stats,
+                          log, lse_err, mimic_max_abs_ok, rel_l2)
 
 pytestmark = pytest.mark.gpu
 
@@ -33,23 +33,27 @@ def test_config_exact_parity(name):
 
 
 @pytest.mark.parametrize("name", ["tiny", "verify", "dsv4"])
-def test_config_one_term_matches_mimic(name):
+def test_config_one_term_matches_recipe_and_exact_gate(name):
+    """The one-term path (the attn_sparse page's E4M3-P recipe) against mimic mode of the same
+    plan, and against the exact formula at the gate the method is held to on these workloads:
+    max-abs <= 3e-2 and LSE within 2e-3 (its relative L2 is the recipe's own, ~2e-2)."""
     p = inputs.CONFIGS[name]()
     d = DeviceProblem(p)
     out, lse, plan = d.run(one_term=True)
     check_empty_rows_exact(d.out, d.lse, p)
     ref, ref_lse = oracle.decode_mimic(p, plan.splits, plan.chunk, terms=1,
-                                       lse_log2=p["lse_log2"], frame_limit=FRAME_LIMIT)
+                                       lse_log2=p["lse_log2"])
+    ex, ex_lse = oracle.decode_exact(p, lse_log2=p["lse_log2"])
     if p["lse_log2"]:
-        ref_lse, lse = ref_lse * LN2, lse * LN2
+        ref_lse, ex_lse, lse = ref_lse * LN2, ex_lse * LN2, lse * LN2
     r, m, le = rel_l2(out, ref), float(np.abs(out - ref).max()), lse_err(lse, ref_lse)
-    ex, _ = oracle.decode_exact(p)
-    log(f"  {p['name']} one-term {plan}: vs mimic rel_l2={r:.3e} max_abs={m:.3e} lse={le:.3e}; "
-        f"vs exact rel_l2={rel_l2(out, ex):.3e}")
-    assert r <= MIMIC_REL_L2 and m <= MIMIC_MAX_ABS and le <= LSE_ABS
-    # against the exact formula: the recipe's own rounding (mimic vs exact) plus the tolerance
-    bound = float(np.abs(ref - ex).max()) + MIMIC_MAX_ABS
-    assert float(np.abs(out - ex).max()) <= bound
+    re, me, lee = rel_l2(out, ex), float(np.abs(out - ex).max()), lse_err(lse, ex_lse)
+    log(f"  {p['name']} one-term {plan}: vs recipe rel_l2={r:.3e} max_abs={m:.3e} lse={le:.3e} "
+        f"({flip_stats(out, ref, MIMIC_MAX_ABS)}); vs exact rel_l2={re:.3e} max_abs={me:.3e} "
+        f"lse={lee:.3e}")
+    assert r <= MIMIC_REL_L2 and le <= LSE_ABS
+    assert mimic_max_abs_ok(out, ref, MIMIC_MAX_ABS, EXACT_MAX_ABS)
+    assert me <= EXACT_MAX_ABS and lee <= LSE_ABS
 
 
 def _throughput_units(T=64, H=128, count=48, seed=7):
@@ -81,19 +85,62 @@ def test_throughput_config_sampled_parity():
                     lens=w["lens"].cpu().numpy(), sinks=None, bmm1=w["bmm1"], bmm2=w["bmm2"])
         got = np.stack([bf16_to_f64(out[t, h]) for t, h in units])
         got_lse = np.array([float(lse[t, h]) for t, h in units])
+        ex, ex_lse = oracle.decode_exact(host, units=units)
+        re, me, lee = rel_l2(got, ex), float(np.abs(got - ex).max()), lse_err(got_lse, ex_lse)
+        assert np.all(np.isfinite(bf16_to_f64(out)))
         if one_term:
             ref, ref_lse = oracle.decode_mimic(host, plan.splits, plan.chunk, terms=1,
-                                               units=units, frame_limit=FRAME_LIMIT)
-            tr, ta = MIMIC_REL_L2, MIMIC_MAX_ABS
+                                               units=units)
+            r, m, le = rel_l2(got, ref), float(np.abs(got - ref).max()), lse_err(got_lse, ref_lse)
+            log(f"  throughput {plan} one-term: vs recipe rel_l2={r:.3e} max_abs={m:.3e} "
+                f"lse={le:.3e} ({flip_stats(got, ref, MIMIC_MAX_ABS)}); vs exact "
+                f"rel_l2={re:.3e} max_abs={me:.3e} lse={lee:.3e} over {len(units)} units")
+            assert r <= MIMIC_REL_L2 and le <= LSE_ABS
+            assert mimic_max_abs_ok(got, ref, MIMIC_MAX_ABS, EXACT_MAX_ABS)
+            assert me <= EXACT_MAX_ABS and lee <= LSE_ABS
         else:
-            ref, ref_lse = oracle.decode_exact(host, units=units)
-            tr, ta = EXACT_REL_L2, EXACT_MAX_ABS
-        r, m, le = rel_l2(got, ref), float(np.abs(got - ref).max()), lse_err(got_lse, ref_lse)
-        log(f"  throughput {plan} one_term={one_term}: rel_l2={r:.3e} max_abs={m:.3e} "
-            f"lse={le:.3e} over {len(units)} units")
-        assert np.all(np.isfinite(bf16_to_f64(out)))
-        assert r <= tr and m <= ta and le <= LSE_ABS
+            log(f"  throughput {plan}: vs exact rel_l2={re:.3e} max_abs={me:.3e} "
+                f"lse={lee:.3e} over {len(units)} units")
+            assert re <= EXACT_REL_L2 and me <= EXACT_MAX_ABS and lee <= LSE_ABS
         del host
+
+
+def test_throughput_config_full_parity():
+    """Every (token, head) of the large-batch launch the benchmark times (default plan,
+    two-term P) against the exact oracle: 8192 units of 2048 columns, computed by the C oracle
+    on host threads (its calls release the GIL), under the gate the method is held to."""
+    import concurrent.futures
+    import os
+    log("generating the throughput workload on the device")
+    w = inputs.config_throughput_device("cuda", index_sets=1)
+    T, H, W = 64, 128, 2048
+    out = torch.empty((T, H, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    plan = smla.plan_for(T, H, W, 576)
+    idx = w["index_sets"][0]
+    smla.sparse_mla_decode(w["q"], w["kv_a"], idx, w["lens"], w["bmm1"], w["bmm2"], out, lse,
+                           plan=plan, workspace=smla.new_workspace(plan, T, H))
+    torch.cuda.synchronize()
+    host = dict(q=w["q"].cpu().numpy(), kv_a=w["kv_a"].cpu().numpy(), kv_b=None,
+                split_col=W, qk_dim=576, indices=idx.cpu().numpy(),
+                lens=w["lens"].cpu().numpy(), sinks=None, bmm1=w["bmm1"], bmm2=w["bmm2"])
+    units = [(t, h) for t in range(T) for h in range(H)]
+    workers = max(1, min(16, os.cpu_count() or 1))
+    parts = [units[i::workers] for i in range(workers)]
+    log(f"  exact oracle over {len(units)} units on {workers} host threads")
+    with concurrent.futures.ThreadPoolExecutor(workers) as ex:
+        res = list(ex.map(lambda u: oracle.decode_exact(host, units=u), parts))
+    ref = np.empty((T * H, 512))
+    ref_lse = np.empty(T * H)
+    for i, (o, l) in enumerate(res):
+        ref[i::workers] = o
+        ref_lse[i::workers] = l
+    got = bf16_to_f64(out).reshape(T * H, 512)
+    got_lse = lse.cpu().numpy().astype(np.float64).reshape(-1)
+    r, m, le = rel_l2(got, ref), float(np.abs(got - ref).max()), lse_err(got_lse, ref_lse)
+    log(f"  throughput {plan}: all units rel_l2={r:.3e} max_abs={m:.3e} lse={le:.3e}")
+    assert np.all(np.isfinite(got))
+    assert r <= EXACT_REL_L2 and m <= EXACT_MAX_ABS and le <= LSE_ABS
 
 
 # ---------------------------------------------------------------------------------------------

@@ -6,9 +6,9 @@ import torch
 import oracle
 import sparse_mla_attention_amd as smla
 from sparse_mla_attention_amd import inputs
-from smla_testlib import (EXACT_MAX_ABS, EXACT_REL_L2, FRAME_LIMIT, LN2, LSE_ABS, MIMIC_MAX_ABS,
-                          mimic_max_abs_ok,
-                          MIMIC_REL_L2, DeviceProblem, check_empty_rows_exact, log, lse_err,
+from smla_testlib import (EXACT_MAX_ABS, EXACT_REL_L2, LN2, LSE_ABS, MIMIC_MAX_ABS,
+                          MIMIC_REL_L2, ONE_TERM_EXACT_REL_L2, DeviceProblem,
+                          check_empty_rows_exact, flip_stats, log, lse_err, mimic_max_abs_ok,
                           rel_l2)
 
 pytestmark = pytest.mark.gpu
@@ -30,17 +30,19 @@ def _check_exact(p, out, lse, lse_log2, label):
 
 
 def _check_mimic(p, out, lse, lse_log2, plan, label):
-    """One-term path: parity with mimic mode of the same plan; returns the mimic output."""
+    """One-term path: parity with mimic mode of the same plan (the attn_sparse page's recipe:
+    P at 448 of the running maximum, rescaled when it rises); returns the mimic output."""
     ref, ref_lse = oracle.decode_mimic(p, splits=plan.splits, chunk=plan.chunk, terms=1,
-                                       lse_log2=lse_log2, frame_limit=FRAME_LIMIT)
+                                       lse_log2=lse_log2)
     if lse_log2:
         ref_lse, lse = ref_lse * np.log(2), lse * np.log(2)
     r = rel_l2(out, ref)
     m = float(np.abs(out - ref).max())
     le = lse_err(lse, ref_lse)
-    log(f"{label} vs mimic: rel_l2={r:.3e} max_abs={m:.3e} lse={le:.3e}")
     tol_abs = MIMIC_MAX_ABS * max(1.0, p.get("value_scale", 1.0))
     cap = EXACT_MAX_ABS * max(1.0, p.get("value_scale", 1.0))
+    log(f"{label} vs mimic: rel_l2={r:.3e} max_abs={m:.3e} lse={le:.3e} "
+        f"({flip_stats(out, ref, tol_abs)})")
     assert r <= MIMIC_REL_L2 and le <= LSE_ABS, (r, m, le)
     assert mimic_max_abs_ok(out, ref, tol_abs, cap), (r, m, le)
     return ref
@@ -84,14 +86,13 @@ def test_decode_random_cases(name, one_term):
         check_empty_rows_exact(d.out, d.lse, p)
         label = f"{name} {plan} log2={lse_log2}"
         if one_term:
-            mim = _check_mimic(p, out, lse, lse_log2, plan, label)
-            # against the exact formula, the one-term path may deviate by the recipe's own
-            # E4M3 rounding of P (mimic vs exact) plus the kernel-vs-mimic tolerance
-            ref, _ = oracle.decode_exact(p, lse_log2=False)
-            m = float(np.abs(out - ref).max())
-            bound = (float(np.abs(mim - ref).max()) +
-                     MIMIC_MAX_ABS * max(1.0, p.get("value_scale", 1.0)))
-            assert m <= bound, (m, bound)
+            _check_mimic(p, out, lse, lse_log2, plan, label)
+            # against the exact formula: the recipe's own E4M3 rounding of P, bounded in
+            # relative L2 (its max-abs passes 3e-2 on some of these edge problems, the
+            # recipe's own, and is asserted on the workload shapes in test_gpu_configs)
+            ref, ref_lse = oracle.decode_exact(p, lse_log2=lse_log2)
+            le = lse_err(lse, ref_lse) * (LN2 if lse_log2 else 1.0)
+            assert rel_l2(out, ref) <= ONE_TERM_EXACT_REL_L2 and le <= LSE_ABS
         else:
             _check_exact(p, out, lse, lse_log2, label)
 
@@ -139,9 +140,10 @@ def test_head_groups_are_independent(one_term):
 def _rising_scores_problem(seed, T, H, W, lens):
     """Scores that climb by ~250 binades along the index row for heads with q[512:] > 0: the 64
     rope columns of row c all hold a ramp value r_c and q[h, 512:] = q_h, so the rope part of
-    the dot product is 64 q_h r_c; V, the first 512 columns, stays unit-scale noise.  The first
-    pass's anchor offset passes the frame limit and the range reruns with a preset frame.  Heads
-    with q_h < 0 see falling scores, those near 0 noise.  The ramp is spread over 64 columns so
+    the dot product is 64 q_h r_c; V, the first 512 columns, stays unit-scale noise.  The
+    running maximum rises at every chunk, by up to ~24 binades (0.37 per column), so the
+    accumulators are rescaled at every chunk, by factors down to ~2^-24.  Heads with q_h < 0
+    see falling scores, those near 0 noise.  The ramp is spread over 64 columns so
     that no single product is large: the FP8 matrix instruction sums a 64-byte block with a
     precision relative to its largest product (~2^-13.5 measured), which a lone 448 x 1 product
     would turn into score errors of 0.04 units."""
@@ -156,7 +158,7 @@ def _rising_scores_problem(seed, T, H, W, lens):
 
 
 @pytest.mark.parametrize("one_term", [False, True])
-def test_rising_scores_rerun_the_range(one_term):
+def test_rising_scores_rescale_every_chunk(one_term):
     p = _rising_scores_problem(405, 2, 32, 700, [700, 377])
     d = DeviceProblem(p)
     for splits in (1, 2):
@@ -184,7 +186,7 @@ def test_repeated_calls_are_deterministic():
     d = DeviceProblem(p)
     plan = smla.make_plan(3, 1)
     ws = d.workspace(plan)
-    counters = (d.T * 2 * 2 * 4 + 255) // 256 * 256  # 64 heads: two groups of 32
+    counters = smla.workspace_header_bytes(plan, d.T, d.H)  # status word and counters
 
     def call():
         smla.sparse_mla_decode(d.q, d.kv_a, d.indices, d.lens, p["bmm1"], p["bmm2"], d.out,

@@ -1,7 +1,8 @@
 """Parity of the 64-head decode kernel (plan tiles=2: rows gathered straight into LDS) with the
 FP64 oracle, and bit equality with the 32-head kernel: both run the same instructions per
-(column tile, head tile) in the same order (QK steps, frame rule, P bytes, P.V chunk order, l
-sums, split merge), so for the same split plan their outputs must agree bit for bit."""
+(column tile, head tile) in the same order (QK steps, running maxima and rescale factors, P
+bytes, accumulator rescales, P.V chunk order, l sums, split merge), so for the same split plan
+their outputs must agree bit for bit."""
 import numpy as np
 import pytest
 import torch
@@ -9,9 +10,9 @@ import torch
 import oracle
 import sparse_mla_attention_amd as smla
 from sparse_mla_attention_amd import inputs
-from smla_testlib import (EXACT_MAX_ABS, EXACT_REL_L2, FRAME_LIMIT, LSE_ABS, MIMIC_MAX_ABS,
-                          MIMIC_REL_L2, DeviceProblem, check_empty_rows_exact, log, lse_err,
-                          mimic_max_abs_ok, rel_l2)
+from smla_testlib import (EXACT_MAX_ABS, EXACT_REL_L2, LSE_ABS, MIMIC_MAX_ABS, MIMIC_REL_L2,
+                          DeviceProblem, bf16_to_f64, check_empty_rows_exact, flip_stats, log,
+                          lse_err, mimic_max_abs_ok, rel_l2)
 
 pytestmark = pytest.mark.gpu
 
@@ -29,22 +30,17 @@ def _exact(p, out, lse, lse_log2, label):
     assert r <= EXACT_REL_L2 and m <= tol_abs and le <= LSE_ABS, (r, m, le)
 
 
-def _mimic(p, out, lse, plan, label, check_max_abs=True):
-    """One-term path against mimic mode of the same plan.  Both quantize P to E4M3, but from
-    scores computed in FP32 (kernel) and FP64 (oracle): a P that sits within rounding distance
-    of an E4M3 midpoint may round to neighbouring codes on the two sides, one code step (1/16 to
-    1/8 of P) apart.  On unit-scale data that stays inside the max-abs tolerance; on softmaxes
-    dominated by a few keys (the large-score case) one such step moves an output by several
-    percent of a V value, so there only rel-L2 and the LSE are gated (that case is also held
-    bit-equal to the 32-head kernel)."""
-    ref, ref_lse = oracle.decode_mimic(p, splits=plan.splits, chunk=plan.chunk, terms=1,
-                                       frame_limit=FRAME_LIMIT)
+def _mimic(p, out, lse, plan, label):
+    """One-term path against mimic mode of the same plan (the attn_sparse page's recipe), at the
+    tolerances stated in smla_testlib (one-code E4M3 flips from FP32 vs FP64 scores allowed on
+    a few isolated elements)."""
+    ref, ref_lse = oracle.decode_mimic(p, splits=plan.splits, chunk=plan.chunk, terms=1)
     r, m, le = rel_l2(out, ref), float(np.abs(out - ref).max()), lse_err(lse, ref_lse)
-    log(f"{label} vs mimic: rel_l2={r:.3e} max_abs={m:.3e} lse={le:.3e}")
     tol_abs = MIMIC_MAX_ABS * max(1.0, p.get("value_scale", 1.0))
+    log(f"{label} vs mimic: rel_l2={r:.3e} max_abs={m:.3e} lse={le:.3e} "
+        f"({flip_stats(out, ref, tol_abs)})")
     assert r <= MIMIC_REL_L2 and le <= LSE_ABS, (r, m, le)
-    if check_max_abs:
-        assert mimic_max_abs_ok(out, ref, tol_abs, EXACT_MAX_ABS * max(1.0, p.get("value_scale", 1.0))), (r, m, le)
+    assert mimic_max_abs_ok(out, ref, tol_abs, EXACT_MAX_ABS * max(1.0, p.get("value_scale", 1.0))), (r, m, le)
 
 
 def _same_bits(d, p, splits, one_term):
@@ -112,8 +108,7 @@ def test_g64_one_term_matches_mimic(name):
         plan = smla.make_plan(splits, 2)
         out, lse, _ = d.run(plan=plan, one_term=True)
         check_empty_rows_exact(d.out, d.lse, p)
-        _mimic(p, out, lse, plan, f"{name} {plan} one-term",
-               check_max_abs=name != "H64_large_scores")
+        _mimic(p, out, lse, plan, f"{name} {plan} one-term")
 
 
 @pytest.mark.parametrize("name", list(CASES))
@@ -139,10 +134,10 @@ def test_g64_split_plans(splits):
     _mimic(p, out, lse, plan, f"64-head splits={splits} one-term")
 
 
-def test_g64_rising_scores_rerun_the_range():
-    """Scores climbing ~250 binades along the row: the first pass's frame offset passes the
-    limit and the range is computed again with a preset frame (same problem as the 32-head
-    kernel's test, at 64 heads)."""
+def test_g64_rising_scores_rescale_every_chunk():
+    """Scores climbing ~250 binades along the row: the running maximum rises at every chunk and
+    the accumulators are rescaled each time (same problem as the 32-head kernel's test, at 64
+    heads)."""
     from test_gpu_decode import _rising_scores_problem
     p = _rising_scores_problem(530, 2, 64, 700, [700, 377])
     d = DeviceProblem(p)
@@ -210,8 +205,9 @@ def test_g64_graph_replay_matches_eager():
 def test_g64_large_batch_split_merge_is_deterministic():
     """The large-batch launch (T=64, H=128, 2048 columns, two ranges per 64-head group: 256
     workgroups that all reach the split exchange together): eight calls on one workspace give
-    the first call's bytes, and the output equals the 32-head kernel's (one range, no
-    exchange) on every call."""
+    the first call's bytes, equal to the 32-head kernel's under the same two-range plan (its
+    store-first exchange), and within the exact-mode tolerance of a one-range launch (no
+    exchange at all)."""
     w = inputs.config_throughput_device("cuda", index_sets=1)
     T, H = 64, 128
     idx = w["index_sets"][0]
@@ -224,7 +220,16 @@ def test_g64_large_batch_split_merge_is_deterministic():
     smla.sparse_mla_decode(w["q"], w["kv_a"], idx, w["lens"], w["bmm1"], w["bmm2"], ref, ref_lse,
                            plan=smla.make_plan(2, 1), workspace=smla.new_workspace(
                                smla.make_plan(2, 1), T, H))
+    one = torch.empty_like(out)
+    one_lse = torch.empty_like(lse)
+    smla.sparse_mla_decode(w["q"], w["kv_a"], idx, w["lens"], w["bmm1"], w["bmm2"], one, one_lse,
+                           plan=smla.make_plan(1, 2))
     torch.cuda.synchronize()
+    a, b = ref.float().cpu().numpy(), one.float().cpu().numpy()
+    r, m = rel_l2(a, b), float(np.abs(a - b).max())
+    dl = float((ref_lse - one_lse).abs().max())
+    log(f"large batch: two ranges vs one range rel_l2={r:.3e} max_abs={m:.3e} lse={dl:.3e}")
+    assert r <= EXACT_REL_L2 and m <= EXACT_MAX_ABS and dl <= LSE_ABS
     first = None
     for i in range(8):
         out.view(torch.int16).fill_(0x7FC0)
@@ -238,3 +243,35 @@ def test_g64_large_batch_split_merge_is_deterministic():
         assert bad == 0, f"call {i}: {bad} output elements differ from the first call"
         assert torch.equal(got, ref.view(torch.int16)), f"call {i}: differs from the 32-head kernel"
         assert torch.equal(lse.view(torch.int32), ref_lse.view(torch.int32))
+
+
+def test_g64_merge_wait_gives_up_loudly():
+    """The merging range's wait is bounded.  Forced from the host (the test hook makes it wait
+    for one partial more than exists, for 16 polls; every kernel still exits normally), each
+    (token, head group) merge gives up: the workspace status word counts them, their outputs
+    and LSEs are NaN, and after the workspace is zero-filled again the next call is correct."""
+    p = inputs.random_problem(540, 3, 128, 300, pool_rows=3000, neg_frac=0.1, sinks=True,
+                              lens=np.array([300, 170, 260]))
+    d = DeviceProblem(p)
+    plan = smla.make_plan(2, 2)
+    ws = smla.new_workspace(plan, d.T, d.H)
+
+    def call():
+        smla.sparse_mla_decode(d.q, d.kv_a, d.indices, d.lens, p["bmm1"], p["bmm2"], d.out,
+                               d.lse, sinks=d.sinks, plan=plan, workspace=ws)
+        torch.cuda.synchronize()
+    try:
+        smla.testing_set_merge_wait(16, unreachable=True)
+        call()
+    finally:
+        smla.testing_set_merge_wait()
+    units = d.T * 2  # two 64-head groups per token
+    assert smla.workspace_status(ws) == units
+    assert torch.isnan(d.out.float()).all(), "a merge that gave up must not write a result"
+    assert torch.isnan(d.lse).all()
+    ws.zero_()
+    call()
+    assert smla.workspace_status(ws) == 0
+    out = bf16_to_f64(d.out).reshape(d.T * d.H, 512)
+    _exact(p, out, d.lse.cpu().numpy().astype(np.float64).reshape(-1), False,
+           "after the workspace was zero-filled again")

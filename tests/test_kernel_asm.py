@@ -121,3 +121,20 @@ def test_async_row_loads_are_never_touched_in_flight():
     # the same kernels spill nothing (the compiler's waits for a spill reload do not know the
     # row loads in flight, so they would drain them)
     assert not re.search(r"\.vgpr_spill_count:\s+[1-9]", text)
+
+
+def test_decode_kernels_spill_nothing():
+    """Neither decode kernel spills registers: a spill reload's wait would also drain the row
+    loads in flight, and scratch traffic would sit on the gather's memory path."""
+    for src in ("smla_decode.hip", "smla_decode_g64.hip"):
+        with tempfile.TemporaryDirectory() as tmp:
+            out = os.path.join(tmp, "k.s")
+            cmd = [build.HIPCC, *build.FLAGS, "--cuda-device-only", "-S",
+                   os.path.join(build.CSRC, src), "-o", out]
+            r = subprocess.run(cmd, capture_output=True, text=True)
+            if r.returncode != 0:
+                pytest.fail(r.stdout + r.stderr)
+            text = open(out).read()
+        counts = re.findall(r"\.vgpr_spill_count:\s+(\d+)", text)
+        assert counts, src
+        assert all(int(c) == 0 for c in counts), (src, counts)

@@ -310,18 +310,7 @@ def test_mimic_lse_ignores_p_quantization():
     np.testing.assert_allclose(lm, lse, rtol=1e-12)
 
 
-@pytest.mark.parametrize("splits,chunk,limit", [(1, 64, 64), (3, 8, 1), (2, 5, 2), (4, 16, 96)])
-def test_mimic_frames_without_quantization_is_exact(splits, chunk, limit):
-    p = inputs.random_problem(20, 2, 16, 40, pool_rows=300, neg_frac=0.2, lens=[40, 23],
-                              sinks=True, value_scale=4.0)
-    out, lse = oracle.decode_exact(p)
-    om, lm = oracle.decode_mimic(p, splits=splits, chunk=chunk, quantize=False,
-                                 frame_limit=limit)
-    np.testing.assert_allclose(om, out, rtol=1e-11, atol=1e-13)
-    np.testing.assert_allclose(lm, lse, rtol=1e-12)
-
-
-def _frame_problem(dots, marker_row, marker_col, c=2.0 / 3.0):
+def _one_head_problem(dots, marker_row, marker_col, c=2.0 / 3.0):
     """One head, q = e_0, row r = dots[r] at column 0 (and 448 at marker_col of marker_row):
     base-2 score of row r = c * dots[r]."""
     def e4(x):
@@ -340,113 +329,66 @@ def _frame_problem(dots, marker_row, marker_col, c=2.0 / 3.0):
                 sinks=None, bmm1=c * LN2, bmm2=1.0)
 
 
-def test_mimic_frames_second_pass_worked_example():
-    """Hand-worked second pass (chunks of one column, base-2 scores 0, 3/2, -40/3; only the
-    last row has latent column 100 = 448).  The first pass sets G = 0 and the second chunk's
-    offset is ceil(3/2) = 2.  Limit 2: no second pass; the third column's P = 448 * 2^(-40/3
-    - 2) = 5.55 * 2^-9 rounds to 6 * 2^-9 (E4M3 subnormal step) with weight 2^2.  Limit 1:
-    the range reruns with G = 3/2: offsets -1, 0, 0, P = 448 * 2^-1/2 -> 320 (weight 1/2),
-    448, and 448 * 2^(-40/3 - 3/2) = 7.86 * 2^-9 -> 8 * 2^-9 (weight 1).  Both passes give the
-    same l in their frames, so the LSE agrees."""
-    p = _frame_problem([0.0, 2.25, -20.0], 2, 100)
-    s2 = np.array([0.0, 1.5, -40.0 / 3.0])
-    o2, l2 = oracle.decode_mimic(p, splits=1, chunk=1, terms=1, frame_limit=2, lse_log2=True)
-    lf = 448.0 * (1.0 + 2.0 ** 1.5 + 2.0 ** s2[2])           # frame G = 0
-    assert abs(o2[0, 100] - 4 * 6 * 2.0 ** -9 * 448.0 / lf) < 1e-12
-    # column 0: rows 1 and 2 (values 2.25 and -20) with P 320 (weight 4) and 6 * 2^-9 (4)
-    assert abs(o2[0, 0] - 4 * (320 * 2.25 - 6 * 2.0 ** -9 * 20) / lf) < 1e-12
-    o1, l1 = oracle.decode_mimic(p, splits=1, chunk=1, terms=1, frame_limit=1, lse_log2=True)
-    lg = 448.0 * (2.0 ** -1.5 + 1.0 + 2.0 ** (s2[2] - 1.5))  # frame G = 3/2
-    assert abs(o1[0, 100] - 8 * 2.0 ** -9 * 448.0 / lg) < 1e-12
-    assert abs(o1[0, 0] - (448 * 2.25 - 8 * 2.0 ** -9 * 20) / lg) < 1e-12
-    assert abs(l1[0] - (1.5 + math.log2(lg) - math.log2(448.0))) < 1e-12
-    assert abs(l1[0] - l2[0]) < 1e-12
+def test_mimic_recipe_worked_example_with_rescale():
+    """Hand-worked recipe (attn_sparse page, module docstring: P at 448 of the running maximum,
+    E4M3, unquantized sums, rescale when the maximum rises), one head, chunks of one column,
+    base-2 scores 3/2, 0, 3 (dot products 2.25, 0, 4.5 at 2/3 per unit); only the second row
+    has latent column 100 = 448.
+      chunk 0: m = 3/2, P = 448 (exact), l = 448.
+      chunk 1: m = 3/2, P = 448 * 2^-1.5 = 158.392 -> E4M3 160 (the grid step is 16 on
+               [128, 256)); l = 606.392.
+      chunk 2: m = 3, alpha = 2^-1.5 rescales acc and l; P = 448 (exact).
+    So out[100] = 160 * 448 * 2^-1.5 / L and out[0] = (448 * 2.25 * 2^-1.5 + 448 * 4.5) / L,
+    L = 606.392 * 2^-1.5 + 448; LSE2 = 3 - log2(448) + log2(L).  Two terms: the second term is
+    E4M3(16 (158.392 - 160)) = E4M3(-25.73) = -26 (step 2 on [16, 32)), so P = 160 - 26/16."""
+    p = _one_head_problem([2.25, 0.0, 4.5], 1, 100)
+    r = 2.0 ** -1.5
+    p1 = 448.0 * r
+    L = (448.0 + p1) * r + 448.0
+    out, lse = oracle.decode_mimic(p, splits=1, chunk=1, terms=1, lse_log2=True)
+    assert abs(out[0, 100] - 160.0 * 448.0 * r / L) < 1e-12
+    assert abs(out[0, 0] - (448.0 * 2.25 * r + 448.0 * 4.5) / L) < 1e-12
+    assert abs(lse[0] - (3.0 - math.log2(448.0) + math.log2(L))) < 1e-12
+    out2, _ = oracle.decode_mimic(p, splits=1, chunk=1, terms=2, lse_log2=True)
+    assert abs(out2[0, 100] - (160.0 - 26.0 / 16.0) * 448.0 * r / L) < 1e-12
+    # one chunk of three columns anchors all three at the final maximum: P = 448 * 2^-1.5
+    # = 158.392 -> 160 for the first row as well, 448 * 2^-3 = 56 (exact) for the second
+    out3, _ = oracle.decode_mimic(p, splits=1, chunk=3, terms=1, lse_log2=True)
+    L3 = p1 + 56.0 + 448.0
+    assert abs(out3[0, 100] - 56.0 * 448.0 / L3) < 1e-12
+    assert abs(out3[0, 0] - (160.0 * 2.25 + 448.0 * 4.5) / L3) < 1e-12
 
 
-def test_mimic_frames_second_pass_floor():
-    """The second pass raises offsets below -120 to -120: with base-2 scores 0 and 149.33 (G =
-    149.33), the first column's P = 448 * 2^(0 - 149.33 + 120) = 7e-7 rounds to E4M3 zero, so
-    its marker column (200, first row) is exactly 0, while the unquantized sum (and so the LSE)
-    still holds it; without the floor P would be 352 at weight 2^-149."""
-    p = _frame_problem([0.0, 224.0], 0, 200)
-    s_top = 224.0 * 2.0 / 3.0
-    out, lse = oracle.decode_mimic(p, splits=1, chunk=1, terms=1, frame_limit=1, lse_log2=True)
-    assert out[0, 200] == 0.0
-    assert abs(out[0, 0] - 224.0 / (1.0 + 2.0 ** -s_top)) < 1e-12 * 224.0
-    assert abs(lse[0] - (s_top + math.log2(1.0 + 2.0 ** -s_top))) < 1e-12
-    ex, _ = oracle.decode_exact(p, lse_log2=True)
-    assert ex[0, 200] > 0.0
+def test_mimic_recipe_underflowing_rescale():
+    """A maximum that rises by more than the FP64 exponent range underflows alpha to zero:
+    base-2 scores 0 and 1120 (dot products 0 and 448 at c = 2.5): everything before the rise
+    is weighted 2^-1120 (zero in double), so the output is the second row and the LSE its
+    score; exact mode agrees."""
+    p = _one_head_problem([0.0, 448.0], 0, 200, c=2.5)
+    out, lse = oracle.decode_mimic(p, splits=1, chunk=1, terms=1, lse_log2=True)
+    assert out[0, 200] == 0.0  # alpha = 0: the first row's contribution is gone
+    assert abs(out[0, 0] / 448.0 - 1.0) < 1e-13
+    assert abs(lse[0] / 1120.0 - 1.0) < 1e-13
+    ex, ex_lse = oracle.decode_exact(p, lse_log2=True)
+    assert ex[0, 200] == 0.0
+    assert abs(ex[0, 0] / 448.0 - 1.0) < 1e-13 and abs(ex_lse[0] / 1120.0 - 1.0) < 1e-13
 
 
-def test_mimic_frames_equal_recipe_when_first_chunk_holds_the_max():
-    """If the first chunk holds the maximum score, every anchor of both variants is that
-    maximum, so frame anchoring and the recipe quantize every P identically."""
-    p = inputs.random_problem(22, 1, 1, 48, pool_rows=400)
-    rows = _e4m3_f64(p["kv_a"][p["indices"][0]]).numpy()
-    q = _e4m3_f64(p["q"][0, 0]).numpy()
-    order = np.argsort(-(rows[:, :576] @ q), kind="stable")
-    p["indices"] = np.ascontiguousarray(p["indices"][:, order])
+def test_mimic_anchor_holds_the_running_max_exactly():
+    """Every chunk whose maximum is the running maximum quantizes that P to exactly 448, so a
+    row that holds the running maximum in every chunk (scores rising chunk by chunk) carries no
+    quantization error: with chunks of one column the recipe equals exact mode."""
+    p = _one_head_problem([0.0, 1.0, 2.5, 4.0, 7.0, 12.0], 5, 300, c=1.0)
     for terms in (1, 2):
-        a = oracle.decode_mimic(p, splits=1, chunk=8, terms=terms, frame_limit=96)
-        b = oracle.decode_mimic(p, splits=1, chunk=8, terms=terms)
-        np.testing.assert_allclose(a[0], b[0], rtol=1e-13, atol=1e-15)
-        np.testing.assert_allclose(a[1], b[1], rtol=1e-13)
-    # reversed order: the maximum arrives last, the anchors differ and so does the rounding
-    p["indices"] = np.ascontiguousarray(p["indices"][:, ::-1])
-    a = oracle.decode_mimic(p, splits=1, chunk=8, terms=1, frame_limit=96)
-    b = oracle.decode_mimic(p, splits=1, chunk=8, terms=1)
-    assert np.abs(a[0] - b[0]).max() > 0
-    np.testing.assert_allclose(a[1], b[1], rtol=1e-12)  # the LSE uses unquantized P
-
-
-def test_mimic_frames_worked_example():
-    """Hand-worked frame anchoring (one head, chunks of one column, base-2 scores 0, 1/2 and
-    -40/3): G = 0; the second and third chunks anchor at F = G + ceil(1/2) = 1, so the third
-    column's P = 448 * 2^(-40/3 - 1) = 11.16 * 2^-9 rounds to the E4M3 value 11 * 2^-9 and
-    enters with weight 2^1.  Only the third row has latent column 100 (value 448), so
-    out[100] = bmm2 * 2 * 11 * 2^-9 * 448 / l with l = sum of 2^e * p over the columns.
-    An anchor one binade higher would round 5.58 * 2^-9 to 6 * 2^-9 (13% off)."""
-    def e4(x):
-        return int(torch.tensor([x], dtype=torch.float64).to(torch.float8_e4m3fn)
-                   .view(torch.uint8)[0])
-    q = np.zeros((1, 1, 576), np.uint8)
-    q[0, 0, 0] = e4(1.0)
-    kv = np.zeros((3, 576), np.uint8)
-    kv[1, 0] = e4(0.75)
-    kv[2, 0] = e4(-20.0)
-    kv[2, 100] = e4(448.0)
-    c = 2.0 / 3.0  # base-2 score per unit dot product
-    p = dict(q=q, kv_a=kv, kv_b=None, split_col=3, qk_dim=576,
-             indices=np.array([[0, 1, 2]], np.int32), lens=np.array([3], np.int32),
-             sinks=None, bmm1=c * LN2, bmm2=1.0)
-    out, lse = oracle.decode_mimic(p, splits=1, chunk=1, terms=1, frame_limit=96, lse_log2=True)
-    s2 = np.array([0.0, 0.5, -40.0 / 3.0])
-    e = np.array([0, 1, 1])
-    l = float(np.sum(2.0 ** e * 448.0 * 2.0 ** (s2 - e)))
-    assert abs(out[0, 100] - 2 * 11 * 2.0 ** -9 * 448.0 / l) < 1e-12
-    assert abs(lse[0] - (math.log2(l) - math.log2(448.0))) < 1e-12
-    # the recipe (anchor at the running max 1/2) rounds 448 * 2^(-40/3 - 1/2) = 15.8 * 2^-9
-    # to 16 * 2^-9 with weight 2^(1/2 - 0) folded into its rescale
-    rec, _ = oracle.decode_mimic(p, splits=1, chunk=1, terms=1)
-    assert abs(rec[0, 100] - 16 * 2.0 ** -9 * 448.0 * 2.0 ** 0.5 / l) < 1e-12
-
-
-def test_mimic_frames_accuracy_matches_recipe():
-    """Frame anchoring rounds P with the same relative precision as the recipe (E4M3's
-    precision does not depend on the binade), so both land at the same error level."""
-    p = inputs.random_problem(23, 4, 16, 256, pool_rows=2000)
-    out, _ = oracle.decode_exact(p)
-    nrm = np.linalg.norm(out)
-    for terms in (1, 2):
-        e_rec = np.linalg.norm(oracle.decode_mimic(p, 1, 64, terms=terms)[0] - out) / nrm
-        e_frm = np.linalg.norm(oracle.decode_mimic(p, 1, 64, terms=terms,
-                                                   frame_limit=96)[0] - out) / nrm
-        assert 0.5 < e_frm / e_rec < 2.0, (terms, e_rec, e_frm)
-        # limit 1: most ranges rerun with a preset frame, at the same error level
-        e_two = np.linalg.norm(oracle.decode_mimic(p, 1, 8, terms=terms,
-                                                   frame_limit=1)[0] - out) / nrm
-        e_r8 = np.linalg.norm(oracle.decode_mimic(p, 1, 8, terms=terms)[0] - out) / nrm
-        assert 0.5 < e_two / e_r8 < 2.0, (terms, e_r8, e_two)
+        out, lse = oracle.decode_mimic(p, splits=1, chunk=1, terms=terms)
+        ex, ex_lse = oracle.decode_exact(p)
+        np.testing.assert_allclose(out, ex, rtol=1e-13, atol=1e-13)
+        np.testing.assert_allclose(lse, ex_lse, rtol=1e-13)
+    # falling scores: every later P is below the anchor and rounds
+    p = _one_head_problem([12.0, 7.0, 4.0, 2.5, 1.0, 0.0], 5, 300, c=1.0)
+    out, _ = oracle.decode_mimic(p, splits=1, chunk=1, terms=1)
+    ex, _ = oracle.decode_exact(p)
+    assert np.abs(out - ex).max() > 1e-6
 
 
 # ---------------------------------------------------------------------------
