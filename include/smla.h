@@ -43,6 +43,8 @@ typedef int32_t smla_status;
 #define SMLA_EUNSUPPORTED 2  /* a shape this build has no kernel for (see each entry point) */
 #define SMLA_EWORKSPACE 3    /* the workspace is missing or smaller than required */
 #define SMLA_EHIP 4          /* a HIP runtime error (device query or kernel launch) */
+#define SMLA_ESCRATCH 5      /* sparse_mla_decode_noalloc: the problem's workspace would exceed
+                                SMLA_NOALLOC_SCRATCH_BYTES */
 
 /* Flags. */
 #define SMLA_LSE_LOG2 0x1u   /* LSE outputs in base 2 (default: natural log) */
@@ -155,6 +157,32 @@ smla_status sparse_mla_decode(const void *q, int64_t q_stride_t, int64_t q_strid
                               void *out, float *lse, uint32_t flags,
                               const smla_plan *plan, void *workspace, size_t workspace_bytes,
                               hipStream_t stream);
+
+/*
+ * sparse_mla_decode_noalloc -- sparse_mla_decode for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * Arguments, results, errors and plan as sparse_mla_decode, without the workspace: the split-KV
+ * workspace is a static device array of SMLA_NOALLOC_SCRATCH_BYTES that the library holds on
+ * every GPU it runs on until the process ends.  No call allocates or frees anything.  Each call
+ * first clears the array's status word and arrival counters with a small kernel on `stream`,
+ * then runs the decode, so every call starts clean.  All calls on one GPU share that GPU's array
+ * and leave their partials in it: calls that may overlap on one GPU (different streams without
+ * ordering, or concurrent host threads) race and give wrong results; stream-ordered calls are
+ * safe.  A problem whose workspace (smla_decode_workspace_size under the plan used) exceeds
+ * SMLA_NOALLOC_SCRATCH_BYTES returns SMLA_ESCRATCH and launches nothing: the large-batch shape
+ * (T = 64, H = 128, 2048 columns, default plan) needs about 34 MB.
+ */
+#define SMLA_NOALLOC_SCRATCH_BYTES (48u << 20)
+smla_status sparse_mla_decode_noalloc(const void *q, int64_t q_stride_t, int64_t q_stride_h,
+                                      const void *kv_a, int64_t rows_a,
+                                      const void *kv_b, int64_t rows_b, int32_t split_col,
+                                      int32_t row_bytes, int32_t qk_dim,
+                                      const int32_t *indices, const int32_t *lens,
+                                      int32_t T, int32_t H, int32_t W,
+                                      float bmm1_scale, float bmm2_scale, const float *sinks,
+                                      void *out, float *lse, uint32_t flags,
+                                      const smla_plan *plan, hipStream_t stream);
 
 /*
  * lse_merge -- LSE-weighted merge of S split-KV partials (dcp page, DcpValue.merge).

@@ -18,6 +18,8 @@ LIB_PATH = os.path.join(_PKG, "_build", "libsmla.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "smla.h")
 
 SMLA_OK, SMLA_EINVAL, SMLA_EUNSUPPORTED, SMLA_EWORKSPACE, SMLA_EHIP = 0, 1, 2, 3, 4
+SMLA_ESCRATCH = 5
+NOALLOC_SCRATCH_BYTES = 48 << 20
 SMLA_LSE_LOG2 = 0x1
 SMLA_P_ONE_TERM = 0x2
 
@@ -59,6 +61,10 @@ def _load():
     L.sparse_mla_decode.restype = I32
     L.lse_merge.argtypes = [P, P, I32, I32, I32, I32, P, P, U32, P]
     L.lse_merge.restype = I32
+    L.sparse_mla_decode_noalloc.argtypes = [P, I64, I64, P, I64, P, I64, I32, I32, I32, P, P,
+                                            I32, I32, I32, F, F, P, P, P, U32,
+                                            ctypes.POINTER(Plan), P]
+    L.sparse_mla_decode_noalloc.restype = I32
     L.smla_testing_set_merge_wait.argtypes = [I32, I32]
     L.smla_testing_set_merge_wait.restype = I32
     _lib = L
@@ -167,6 +173,19 @@ def sparse_mla_decode(q, kv_a, indices, lens, bmm1_scale, bmm2_scale, out, lse=N
         qk_dim, lse_log2, one_term, plan, workspace, stream))
     if st != SMLA_OK:
         raise SmlaError(st, "sparse_mla_decode")
+    return out, lse
+
+
+def sparse_mla_decode_noalloc(q, kv_a, indices, lens, bmm1_scale, bmm2_scale, out, lse=None, *,
+                              kv_b=None, split_col=None, sinks=None, qk_dim=None, lse_log2=False,
+                              one_term=False, plan=None, stream=None):
+    """sparse_mla_decode without a workspace argument: the library's static per-device scratch
+    serves as the workspace (no allocation anywhere; calls that overlap on one GPU race)."""
+    a = _decode_args(q, kv_a, indices, lens, bmm1_scale, bmm2_scale, out, lse, kv_b, split_col,
+                     sinks, qk_dim, lse_log2, one_term, plan, None, stream)
+    st = _load().sparse_mla_decode_noalloc(*a[:22], a[24])
+    if st != SMLA_OK:
+        raise SmlaError(st, "sparse_mla_decode_noalloc")
     return out, lse
 
 

@@ -115,7 +115,24 @@ WsLayout ws_layout(const smla_plan *plan, int32_t T, int32_t H)
     return w;
 }
 
+// Zero `n` int32 words at p (the workspace's status word and arrival counters).  A kernel, not a
+// memset, so that a call captured in a graph replays it faithfully.
+__global__ void zero_words_kernel(int32_t *p, int n)
+{
+    for (int i = threadIdx.x; i < n; i += blockDim.x)
+        p[i] = 0;
+}
+
 }  // namespace
+
+namespace smla {
+
+size_t workspace_header_bytes(const smla_plan *plan, int32_t T, int32_t H)
+{
+    return ws_layout(plan, T, H).partials;
+}
+
+}  // namespace smla
 
 extern "C" {
 
@@ -127,6 +144,7 @@ const char *smla_strerror(smla_status status)
     case SMLA_EUNSUPPORTED: return "unsupported shape";
     case SMLA_EWORKSPACE: return "workspace missing or too small";
     case SMLA_EHIP: return "HIP runtime error";
+    case SMLA_ESCRATCH: return "the problem needs more scratch than the library's static buffer";
     default: return "unknown status";
     }
 }
@@ -169,16 +187,20 @@ size_t smla_decode_workspace_size(const smla_plan *plan, int32_t T, int32_t H)
     return ws_layout(plan, T, H).total;
 }
 
-smla_status sparse_mla_decode(const void *q, int64_t q_stride_t, int64_t q_stride_h,
-                              const void *kv_a, int64_t rows_a,
-                              const void *kv_b, int64_t rows_b, int32_t split_col,
-                              int32_t row_bytes, int32_t qk_dim,
-                              const int32_t *indices, const int32_t *lens,
-                              int32_t T, int32_t H, int32_t W,
-                              float bmm1_scale, float bmm2_scale, const float *sinks,
-                              void *out, float *lse, uint32_t flags,
-                              const smla_plan *plan, void *workspace, size_t workspace_bytes,
-                              hipStream_t stream)
+}  // extern "C"
+
+namespace smla {
+
+smla_status decode_impl(const void *q, int64_t q_stride_t, int64_t q_stride_h,
+                        const void *kv_a, int64_t rows_a,
+                        const void *kv_b, int64_t rows_b, int32_t split_col,
+                        int32_t row_bytes, int32_t qk_dim,
+                        const int32_t *indices, const int32_t *lens,
+                        int32_t T, int32_t H, int32_t W,
+                        float bmm1_scale, float bmm2_scale, const float *sinks,
+                        void *out, float *lse, uint32_t flags,
+                        const smla_plan *plan, void *workspace, size_t workspace_bytes,
+                        bool clear_header, hipStream_t stream)
 {
     // ---- validation (host only) ----------------------------------------------------------
     if (T < 0 || H <= 0 || H % 16 != 0 || W < 1)
@@ -258,9 +280,37 @@ smla_status sparse_mla_decode(const void *q, int64_t q_stride_t, int64_t q_strid
         p.ws_o = reinterpret_cast<float *>(base + w.partials);
         p.ws_ml = reinterpret_cast<float *>(base + w.ml);
     }
+    if (need > 0 && clear_header) {
+        const WsLayout w = ws_layout(&chosen, T, H);
+        hipLaunchKernelGGL(zero_words_kernel, dim3(1), dim3(256), 0, stream,
+                           static_cast<int32_t *>(workspace), (int)(w.partials / 4));
+        if (hipGetLastError() != hipSuccess)
+            return SMLA_EHIP;
+    }
     const hipError_t e = smla::launch_decode(p, chosen.tiles, row_bytes, qk_dim,
                                              (flags & SMLA_P_ONE_TERM) == 0, stream);
     return e == hipSuccess ? SMLA_OK : SMLA_EHIP;
+}
+
+}  // namespace smla
+
+extern "C" {
+
+smla_status sparse_mla_decode(const void *q, int64_t q_stride_t, int64_t q_stride_h,
+                              const void *kv_a, int64_t rows_a,
+                              const void *kv_b, int64_t rows_b, int32_t split_col,
+                              int32_t row_bytes, int32_t qk_dim,
+                              const int32_t *indices, const int32_t *lens,
+                              int32_t T, int32_t H, int32_t W,
+                              float bmm1_scale, float bmm2_scale, const float *sinks,
+                              void *out, float *lse, uint32_t flags,
+                              const smla_plan *plan, void *workspace, size_t workspace_bytes,
+                              hipStream_t stream)
+{
+    return smla::decode_impl(q, q_stride_t, q_stride_h, kv_a, rows_a, kv_b, rows_b, split_col,
+                             row_bytes, qk_dim, indices, lens, T, H, W, bmm1_scale, bmm2_scale,
+                             sinks, out, lse, flags, plan, workspace, workspace_bytes, false,
+                             stream);
 }
 
 smla_status smla_testing_set_merge_wait(int32_t max_polls, int32_t unreachable)

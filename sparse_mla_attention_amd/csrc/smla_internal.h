@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "smla.h"
+
 namespace smla {
 
 // One sparse_mla_decode launch, fully resolved on the host.
@@ -55,5 +57,23 @@ struct LseMergeParams {
 };
 
 hipError_t launch_lse_merge(const LseMergeParams &p, hipStream_t stream);
+
+// Bytes at the start of a workspace under `plan` that must be zero before a call: the status
+// word and the arrival counters, padded to 256.
+size_t workspace_header_bytes(const smla_plan *plan, int32_t T, int32_t H);
+
+// sparse_mla_decode with, when clear_header is set and the plan needs a workspace, a small
+// kernel that zeroes the workspace's header on `stream` first (the caller's workspace then
+// needs no zero-fill of its own).
+smla_status decode_impl(const void *q, int64_t q_stride_t, int64_t q_stride_h,
+                        const void *kv_a, int64_t rows_a,
+                        const void *kv_b, int64_t rows_b, int32_t split_col,
+                        int32_t row_bytes, int32_t qk_dim,
+                        const int32_t *indices, const int32_t *lens,
+                        int32_t T, int32_t H, int32_t W,
+                        float bmm1_scale, float bmm2_scale, const float *sinks,
+                        void *out, float *lse, uint32_t flags,
+                        const smla_plan *plan, void *workspace, size_t workspace_bytes,
+                        bool clear_header, hipStream_t stream);
 
 }  // namespace smla

@@ -132,3 +132,15 @@ def test_lse_merge_pointer_checks():
     assert L.lse_merge(P(8), P(16), 2, 1, 1, 8, P(16), None, 0, None) == smla.SMLA_EINVAL
     assert L.lse_merge(P(16), P(16), 2, 1, 1, 8, P(16), None, 0x2, None) == smla.SMLA_EINVAL
     assert L.lse_merge(None, None, 2, 0, 1, 8, None, None, 0, None) == smla.SMLA_OK
+
+
+def test_noalloc_scratch_size_matches_header():
+    """The binding's scratch bound is the header's SMLA_NOALLOC_SCRATCH_BYTES."""
+    import re
+    text = open(smla.HEADER_PATH).read()
+    m = re.search(r"#define SMLA_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m, "SMLA_NOALLOC_SCRATCH_BYTES not found"
+    assert smla.NOALLOC_SCRATCH_BYTES == int(m.group(1)) << int(m.group(2))
+    # the large-batch default plan fits; 64 ranges of 32 heads at T=64, H=128 do not
+    assert smla.workspace_size(smla.make_plan(2, 2), 64, 128) <= smla.NOALLOC_SCRATCH_BYTES
+    assert smla.workspace_size(smla.make_plan(64, 1), 64, 128) > smla.NOALLOC_SCRATCH_BYTES
