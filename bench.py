@@ -215,6 +215,34 @@ def merge_leg(smla, inputs, replays):
             "timing": f"100 calls in one HIP graph, median of {replays} replays"}
 
 
+def value_leg(smla, inputs, replays):
+    """mla_value (split merge, W_UV and the sigmoid gate) at the merge workload's shape with
+    W_UV [128, 512, 128] and gates: us per call and GB/s on its algorithmic bytes."""
+    import numpy as np
+    import torch
+    v = inputs.value_problem(900, 8, 32, 128)
+    S, T, H, D = v["partials"].shape
+    x = torch.from_numpy(v["partials"]).cuda().view(torch.bfloat16)
+    l2 = torch.from_numpy(v["lse"]).cuda()
+    w = torch.from_numpy(v["w_uv_t"]).cuda().view(torch.bfloat16).transpose(1, 2)
+    g = torch.from_numpy(v["gate"]).cuda().view(torch.bfloat16)
+    tot = torch.from_numpy(v["totals"]).cuda()
+    out = torch.empty((T, H * 128), dtype=torch.bfloat16, device="cuda")
+    t = graph_replays(lambda i, s: smla.mla_value(x, l2, w, g, out, totals=tot, stream=s), 100,
+                      replays)
+    us = statistics.median(t) * 1e3
+    nbytes = (S * T * H * D * 2 + S * T * H * 4 + H * 512 * 128 * 2 + 2 * T * H * 128 * 2 +
+              T * 4)
+    gbs = nbytes / (us * 1e-6) / 1e9
+    flops = 2 * T * H * 512 * 128
+    log(f"mla_value: {us:.2f} us, {gbs:.0f} GB/s")
+    return {"workload": f"S={S} sources, T={T}, H={H}: merge + W_UV [H, 512, 128] BF16 + "
+                        "sigmoid gate", "us_per_call": round(us, 3), "algorithmic_bytes": nbytes,
+            "gbs": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "tflops_bf16": round(flops / (us * 1e-6) / 1e12, 2), "kernel": "mla_value_kernel",
+            "timing": f"100 calls in one HIP graph, median of {replays} replays"}
+
+
 def cpu_info():
     model = "unknown"
     try:
@@ -368,6 +396,7 @@ def main():
         result["latency_small_batch"] = small_batch(smla, inputs, args.replays)
     if not args.no_merge:
         result["lse_merge"] = merge_leg(smla, inputs, args.replays)
+        result["mla_value"] = value_leg(smla, inputs, args.replays)
     if not args.no_cpu_baseline:
         log("CPU oracle baseline")
         result["cpu_baseline"] = cpu_baseline(w, sets[0].cpu().numpy(), args.cpu_seconds)

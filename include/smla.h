@@ -204,6 +204,36 @@ smla_status sparse_mla_decode_noalloc(const void *q, int64_t q_stride_t, int64_t
 smla_status lse_merge(const void *partials, const float *lse2, int32_t S, int32_t T, int32_t H,
                       int32_t D, void *out, float *lse_out, uint32_t flags, hipStream_t stream);
 
+/*
+ * mla_value -- the MLA value tail after the split merge (dcp page, DcpValue class docstring and
+ * its merge method: the owner's LSE merge over the sources, then W_UV and the sigmoid gate "as
+ * in MlaValue").  With S = 1 it is the value tail of sparse_mla_decode's own output (pass its
+ * base-2 LSE; any finite LSE weighs 1).  For each row t < T and head h < H:
+ *   latent = BF16( sum_s (2^{lse_s - top} / sum_r 2^{lse_r - top}) x_s )   (FP32 sums; sources
+ *            with a non-finite LSE weigh 0 and are never read; none finite: latent = 0)
+ *   out[t, 128 h + v] = BF16( BF16( sum_{k<512} latent[k] W_UV[h, k, v] ) * sigmoid(gate[t,
+ *            128 h + v]) ),   W_UV in BF16, FP32 accumulation, sigmoid(g) = 1 / (1 + e^{-g}),
+ * and rows whose request total totals[t / rows_per_request] is <= 0 (padded rows, whose gate
+ * may be NaN) are zeros; totals == NULL makes every row live.
+ *
+ *   partials  device BF16 [S, T, H, 512] (16-byte aligned).
+ *   lse2      device float32 [S, T, H], base 2.
+ *   w_uv      device BF16: element (h, k, v) (h < H, latent k < 512, value v < 128) at
+ *             w_uv + h * w_stride_h + v * w_stride_v + k: latent-contiguous, as the pages'
+ *             kernel reads eight latent values per load; 16-byte aligned, strides (elements)
+ *             multiples of 8.
+ *   gate      device BF16 [T, H * 128].
+ *   totals    device int32 [ceil(T / rows_per_request)] or NULL.
+ *   out       device BF16 [T, H * 128], every element written.
+ *   flags     0.
+ * S in [1, 64].  T == 0 is a no-op.  Errors: SMLA_EINVAL (sizes, null pointers, alignment,
+ * strides, flags), SMLA_EHIP.
+ */
+smla_status mla_value(const void *partials, const float *lse2, int32_t S, int32_t T, int32_t H,
+                      const void *w_uv, int64_t w_stride_h, int64_t w_stride_v, const void *gate,
+                      const int32_t *totals, int32_t rows_per_request, void *out, uint32_t flags,
+                      hipStream_t stream);
+
 /* A static string describing a status code (the pages raise RuntimeError or assert on bad
  * arguments; a C caller gets a status code and this text instead). */
 const char *smla_strerror(smla_status status);

@@ -8,7 +8,8 @@ module only builds it with gcc and marshals numpy arrays through ctypes.
 What each function computes, and the passage it follows, is stated in ``smla_oracle.c``:
 exact mode follows the formula of the sparse_mla_cute page ("What this module computes"),
 mimic mode the E4M3-P recipe of the attn_sparse page (module docstring and the merge method),
-and ``lse_merge`` the DcpValue.merge method of the dcp page.
+``lse_merge`` the DcpValue.merge method of the dcp page, and ``mla_value`` that merge followed by
+W_UV and the sigmoid gate (the DcpValue class docstring and merge method).
 """
 from __future__ import annotations
 
@@ -66,6 +67,8 @@ def lib():
         L.oracle_decode_mimic.restype = ctypes.c_int
         L.oracle_lse_merge.argtypes = [P, P, I32, I32, I32, I32, U32, P, P]
         L.oracle_lse_merge.restype = ctypes.c_int
+        L.oracle_mla_value.argtypes = [P, P, I32, I32, I32, P, I64, I64, P, P, I32, P]
+        L.oracle_mla_value.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -160,3 +163,25 @@ def lse_merge(partials_bits, lse2, lse_log2=False):
     _check(lib().oracle_lse_merge(_ptr(x), _ptr(l2), S, T, H, D, LSE_LOG2 if lse_log2 else 0,
                                   _ptr(out), _ptr(lse)))
     return out, lse
+
+
+def mla_value(partials_bits, lse2, w_uv_bits, gate_bits, totals=None, rows_per_request=1):
+    """The MLA value tail: LSE merge of S sources (BF16 bits [S,T,H,512], base-2 LSE [S,T,H]),
+    one BF16 rounding, W_UV (BF16 bits [H,512,128], element (h,k,v)), BF16 rounding, times
+    sigmoid(gate) (BF16 bits [T, H*128]), BF16 rounding; rows with totals[t // rows_per_request]
+    <= 0 are zeros.  Returns out [T, H*128] float64 (each a BF16 value)."""
+    x = np.ascontiguousarray(partials_bits, dtype=np.uint16)
+    l2 = np.ascontiguousarray(lse2, dtype=np.float32)
+    w = np.ascontiguousarray(w_uv_bits, dtype=np.uint16)
+    g = np.ascontiguousarray(gate_bits, dtype=np.uint16)
+    S, T, H, D = x.shape
+    assert D == 512 and l2.shape == (S, T, H) and w.shape == (H, 512, 128)
+    assert g.shape == (T, H * 128)
+    tot = None if totals is None else np.ascontiguousarray(totals, dtype=np.int32)
+    out = np.empty((T, H * 128), dtype=np.float64)
+    # element (h, k, v) of the [H, 512, 128] array: h * 512 * 128 + k * 128 + v; the oracle
+    # addresses it as h * stride_h + v * stride_v + k, so pass the transposed copy
+    wt = np.ascontiguousarray(np.transpose(w, (0, 2, 1)))  # [H, 128, 512]: k contiguous
+    _check(lib().oracle_mla_value(_ptr(x), _ptr(l2), S, T, H, _ptr(wt), 128 * 512, 512, _ptr(g),
+                                  _ptr(tot), int(rows_per_request), _ptr(out)))
+    return out

@@ -488,3 +488,90 @@ int oracle_lse_merge(const uint16_t *partials, const float *lse2,
     }
     return ORACLE_OK;
 }
+
+/* ---------------------------------------------------------------------------
+ * C4: the MLA value tail (the dcp page, DcpValue class docstring and its merge
+ * method; "as in MlaValue"): per row t and head h, the S sources' partials are
+ * LSE-merged as in C3 and rounded once to BF16 (the merged latent row); W_UV
+ * maps it to the head's 128 output values,
+ *     acc[v] = sum_{k < 512} latent[k] * W_UV[h][k][v],
+ * the product is rounded to BF16, multiplied by sigmoid(gate[t][h*128 + v]) =
+ * 1 / (1 + e^{-gate}) and rounded to BF16 again.  A row whose request total
+ * totals[t / rows_per_request] is <= 0 (a padded row, whose gate may be NaN)
+ * is written as zeros; totals == NULL makes every row live.
+ * partials: BF16 bits [S, T, H, 512]; lse2: [S, T, H] base 2; w_uv: BF16 bits,
+ * element (h, k, v) at w_uv[h * w_stride_h + v * w_stride_v + k]; gate: BF16
+ * bits [T, H * 128]; out: [T, H * 128] doubles, each exactly a BF16 value.
+ * ------------------------------------------------------------------------- */
+
+/* BF16 of x, round to nearest even: 8 significant bits for normal values, the fixed quantum
+ * 2^-133 below 2^-126; zeros, infinities and NaN pass through. */
+static double bf16_round(double x)
+{
+    int e;
+    double m;
+    if (x == 0.0 || isnan(x) || isinf(x))
+        return x;
+    if (fabs(x) < ldexp(1.0, -126))
+        return ldexp(nearbyint(ldexp(x, 133)), -133);
+    m = frexp(x, &e); /* x = m 2^e, 1/2 <= |m| < 1 */
+    return ldexp(nearbyint(ldexp(m, 8)), e - 8);
+}
+
+int oracle_mla_value(const uint16_t *partials, const float *lse2, int32_t S, int32_t T,
+                     int32_t H, const uint16_t *w_uv, int64_t w_stride_h, int64_t w_stride_v,
+                     const uint16_t *gate, const int32_t *totals, int32_t rows_per_request,
+                     double *out)
+{
+    double latent[V_DIM];
+    if (!partials || !lse2 || !w_uv || !gate || !out || S < 1 || T < 0 || H < 1 ||
+        rows_per_request < 1)
+        return ORACLE_EBADARG;
+    for (int t = 0; t < T; t++) {
+        int live = !totals || totals[t / rows_per_request] > 0;
+        for (int h = 0; h < H; h++) {
+            int64_t th = (int64_t)t * H + h;
+            double top = -INFINITY, total = 0.0;
+            double *o = out + th * 128;
+            for (int j = 0; j < V_DIM; j++)
+                latent[j] = 0.0;
+            for (int s = 0; s < S; s++) {
+                double v = (double)lse2[(int64_t)s * T * H + th];
+                if (isfinite(v) && v > top)
+                    top = v;
+            }
+            if (top != -INFINITY) {
+                for (int s = 0; s < S; s++) {
+                    double v = (double)lse2[(int64_t)s * T * H + th];
+                    if (isfinite(v))
+                        total += exp2(v - top);
+                }
+                for (int s = 0; s < S; s++) {
+                    double v = (double)lse2[(int64_t)s * T * H + th];
+                    const uint16_t *x = partials + ((int64_t)s * T * H + th) * V_DIM;
+                    double w;
+                    if (!isfinite(v))
+                        continue;
+                    w = exp2(v - top) / total;
+                    for (int j = 0; j < V_DIM; j++)
+                        latent[j] += w * oracle_bf16_value(x[j]);
+                }
+            }
+            for (int j = 0; j < V_DIM; j++)
+                latent[j] = bf16_round(latent[j]);
+            for (int v = 0; v < 128; v++) {
+                double acc = 0.0, g, sig;
+                if (!live) {
+                    o[v] = 0.0;
+                    continue;
+                }
+                for (int k = 0; k < V_DIM; k++)
+                    acc += latent[k] * oracle_bf16_value(w_uv[h * w_stride_h + v * w_stride_v + k]);
+                g = oracle_bf16_value(gate[(int64_t)t * H * 128 + h * 128 + v]);
+                sig = 1.0 / (1.0 + exp(-g));
+                o[v] = bf16_round(bf16_round(acc) * sig);
+            }
+        }
+    }
+    return ORACLE_OK;
+}

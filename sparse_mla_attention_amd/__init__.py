@@ -65,6 +65,8 @@ def _load():
                                             I32, I32, I32, F, F, P, P, P, U32,
                                             ctypes.POINTER(Plan), P]
     L.sparse_mla_decode_noalloc.restype = I32
+    L.mla_value.argtypes = [P, P, I32, I32, I32, P, I64, I64, P, P, I32, P, U32, P]
+    L.mla_value.restype = I32
     L.smla_testing_set_merge_wait.argtypes = [I32, I32]
     L.smla_testing_set_merge_wait.restype = I32
     _lib = L
@@ -208,6 +210,20 @@ def prepare_decode(q, kv_a, indices, lens, bmm1_scale, bmm2_scale, out, lse=None
         return keep[4], keep[5]
 
     return launch
+
+
+def mla_value(partials, lse2, w_uv, gate, out, *, totals=None, rows_per_request=1, stream=None):
+    """partials bf16 [S, T, H, 512]; lse2 float32 [S, T, H] (base 2); w_uv bf16 viewed as
+    [H, 512, 128] with unit latent stride (e.g. a transposed view of a [H, 128, 512] tensor);
+    gate bf16 [T, H * 128]; out bf16 [T, H * 128]; totals int32 per request or None."""
+    S, T, H, D = partials.shape
+    assert D == 512 and tuple(w_uv.shape) == (H, 512, 128) and w_uv.stride(1) == 1
+    st = _load().mla_value(_ptr(partials), _ptr(lse2), S, T, H, _ptr(w_uv), w_uv.stride(0),
+                           w_uv.stride(2), _ptr(gate), _ptr(totals), rows_per_request, _ptr(out),
+                           0, _stream(stream))
+    if st != SMLA_OK:
+        raise SmlaError(st, "mla_value")
+    return out
 
 
 def lse_merge(partials, lse2, out, lse_out=None, *, lse_log2=False, stream=None):

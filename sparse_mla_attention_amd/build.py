@@ -12,7 +12,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(BUILD, "libsmla.so")
 SOURCES = ["smla_api.hip", "smla_decode.hip", "smla_decode_g64.hip", "smla_lse_merge.hip",
-           "smla_noalloc.hip"]
+           "smla_noalloc.hip", "smla_value.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -313,6 +313,39 @@ smla_status sparse_mla_decode(const void *q, int64_t q_stride_t, int64_t q_strid
                              stream);
 }
 
+smla_status mla_value(const void *partials, const float *lse2, int32_t S, int32_t T, int32_t H,
+                      const void *w_uv, int64_t w_stride_h, int64_t w_stride_v, const void *gate,
+                      const int32_t *totals, int32_t rows_per_request, void *out, uint32_t flags,
+                      hipStream_t stream)
+{
+    if (S < 1 || S > 64 || T < 0 || H < 1 || rows_per_request < 1 || flags != 0)
+        return SMLA_EINVAL;
+    if (w_stride_h < 0 || w_stride_v < 0 || (w_stride_h & 7) || (w_stride_v & 7))
+        return SMLA_EINVAL;
+    if (T == 0)  // empty tensors may have null data pointers
+        return SMLA_OK;
+    if (partials == nullptr || lse2 == nullptr || w_uv == nullptr || gate == nullptr ||
+        out == nullptr)
+        return SMLA_EINVAL;
+    if (!aligned16(partials) || !aligned16(w_uv) || !aligned4(lse2) ||
+        ((uintptr_t)gate & 1u) || ((uintptr_t)out & 1u) || (totals != nullptr && !aligned4(totals)))
+        return SMLA_EINVAL;
+    smla::ValueParams p;
+    p.partials = static_cast<const uint16_t *>(partials);
+    p.lse2 = lse2;
+    p.S = S;
+    p.T = T;
+    p.H = H;
+    p.w_uv = static_cast<const uint16_t *>(w_uv);
+    p.w_sh = w_stride_h;
+    p.w_sv = w_stride_v;
+    p.gate = static_cast<const uint16_t *>(gate);
+    p.totals = totals;
+    p.rows_per_request = rows_per_request;
+    p.out = static_cast<uint16_t *>(out);
+    return smla::launch_mla_value(p, stream) == hipSuccess ? SMLA_OK : SMLA_EHIP;
+}
+
 smla_status smla_testing_set_merge_wait(int32_t max_polls, int32_t unreachable)
 {
     if (max_polls < 0 || (unreachable != 0 && unreachable != 1))

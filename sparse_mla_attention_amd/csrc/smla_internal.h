@@ -58,6 +58,21 @@ struct LseMergeParams {
 
 hipError_t launch_lse_merge(const LseMergeParams &p, hipStream_t stream);
 
+// One mla_value launch: the split merge of S sources, W_UV and the sigmoid gate.
+struct ValueParams {
+    const uint16_t *partials;   // BF16 [S, T, H, 512]
+    const float *lse2;          // [S, T, H] base 2
+    int32_t S, T, H;
+    const uint16_t *w_uv;       // BF16, element (h, k, v) at h * w_sh + v * w_sv + k
+    int64_t w_sh, w_sv;         // strides in elements
+    const uint16_t *gate;       // BF16 [T, H * 128]
+    const int32_t *totals;      // per request, or null (every row live)
+    int32_t rows_per_request;
+    uint16_t *out;              // BF16 [T, H * 128]
+};
+
+hipError_t launch_mla_value(const ValueParams &p, hipStream_t stream);
+
 // Bytes at the start of a workspace under `plan` that must be zero before a call: the status
 // word and the arrival counters, padded to 256.
 size_t workspace_header_bytes(const smla_plan *plan, int32_t T, int32_t H);

@@ -2,10 +2,10 @@
 // valid sources (finite base-2 LSE) are weighted by 2^(lse_s - top) / sum_r 2^(lse_r - top),
 // their BF16 rows summed in FP32 and rounded to BF16 once; no valid source gives +0 and -inf.
 //
-// Pure HBM streaming: one thread per 8 columns (one 16-byte load per source, one 16-byte
-// store).  The per-unit weights are computed once per thread from the S LSE values (a few
-// L1-resident floats shared by the D/8 threads of the unit); the source loads of a thread are
-// independent and issued back to back.
+// Pure HBM streaming.  One wave per (token, head) unit: the unit's S LSEs and weights are the
+// same for all its lanes (scalar loads, computed once), and each lane takes 16-byte runs of 8
+// columns, issuing the loads of a block of up to 8 valid sources back to back before summing
+// them in source order; one 16-byte store per run.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -30,91 +30,90 @@ __device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0
 // NaN and +-inf both mark an empty source.
 __device__ inline bool valid_lse(float x) { return __builtin_isfinite(x); }
 
-template <int SMAX>
-__global__ void __launch_bounds__(256) lse_merge_kernel(LseMergeParams p)
+constexpr int WAVES = 4;   // units per workgroup
+constexpr int SB = 8;      // sources loaded together
+
+__global__ void __launch_bounds__(64 * WAVES) lse_merge_kernel(LseMergeParams p)
 {
-    const int per_unit = p.D / 8;
-    const int64_t total = (int64_t)p.T * p.H * per_unit;
+    const int lane = threadIdx.x & 63;
+    const int64_t unit = (int64_t)blockIdx.x * WAVES +
+                         __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t TH = (int64_t)p.T * p.H;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-         i += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t unit = i / per_unit;
-        const int k = (int)(i - unit * per_unit);
-        float top = -INFINITY;
-        for (int s = 0; s < p.S; s++) {
-            const float l = p.lse2[s * TH + unit];
-            if (valid_lse(l))
-                top = fmaxf(top, l);
-        }
-        uint4 res = make_uint4(0, 0, 0, 0);
-        if (top != -INFINITY) {
-            float w[SMAX];
-            float sum = 0.0f;
-#pragma unroll
-            for (int s = 0; s < SMAX; s++) {
-                w[s] = 0.0f;
-                if (s < p.S) {
-                    const float l = p.lse2[s * TH + unit];
-                    w[s] = valid_lse(l) ? exp2f(l - top) : 0.0f;
-                    sum += w[s];
-                }
-            }
-            float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-            const uint4 *src = reinterpret_cast<const uint4 *>(p.partials) + unit * per_unit + k;
-#pragma unroll
-            for (int s = 0; s < SMAX; s++) {
-                if (s < p.S && w[s] != 0.0f) {
-                    const float scale = w[s] / sum;
-                    const uint4 x = src[s * TH * per_unit];
-                    acc[0] += scale * bf16_lo(x.x);
-                    acc[1] += scale * bf16_hi(x.x);
-                    acc[2] += scale * bf16_lo(x.y);
-                    acc[3] += scale * bf16_hi(x.y);
-                    acc[4] += scale * bf16_lo(x.z);
-                    acc[5] += scale * bf16_hi(x.z);
-                    acc[6] += scale * bf16_lo(x.w);
-                    acc[7] += scale * bf16_hi(x.w);
-                }
-            }
-            res.x = bf16_bits(acc[0]) | (bf16_bits(acc[1]) << 16);
-            res.y = bf16_bits(acc[2]) | (bf16_bits(acc[3]) << 16);
-            res.z = bf16_bits(acc[4]) | (bf16_bits(acc[5]) << 16);
-            res.w = bf16_bits(acc[6]) | (bf16_bits(acc[7]) << 16);
-            if (k == 0 && p.lse_out != nullptr) {
-                const float lse2 = top + log2f(sum);
-                p.lse_out[unit] = p.lse_log2 ? lse2 : lse2 * LN2;
-            }
-        } else if (k == 0 && p.lse_out != nullptr) {
+    if (unit >= TH)
+        return;
+    const int per_unit = p.D / 8;
+    // the unit's weights (wave-uniform): top over the valid sources, 2^(lse - top) / sum
+    float top = -INFINITY;
+    for (int s = 0; s < p.S; s++) {
+        const float l = p.lse2[s * TH + unit];
+        if (valid_lse(l))
+            top = fmaxf(top, l);
+    }
+    if (top == -INFINITY) {  // no valid source: +0 and -inf
+        for (int k = lane; k < per_unit; k += 64)
+            reinterpret_cast<uint4 *>(p.out)[unit * per_unit + k] = make_uint4(0, 0, 0, 0);
+        if (lane == 0 && p.lse_out != nullptr)
             p.lse_out[unit] = -INFINITY;
+        return;
+    }
+    float sum = 0.0f;
+    for (int s = 0; s < p.S; s++) {
+        const float l = p.lse2[s * TH + unit];
+        sum += valid_lse(l) ? exp2f(l - top) : 0.0f;
+    }
+    const float inv = 1.0f / sum;
+    const uint4 *src = reinterpret_cast<const uint4 *>(p.partials) + unit * per_unit;
+    for (int k = lane; k < per_unit; k += 64) {
+        float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        for (int s0 = 0; s0 < p.S; s0 += SB) {
+            uint4 x[SB];
+            float wgt[SB];
+#pragma unroll
+            for (int j = 0; j < SB; j++) {
+                const int s = s0 + j;
+                const float l = s < p.S ? p.lse2[s * TH + unit] : -INFINITY;
+                wgt[j] = valid_lse(l) ? exp2f(l - top) * inv : 0.0f;
+                x[j] = make_uint4(0, 0, 0, 0);
+                if (wgt[j] != 0.0f)  // wave-uniform; an empty source is never read
+                    x[j] = src[s * TH * per_unit + k];
+            }
+#pragma unroll
+            for (int j = 0; j < SB; j++) {
+                acc[0] += wgt[j] * bf16_lo(x[j].x);
+                acc[1] += wgt[j] * bf16_hi(x[j].x);
+                acc[2] += wgt[j] * bf16_lo(x[j].y);
+                acc[3] += wgt[j] * bf16_hi(x[j].y);
+                acc[4] += wgt[j] * bf16_lo(x[j].z);
+                acc[5] += wgt[j] * bf16_hi(x[j].z);
+                acc[6] += wgt[j] * bf16_lo(x[j].w);
+                acc[7] += wgt[j] * bf16_hi(x[j].w);
+            }
         }
+        uint4 res;
+        res.x = bf16_bits(acc[0]) | (bf16_bits(acc[1]) << 16);
+        res.y = bf16_bits(acc[2]) | (bf16_bits(acc[3]) << 16);
+        res.z = bf16_bits(acc[4]) | (bf16_bits(acc[5]) << 16);
+        res.w = bf16_bits(acc[6]) | (bf16_bits(acc[7]) << 16);
         reinterpret_cast<uint4 *>(p.out)[unit * per_unit + k] = res;
     }
-}
-
-template <int SMAX>
-hipError_t launch_smax(const LseMergeParams &p, hipStream_t stream)
-{
-    const int64_t total = (int64_t)p.T * p.H * (p.D / 8);
-    int64_t blocks = (total + 255) / 256;
-    if (blocks > 65536)
-        blocks = 65536;
-    hipLaunchKernelGGL(lse_merge_kernel<SMAX>, dim3((unsigned)blocks), dim3(256), 0, stream, p);
-    return hipGetLastError();
+    if (lane == 0 && p.lse_out != nullptr) {
+        const float lse2 = top + log2f(sum);
+        p.lse_out[unit] = p.lse_log2 ? lse2 : lse2 * LN2;
+    }
 }
 
 }  // namespace
 
 hipError_t launch_lse_merge(const LseMergeParams &p, hipStream_t stream)
 {
-    if (p.S <= 4)
-        return launch_smax<4>(p, stream);
-    if (p.S <= 8)
-        return launch_smax<8>(p, stream);
-    if (p.S <= 16)
-        return launch_smax<16>(p, stream);
-    if (p.S <= MAX_SOURCES)
-        return launch_smax<MAX_SOURCES>(p, stream);
-    return hipErrorInvalidValue;
+    if (p.S > MAX_SOURCES)
+        return hipErrorInvalidValue;
+    const int64_t units = (int64_t)p.T * p.H;
+    const int64_t blocks = (units + WAVES - 1) / WAVES;
+    if (blocks > 0x7FFFFFFF)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(lse_merge_kernel, dim3((unsigned)blocks), dim3(64 * WAVES), 0, stream, p);
+    return hipGetLastError();
 }
 
 }  // namespace smla

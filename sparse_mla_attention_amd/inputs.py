@@ -287,3 +287,22 @@ CONFIGS = {
     "verify": config_verify,
     "dsv4": config_dsv4,
 }
+
+
+def value_problem(seed: int, S: int, T: int, H: int, empty_frac: float = 0.1,
+                  padded_requests: int = 0, rows_per_request: int = 1) -> dict:
+    """Inputs of the MLA value tail: the split partials and LSEs of random_merge, a BF16 W_UV
+    stored [H, 128, 512] (latent-contiguous; N(0,1)/16, so the 512-term products are unit
+    scale), BF16 gates N(0, 2^2) [T, H*128], and per-request totals (the first
+    `padded_requests` requests are padding: total 0, their gates NaN)."""
+    m = random_merge(seed, S, T, H, 512, empty_frac=empty_frac)
+    rng = np.random.default_rng(seed + 1)
+    w_t = bf16_bits(rng.standard_normal((H, 128, 512)).astype(np.float32) / 16.0)
+    gate = bf16_bits((2.0 * rng.standard_normal((T, H * 128))).astype(np.float32))
+    nreq = -(-T // rows_per_request)
+    totals = rng.integers(1, 4096, size=nreq).astype(np.int32)
+    totals[:padded_requests] = 0
+    for r in range(padded_requests):
+        gate[r * rows_per_request:(r + 1) * rows_per_request] = NAN_BF16
+    return dict(name=f"value{seed}", partials=m["partials"], lse=m["lse"], w_uv_t=w_t,
+                gate=gate, totals=totals, rows_per_request=rows_per_request)

@@ -459,3 +459,82 @@ def test_dominant_sink_does_not_overflow():
     om, lm = oracle.decode_mimic(p, 2, 8, terms=1)
     np.testing.assert_allclose(lm, 800.0, rtol=1e-12)
     assert np.all(np.isfinite(om)) and np.abs(om).max() < 1e-300
+
+
+# ---------------------------------------------------------------------------
+# mla_value: LSE merge, W_UV and the sigmoid gate (dcp page, DcpValue.merge)
+# ---------------------------------------------------------------------------
+
+def _bf16(x):
+    return torch.as_tensor(np.asarray(x, np.float32)).to(torch.bfloat16)
+
+
+def _bits(t):
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def _value_problem(seed, S, T, H, empty_frac=0.2):
+    m = inputs.random_merge(seed, S, T, H, 512, empty_frac=empty_frac)
+    rng = np.random.default_rng(seed + 1)
+    w = _bits(_bf16(rng.standard_normal((H, 512, 128)) / 16.0))
+    g = _bits(_bf16(rng.standard_normal((T, H * 128)) * 2.0))
+    return m["partials"], m["lse"], w, g
+
+
+def test_mla_value_matches_torch_float64():
+    """The merge weights, the BF16 latent, a float64 matmul with W_UV, BF16, times torch's
+    sigmoid of the gate, BF16 (torch on the CPU, independent of the oracle's loops): equal up
+    to one BF16 step where torch's float64 -> BF16 cast rounds twice (through float32)."""
+    x, l2, w, g = _value_problem(800, 3, 5, 4)
+    got = oracle.mla_value(x, l2, w, g)
+    xs = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).double()  # [S,T,H,512]
+    ls = torch.from_numpy(l2).double()
+    fin = torch.isfinite(ls)
+    top = torch.where(fin, ls, torch.tensor(-np.inf, dtype=torch.float64)).amax(0)
+    wts = torch.where(fin, torch.exp2(ls - top), torch.zeros_like(ls))
+    wts = wts / wts.sum(0).clamp_min(1e-300)
+    lat = (wts[..., None] * torch.nan_to_num(xs)).sum(0).to(torch.bfloat16).double()
+    W = torch.from_numpy(w.view(np.int16)).view(torch.bfloat16).double()   # [H,512,128]
+    acc = torch.einsum("thk,hkv->thv", lat, W)
+    G = torch.from_numpy(g.view(np.int16)).view(torch.bfloat16).double().reshape(5, 4, 128)
+    ref = (acc.to(torch.bfloat16).double() * torch.sigmoid(G)).to(torch.bfloat16).double()
+    ref = ref.reshape(5, 512).numpy()
+    diff = np.abs(got - ref)
+    step = np.abs(ref) * 2.0 ** -7 + 1e-30
+    assert np.all(diff <= step)
+    assert (diff == 0).mean() > 0.99
+
+
+def test_mla_value_selection_weights_and_gates_in_closed_form():
+    """W_UV picking latent column v + 32 h for value v (one product with 1) reproduces the merged
+    BF16 latent; a gate of 30 (sigmoid 1 - 9e-14) leaves it unchanged after BF16 rounding, a
+    gate of 0 halves it exactly.  One source with a finite LSE merges to itself."""
+    S, T, H = 1, 3, 2
+    rng = np.random.default_rng(801)
+    x = _bits(_bf16(rng.standard_normal((S, T, H, 512))))
+    l2 = np.full((S, T, H), 3.5, np.float32)
+    w = np.zeros((H, 512, 128), np.uint16)
+    one = _bits(_bf16([1.0]))[0]
+    for h in range(H):
+        w[h, np.arange(128) + 32 * h, np.arange(128)] = one
+    xv = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).double().numpy()[0]
+    for gval, factor in ((30.0, 1.0), (0.0, 0.5)):
+        g = _bits(_bf16(np.full((T, H * 128), gval)))
+        got = oracle.mla_value(x, l2, w, g).reshape(T, H, 128)
+        for h in range(H):
+            np.testing.assert_array_equal(got[:, h], xv[:, h, 32 * h:32 * h + 128] * factor)
+
+
+def test_mla_value_padded_rows_are_zero_and_empty_sources_merge_to_zero():
+    """Rows of a request whose total is 0 are zeros even when their gate is NaN (two rows per
+    request here); a live row whose sources are all empty merges to a zero latent, so its
+    values are 0 * sigmoid(gate) = 0."""
+    x, l2, w, g = _value_problem(802, 2, 6, 2, empty_frac=0.0)
+    totals = np.array([5, 0, 7], np.int32)             # rows 2, 3 padded
+    g[2:4] = _bits(_bf16([np.nan]))[0]
+    l2[:, 4, :] = -np.inf                               # row 4: every source empty
+    x[:, 4, :, :] = 0x7FC0                              # (never read)
+    out = oracle.mla_value(x, l2, w, g, totals=totals, rows_per_request=2)
+    assert np.all(out[2:4] == 0.0)
+    assert np.all(out[4] == 0.0)
+    assert np.all(np.isfinite(out)) and np.any(out[0] != 0.0)
