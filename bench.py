@@ -243,6 +243,34 @@ def value_leg(smla, inputs, replays):
             "timing": f"100 calls in one HIP graph, median of {replays} replays"}
 
 
+def paged_leg(smla, inputs, replays):
+    """paged_mla_decode (dense paged MLA decode on the same skeleton): B=32 requests, one q
+    row each, H=128, 4096-token contexts in 64-row pages (75.5 MB of KV gathered per call,
+    as the large sparse batch); us per call and gathered GB/s, two-term P, default plan."""
+    import torch
+    p = inputs.paged_problem(1030, 32, 1, 128, [4096] * 32, page_size=64, poison=False)
+    q, cache = torch.from_numpy(p["q"]).cuda(), torch.from_numpy(p["cache"]).cuda()
+    bt, lens = torch.from_numpy(p["block_table"]).cuda(), torch.from_numpy(p["lengths"]).cuda()
+    T, H = 32, 128
+    out = torch.empty((T, H, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    plan = smla.paged_plan_for(32, 1, H, p["block_table"].shape[1], 64)
+    ws = smla.new_workspace(plan, T, H)
+    t = graph_replays(lambda i, s: smla.paged_mla_decode(q, cache, bt, lens, 1, p["bmm1"],
+                                                         p["bmm2"], out, lse, plan=plan,
+                                                         workspace=ws, stream=s),
+                      20, replays)
+    us = statistics.median(t) * 1e3
+    gathered = 32 * 4096 * 576
+    gbs = gathered / (us * 1e-6) / 1e9
+    log(f"paged decode: {us:.2f} us, {gbs:.0f} GB/s")
+    return {"workload": "B=32 requests x 1 q row, H=128, 4096-token contexts, 64-row pages",
+            "plan": f"splits={plan.splits},tiles={plan.tiles}", "us_per_call": round(us, 2),
+            "gathered_bytes": gathered, "gathered_gbs": round(gbs, 1),
+            "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "timing": f"20 calls in one HIP graph, median of {replays} replays"}
+
+
 def cpu_info():
     model = "unknown"
     try:
@@ -397,6 +425,7 @@ def main():
     if not args.no_merge:
         result["lse_merge"] = merge_leg(smla, inputs, args.replays)
         result["mla_value"] = value_leg(smla, inputs, args.replays)
+        result["paged_decode"] = paged_leg(smla, inputs, args.replays)
     if not args.no_cpu_baseline:
         log("CPU oracle baseline")
         result["cpu_baseline"] = cpu_baseline(w, sets[0].cpu().numpy(), args.cpu_seconds)

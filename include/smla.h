@@ -205,6 +205,44 @@ smla_status lse_merge(const void *partials, const float *lse2, int32_t S, int32_
                       int32_t D, void *out, float *lse_out, uint32_t flags, hipStream_t stream);
 
 /*
+ * paged_mla_decode -- dense paged MLA decode (the dcp page, stock_decode: the FP8 cache in pages
+ * addressed through a block table, the q rows of a request masked causally, caller-owned out
+ * and LSE, a split-KV workspace sized before capture), on the gather and matrix skeleton of
+ * sparse_mla_decode: row t = b * q_len + i (request b's i-th of q_len rows) attends over the
+ * first n_t = clamp(lengths[b] - (q_len - 1 - i), 0, max_pages * page_size) keys of request b's
+ * context, key k being row k % page_size of page block_table[b][k / page_size]; the score,
+ * softmax recipe, split merge, outputs and flags are sparse_mla_decode's with one pool, no
+ * sink and qk_dim = row_bytes = 576 (V the first 512 bytes of a row).
+ *
+ *   q            device, E4M3 [B * q_len, H, 576] with byte strides q_stride_t, q_stride_h
+ *                (multiples of 16; 16-byte aligned).
+ *   cache        device, E4M3 pages: row r of page g at cache + g * page_stride + r * 576
+ *                (page_stride >= page_size * 576, a multiple of 16; 16-byte aligned).
+ *   num_pages    pages in the cache: every block_table entry a row reads must be in [0,
+ *                num_pages) (precondition, not checked); entries past a request's context
+ *                are never read.
+ *   block_table  device int32 [B, max_pages].
+ *   lengths      device int32 [B]: context lengths (the q_len new rows included).
+ *   out, lse     device BF16 [B * q_len, H, 512] and float32 [B * q_len, H] (or NULL).
+ *   plan         NULL for smla_paged_decode_plan's, else one with tiles = 2 (64 heads per
+ *                workgroup; SMLA_EUNSUPPORTED otherwise) and ranges of at most 2048 keys.
+ *   workspace    as sparse_mla_decode, sized by smla_decode_workspace_size(plan, B * q_len, H).
+ * Errors as sparse_mla_decode.
+ */
+smla_status paged_mla_decode(const void *q, int64_t q_stride_t, int64_t q_stride_h,
+                             const void *cache, int64_t num_pages, int32_t page_size,
+                             int64_t page_stride, const int32_t *block_table, int32_t max_pages,
+                             const int32_t *lengths, int32_t B, int32_t q_len, int32_t H,
+                             float bmm1_scale, float bmm2_scale, void *out, float *lse,
+                             uint32_t flags, const smla_plan *plan, void *workspace,
+                             size_t workspace_bytes, hipStream_t stream);
+
+/* The plan paged_mla_decode uses when given none: 64 heads per workgroup, key ranges as
+ * smla_decode_plan over the max_pages * page_size columns (at least ceil(columns / 2048)). */
+smla_status smla_paged_decode_plan(int32_t B, int32_t q_len, int32_t H, int32_t max_pages,
+                                   int32_t page_size, uint32_t flags, smla_plan *plan);
+
+/*
  * mla_value -- the MLA value tail after the split merge (dcp page, DcpValue class docstring and
  * its merge method: the owner's LSE merge over the sources, then W_UV and the sigmoid gate "as
  * in MlaValue").  With S = 1 it is the value tail of sparse_mla_decode's own output (pass its

@@ -67,6 +67,9 @@ def lib():
         L.oracle_decode_mimic.restype = ctypes.c_int
         L.oracle_lse_merge.argtypes = [P, P, I32, I32, I32, I32, U32, P, P]
         L.oracle_lse_merge.restype = ctypes.c_int
+        L.oracle_paged_decode_exact.argtypes = [P, I64, I64, P, I64, I32, I64, P, I32, P, I32,
+                                                I32, I32, D, D, U32, P, I32, P, P]
+        L.oracle_paged_decode_exact.restype = ctypes.c_int
         L.oracle_mla_value.argtypes = [P, P, I32, I32, I32, P, I64, I64, P, P, I32, P]
         L.oracle_mla_value.restype = ctypes.c_int
         _lib = L
@@ -185,3 +188,30 @@ def mla_value(partials_bits, lse2, w_uv_bits, gate_bits, totals=None, rows_per_r
     _check(lib().oracle_mla_value(_ptr(x), _ptr(l2), S, T, H, _ptr(wt), 128 * 512, 512, _ptr(g),
                                   _ptr(tot), int(rows_per_request), _ptr(out)))
     return out
+
+
+def paged_decode_exact(p, lse_log2=False, units=None):
+    """Dense paged MLA decode (the dcp page's stock_decode), exact FP64: p holds q [B*q_len, H,
+    576] E4M3 bytes, cache [num_pages, page_size, 576] bytes, block_table [B, max_pages] int32,
+    lengths [B] int32, q_len, bmm1, bmm2.  Returns (out [n, 512], lse [n]) for every (t, h) or
+    the given (t, h) pairs."""
+    q = np.ascontiguousarray(p["q"], dtype=np.uint8)
+    cache = np.ascontiguousarray(p["cache"], dtype=np.uint8)
+    bt = np.ascontiguousarray(p["block_table"], dtype=np.int32)
+    lens = np.ascontiguousarray(p["lengths"], dtype=np.int32)
+    T, H, qd = q.shape
+    assert qd == 576
+    num_pages, page_size, rb = cache.shape
+    assert rb == 576
+    B, max_pages = bt.shape
+    q_len = int(p["q_len"])
+    assert T == B * q_len
+    u, n = _units_array(units)
+    count = n if u is not None else T * H
+    out = np.empty((count, 512), dtype=np.float64)
+    lse = np.empty((count,), dtype=np.float64)
+    _check(lib().oracle_paged_decode_exact(
+        _ptr(q), H * 576, 576, _ptr(cache), num_pages, page_size, page_size * 576, _ptr(bt),
+        max_pages, _ptr(lens), B, q_len, H, float(p["bmm1"]), float(p["bmm2"]),
+        LSE_LOG2 if lse_log2 else 0, _ptr(u), n, _ptr(out), _ptr(lse)))
+    return out, lse

@@ -575,3 +575,100 @@ int oracle_mla_value(const uint16_t *partials, const float *lse2, int32_t S, int
     }
     return ORACLE_OK;
 }
+
+/* ---------------------------------------------------------------------------
+ * C5: dense paged MLA decode (the dcp page, stock_decode: a paged FP8 cache
+ * addressed through a block table, the q rows of a request masked causally,
+ * caller-owned out and LSE).  Query row t = b * q_len + i (request b, its i-th
+ * of q_len rows) attends to the first n_t = clamp(lengths[b] - (q_len - 1 - i),
+ * 0, max_pages * page_size) keys of the request's context; key k lives in row
+ * k % page_size of page block_table[b][k / page_size], each row 576 bytes (512
+ * latent + 64 rope, V the first 512).  The score and the softmax are the
+ * sparse_mla_cute formula of C1 (no sink), the LSE natural or base 2; a row
+ * with n_t = 0 gives zeros and LSE -inf.
+ * q: [B * q_len, H, 576] (strides in bytes); cache: pages of page_stride bytes.
+ * out: [n_units, 512]; lse: [n_units]; units as in C1 (NULL: every (t, h)).
+ * ------------------------------------------------------------------------- */
+int oracle_paged_decode_exact(
+    const uint8_t *q, int64_t q_stride_t, int64_t q_stride_h,
+    const uint8_t *cache, int64_t num_pages, int32_t page_size, int64_t page_stride,
+    const int32_t *block_table, int32_t max_pages, const int32_t *lengths,
+    int32_t B, int32_t q_len, int32_t H, double bmm1, double bmm2, uint32_t flags,
+    const int32_t *units, int32_t n_units, double *out, double *lse)
+{
+    const int32_t T = B * q_len;
+    const int64_t width = (int64_t)max_pages * page_size;
+    int count = units ? n_units : T * H;
+    double *scores;
+    int status = ORACLE_OK;
+    if (!q || !cache || !block_table || !lengths || !out || !lse || B < 0 || q_len < 1 ||
+        H < 1 || page_size < 1 || max_pages < 1 || page_stride < (int64_t)page_size * 576)
+        return ORACLE_EBADARG;
+    scores = (double *)malloc(sizeof(double) * (size_t)(width > 0 ? width : 1));
+    if (!scores)
+        return ORACLE_EBADARG;
+    for (int u = 0; u < count && status == ORACLE_OK; u++) {
+        int t = units ? units[2 * u] : u / H;
+        int h = units ? units[2 * u + 1] : u % H;
+        int b, i;
+        int64_t n;
+        double m = -INFINITY, z = 0.0;
+        double *o = out + (int64_t)u * V_DIM;
+        const uint8_t *qr;
+        if (t < 0 || t >= T || h < 0 || h >= H) {
+            status = ORACLE_EBADARG;
+            break;
+        }
+        b = t / q_len;
+        i = t % q_len;
+        qr = q + (int64_t)t * q_stride_t + (int64_t)h * q_stride_h;
+        n = (int64_t)lengths[b] - (q_len - 1 - i); /* causal: row i sees one key more than i-1 */
+        if (n < 0)
+            n = 0;
+        if (n > width)
+            n = width;
+        for (int j = 0; j < V_DIM; j++)
+            o[j] = 0.0;
+        if (n == 0) {
+            lse[u] = -INFINITY;
+            continue;
+        }
+        for (int64_t k = 0; k < n; k++) {
+            int32_t page = block_table[(int64_t)b * max_pages + k / page_size];
+            const uint8_t *row;
+            double acc = 0.0;
+            if (page < 0 || page >= num_pages) {
+                status = ORACLE_ERANGE;
+                break;
+            }
+            row = cache + (int64_t)page * page_stride + (k % page_size) * 576;
+            for (int d = 0; d < 576; d++) {
+                double a = oracle_e4m3_value(qr[d]);
+                double c = oracle_e4m3_value(row[d]);
+                if (isnan(a) || isnan(c))
+                    status = ORACLE_ENAN;
+                acc += a * c;
+            }
+            scores[k] = bmm1 * acc;
+            if (scores[k] > m)
+                m = scores[k];
+        }
+        if (status != ORACLE_OK)
+            break;
+        for (int64_t k = 0; k < n; k++) {
+            int32_t page = block_table[(int64_t)b * max_pages + k / page_size];
+            const uint8_t *row = cache + (int64_t)page * page_stride + (k % page_size) * 576;
+            double w = exp(scores[k] - m);
+            z += w;
+            for (int j = 0; j < V_DIM; j++)
+                o[j] += w * oracle_e4m3_value(row[j]);
+        }
+        for (int j = 0; j < V_DIM; j++)
+            o[j] = bmm2 * o[j] / z;
+        lse[u] = m + log(z);
+        if (flags & ORACLE_LSE_LOG2)
+            lse[u] /= log(2.0);
+    }
+    free(scores);
+    return status;
+}

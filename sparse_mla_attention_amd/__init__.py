@@ -65,6 +65,11 @@ def _load():
                                             I32, I32, I32, F, F, P, P, P, U32,
                                             ctypes.POINTER(Plan), P]
     L.sparse_mla_decode_noalloc.restype = I32
+    L.paged_mla_decode.argtypes = [P, I64, I64, P, I64, I32, I64, P, I32, P, I32, I32, I32, F, F,
+                                   P, P, U32, ctypes.POINTER(Plan), P, SZ, P]
+    L.paged_mla_decode.restype = I32
+    L.smla_paged_decode_plan.argtypes = [I32, I32, I32, I32, I32, U32, ctypes.POINTER(Plan)]
+    L.smla_paged_decode_plan.restype = I32
     L.mla_value.argtypes = [P, P, I32, I32, I32, P, I64, I64, P, P, I32, P, U32, P]
     L.mla_value.restype = I32
     L.smla_testing_set_merge_wait.argtypes = [I32, I32]
@@ -210,6 +215,39 @@ def prepare_decode(q, kv_a, indices, lens, bmm1_scale, bmm2_scale, out, lse=None
         return keep[4], keep[5]
 
     return launch
+
+
+def paged_plan_for(B: int, q_len: int, H: int, max_pages: int, page_size: int,
+                   flags: int = 0) -> Plan:
+    p = Plan()
+    st = _load().smla_paged_decode_plan(B, q_len, H, max_pages, page_size, flags, ctypes.byref(p))
+    if st != SMLA_OK:
+        raise SmlaError(st, "smla_paged_decode_plan")
+    return p
+
+
+def paged_mla_decode(q, cache, block_table, lengths, q_len, bmm1_scale, bmm2_scale, out,
+                     lse=None, *, lse_log2=False, one_term=False, plan=None, workspace=None,
+                     stream=None):
+    """Dense paged MLA decode: q uint8 [B*q_len, H, 576]; cache uint8 [num_pages, page_size,
+    576] (any page stride, unit row layout); block_table int32 [B, max_pages]; lengths int32
+    [B]; out bf16 [B*q_len, H, 512]; lse float32 [B*q_len, H] or None."""
+    T, H, qd = q.shape
+    num_pages, page_size, rb = cache.shape
+    B, max_pages = block_table.shape
+    assert qd == 576 and rb == 576 and T == B * q_len
+    assert cache.stride(2) == 1 and cache.stride(1) == 576
+    flags = (SMLA_LSE_LOG2 if lse_log2 else 0) | (SMLA_P_ONE_TERM if one_term else 0)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = _load().paged_mla_decode(
+        _ptr(q), q.stride(0) * q.element_size(), q.stride(1) * q.element_size(), _ptr(cache),
+        num_pages, page_size, cache.stride(0) * cache.element_size(), _ptr(block_table),
+        max_pages, _ptr(lengths), B, q_len, H, float(bmm1_scale), float(bmm2_scale), _ptr(out),
+        _ptr(lse), flags, None if plan is None else ctypes.byref(plan), _ptr(workspace),
+        ws_bytes, _stream(stream))
+    if st != SMLA_OK:
+        raise SmlaError(st, "paged_mla_decode")
+    return out, lse
 
 
 def mla_value(partials, lse2, w_uv, gate, out, *, totals=None, rows_per_request=1, stream=None):

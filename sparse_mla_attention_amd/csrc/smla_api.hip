@@ -246,7 +246,7 @@ smla_status decode_impl(const void *q, int64_t q_stride_t, int64_t q_stride_h,
         return SMLA_EWORKSPACE;
 
     // ---- launch ------------------------------------------------------------------------
-    smla::DecodeParams p;
+    smla::DecodeParams p{};  // zero: every field not set below (the paged mode among them)
     p.q = static_cast<const uint8_t *>(q);
     p.q_st = q_stride_t;
     p.q_sh = q_stride_h;
@@ -311,6 +311,116 @@ smla_status sparse_mla_decode(const void *q, int64_t q_stride_t, int64_t q_strid
                              row_bytes, qk_dim, indices, lens, T, H, W, bmm1_scale, bmm2_scale,
                              sinks, out, lse, flags, plan, workspace, workspace_bytes, false,
                              stream);
+}
+
+smla_status smla_paged_decode_plan(int32_t B, int32_t q_len, int32_t H, int32_t max_pages,
+                                   int32_t page_size, uint32_t flags, smla_plan *plan)
+{
+    if (plan == nullptr || B < 0 || q_len < 1 || H <= 0 || H % 16 != 0 || max_pages < 1 ||
+        page_size < 1 || (int64_t)max_pages * page_size > 0x7FFFFFFF)
+        return SMLA_EINVAL;
+    if (flags & ~(SMLA_LSE_LOG2 | SMLA_P_ONE_TERM))
+        return SMLA_EINVAL;
+    int cus = 0;
+    if (current_cu_count(&cus) != hipSuccess)
+        return SMLA_EHIP;
+    const int32_t W = max_pages * page_size;
+    plan->tiles = 2;
+    plan->splits = default_splits(B * q_len, head_groups(H, 2), W, cus, 2);
+    if (plan->splits > kMaxSplits)
+        return SMLA_EUNSUPPORTED;
+    plan->chunk = kChunk;
+    plan->reserved = 0;
+    return SMLA_OK;
+}
+
+smla_status paged_mla_decode(const void *q, int64_t q_stride_t, int64_t q_stride_h,
+                             const void *cache, int64_t num_pages, int32_t page_size,
+                             int64_t page_stride, const int32_t *block_table, int32_t max_pages,
+                             const int32_t *lengths, int32_t B, int32_t q_len, int32_t H,
+                             float bmm1_scale, float bmm2_scale, void *out, float *lse,
+                             uint32_t flags, const smla_plan *plan, void *workspace,
+                             size_t workspace_bytes, hipStream_t stream)
+{
+    if (B < 0 || q_len < 1 || H <= 0 || H % 16 != 0 || max_pages < 1 || page_size < 1 ||
+        num_pages < 1 || (int64_t)max_pages * page_size > 0x7FFFFFFF ||
+        (int64_t)B * q_len > 0x7FFFFFFF)
+        return SMLA_EINVAL;
+    if (flags & ~(SMLA_LSE_LOG2 | SMLA_P_ONE_TERM))
+        return SMLA_EINVAL;
+    if (!isfinite(bmm1_scale) || !isfinite(bmm2_scale))
+        return SMLA_EINVAL;
+    if (page_stride < (int64_t)page_size * 576 || (page_stride & 15))
+        return SMLA_EINVAL;
+    smla_plan chosen;
+    if (plan != nullptr) {
+        if (!plan_ok(plan, H))
+            return SMLA_EINVAL;
+        chosen = *plan;
+    } else {
+        const smla_status st = smla_paged_decode_plan(B, q_len, H, max_pages, page_size, flags,
+                                                      &chosen);
+        if (st != SMLA_OK)
+            return st;
+    }
+    if (chosen.tiles != 2)
+        return SMLA_EUNSUPPORTED;  // the paged mode is built into the 64-head kernel
+    const int32_t W = max_pages * page_size;
+    if ((W + chosen.splits - 1) / chosen.splits > smla::G64_MAX_RANGE)
+        return SMLA_EUNSUPPORTED;
+    const int32_t T = B * q_len;
+    if (T == 0)
+        return SMLA_OK;
+    if (q == nullptr || cache == nullptr || block_table == nullptr || lengths == nullptr ||
+        out == nullptr)
+        return SMLA_EINVAL;
+    if (!aligned16(q) || (q_stride_t & 15) || (q_stride_h & 15) || q_stride_t < 0 ||
+        q_stride_h < 0 || !aligned16(cache) || !aligned16(out) || !aligned4(block_table) ||
+        !aligned4(lengths) || (lse != nullptr && !aligned4(lse)))
+        return SMLA_EINVAL;
+    const size_t need = smla_decode_workspace_size(&chosen, T, H);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
+        return SMLA_EWORKSPACE;
+
+    smla::DecodeParams p{};
+    p.q = static_cast<const uint8_t *>(q);
+    p.q_st = q_stride_t;
+    p.q_sh = q_stride_h;
+    p.kv_a = static_cast<const uint8_t *>(cache);
+    p.kv_b = nullptr;
+    p.split_col = W;
+    p.indices = nullptr;
+    p.lens = lengths;
+    p.T = T;
+    p.H = H;
+    p.W = W;
+    p.scale_log2 = (float)((double)bmm1_scale * 1.4426950408889634);
+    p.bmm2 = bmm2_scale;
+    p.sinks = nullptr;
+    p.out = static_cast<uint16_t *>(out);
+    p.lse = lse;
+    p.lse_log2 = (flags & SMLA_LSE_LOG2) ? 1 : 0;
+    p.splits = chosen.splits;
+    p.groups = head_groups(H, 2);
+    p.wait_polls = g_wait_polls.load(std::memory_order_relaxed);
+    p.wait_extra = g_wait_extra.load(std::memory_order_relaxed);
+    p.paged = 1;
+    p.block_table = block_table;
+    p.max_pages = max_pages;
+    p.page_size = page_size;
+    p.q_len = q_len;
+    p.page_stride = page_stride;
+    if (need > 0) {
+        const WsLayout w = ws_layout(&chosen, T, H);
+        uint8_t *base = static_cast<uint8_t *>(workspace);
+        p.status = reinterpret_cast<int32_t *>(base + w.status);
+        p.counters = reinterpret_cast<int32_t *>(base + w.counters);
+        p.ws_o = reinterpret_cast<float *>(base + w.partials);
+        p.ws_ml = reinterpret_cast<float *>(base + w.ml);
+    }
+    const hipError_t e = smla::launch_decode_g64(p, 576, 576, (flags & SMLA_P_ONE_TERM) == 0,
+                                                 stream);
+    return e == hipSuccess ? SMLA_OK : SMLA_EHIP;
 }
 
 smla_status mla_value(const void *partials, const float *lse2, int32_t S, int32_t T, int32_t H,

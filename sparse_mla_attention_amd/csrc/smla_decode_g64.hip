@@ -132,7 +132,12 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
     const int hg = unit % a.groups;
     const int split = unit / a.groups;
 
-    int n = a.lens[t];
+    // the token's active count: lens[t] (sparse), or its request's context length less the
+    // causal offset of its row (paged)
+    const int req = a.paged ? t / a.q_len : t;
+    int n = a.lens[req];
+    if (a.paged)
+        n -= a.q_len - 1 - (t - req * a.q_len);
     n = n < 0 ? 0 : (n > a.W ? a.W : n);
     const int per = (n + a.splits - 1) / a.splits;
     const int first = min(n, split * per);
@@ -157,10 +162,17 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
         for (int i = tid; i < nch * CHUNK; i += NT) {
             uint64_t src = zero;
             if (i < mine) {
-                const int raw = idx_row[first + i];
-                if (raw >= 0)
-                    src = (uint64_t)(uintptr_t)((first + i >= split_col ? pool_b : pool_a) +
-                                                (int64_t)raw * RB);
+                if (a.paged) {
+                    const int k = first + i;
+                    const int page = a.block_table[(int64_t)req * a.max_pages + k / a.page_size];
+                    src = (uint64_t)(uintptr_t)(pool_a + (int64_t)page * a.page_stride +
+                                                (int64_t)(k % a.page_size) * RB);
+                } else {
+                    const int raw = idx_row[first + i];
+                    if (raw >= 0)
+                        src = (uint64_t)(uintptr_t)((first + i >= split_col ? pool_b : pool_a) +
+                                                    (int64_t)raw * RB);
+                }
             }
             ad[i] = src;
         }

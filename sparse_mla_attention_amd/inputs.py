@@ -306,3 +306,62 @@ def value_problem(seed: int, S: int, T: int, H: int, empty_frac: float = 0.1,
         gate[r * rows_per_request:(r + 1) * rows_per_request] = NAN_BF16
     return dict(name=f"value{seed}", partials=m["partials"], lse=m["lse"], w_uv_t=w_t,
                 gate=gate, totals=totals, rows_per_request=rows_per_request)
+
+
+def paged_problem(seed: int, B: int, q_len: int, H: int, lengths, *, page_size: int = 64,
+                  max_pages: int | None = None, spare_pages: int = 8, kv_scale_to_amax=True,
+                  poison: bool = True) -> dict:
+    """A dense paged MLA decode problem (the dcp page's stock_decode): B requests of q_len
+    query rows each (row t = b * q_len + i), H heads, a paged FP8 cache [num_pages, page_size,
+    576] (N(0,1) scaled per tensor to amax 448), block_table [B, max_pages] of distinct pages in
+    random order (entries past a request's context point at other, poisoned pages), context
+    lengths [B]; bmm1 = k_scale / sqrt(576), bmm2 = k_scale, natural-log LSE.  Cache rows no
+    request's context covers are E4M3 NaN when `poison` is set."""
+    rng = np.random.default_rng(seed)
+    lengths = np.asarray(lengths, dtype=np.int32)
+    need = [-(-int(max(l, 0)) // page_size) for l in lengths]
+    max_pages = max(1, max(need)) if max_pages is None else max_pages
+    num_pages = sum(need) + spare_pages
+    x = rng.standard_normal((num_pages * page_size, 576)).astype(np.float32)
+    k_scale = float(np.abs(x).max()) / E4M3_MAX if kv_scale_to_amax else 1.0
+    cache = e4m3_bytes(x / k_scale).reshape(num_pages, page_size, 576)
+    del x
+    q = e4m3_bytes(rng.standard_normal((B * q_len, H, 576)))
+    perm = rng.permutation(num_pages).astype(np.int32)
+    bt = np.empty((B, max_pages), np.int32)
+    pos = 0
+    spare = perm[sum(need):]
+    for b in range(B):
+        bt[b, :need[b]] = perm[pos:pos + need[b]]
+        pos += need[b]
+        bt[b, need[b]:] = rng.choice(spare, size=max_pages - need[b]) if spare.size else 0
+    if poison:
+        used = np.zeros((num_pages, page_size), dtype=bool)
+        for b in range(B):
+            for k in range(int(max(lengths[b], 0))):
+                used[bt[b, k // page_size], k % page_size] = True
+        cache[~used] = NAN_E4M3
+    return dict(name=f"paged B={B} q_len={q_len} H={H}", q=q, cache=cache, block_table=bt,
+                lengths=lengths, q_len=q_len, bmm1=k_scale / 24.0, bmm2=k_scale, lse_log2=False)
+
+
+def paged_as_sparse(p: dict) -> dict:
+    """The same paged problem as a sparse one over the flattened cache: row t's indices are its
+    context's storage rows in order, its count the causal count."""
+    num_pages, page_size, _ = p["cache"].shape
+    B, max_pages = p["block_table"].shape
+    q_len = p["q_len"]
+    W = max_pages * page_size
+    T = B * q_len
+    idx = np.full((T, W), -1, np.int32)
+    lens = np.zeros(T, np.int32)
+    k = np.arange(W)
+    for t in range(T):
+        b, i = divmod(t, q_len)
+        n = int(np.clip(p["lengths"][b] - (q_len - 1 - i), 0, W))
+        lens[t] = n
+        idx[t, :n] = p["block_table"][b, k[:n] // page_size] * page_size + k[:n] % page_size
+    return dict(name=p["name"] + " as sparse", q=p["q"],
+                kv_a=p["cache"].reshape(num_pages * page_size, 576), kv_b=None, split_col=W,
+                qk_dim=576, indices=idx, lens=lens, sinks=None, bmm1=p["bmm1"], bmm2=p["bmm2"],
+                lse_log2=p["lse_log2"])

@@ -538,3 +538,59 @@ def test_mla_value_padded_rows_are_zero_and_empty_sources_merge_to_zero():
     assert np.all(out[2:4] == 0.0)
     assert np.all(out[4] == 0.0)
     assert np.all(np.isfinite(out)) and np.any(out[0] != 0.0)
+
+
+# ---------------------------------------------------------------------------
+# paged decode (dcp page, stock_decode)
+# ---------------------------------------------------------------------------
+
+def test_paged_equals_sparse_over_the_materialized_rows():
+    """The paged oracle on a block table equals the (independently pinned) sparse exact mode
+    over the same rows listed as indices with the causal counts."""
+    p = inputs.paged_problem(60, 3, 4, 16, [150, 3, 64], page_size=16)
+    out, lse = oracle.paged_decode_exact(p)
+    ref, ref_lse = oracle.decode_exact(inputs.paged_as_sparse(p))
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-14)
+    np.testing.assert_array_equal(np.isfinite(lse), np.isfinite(ref_lse))
+    fin = np.isfinite(lse)
+    np.testing.assert_allclose(lse[fin], ref_lse[fin], rtol=1e-13)
+
+
+def test_paged_causal_mask_matches_sdpa():
+    """float64 scaled-dot-product attention over each request's materialized context with the
+    causal offset mask (row i of q_len sees keys < length - (q_len - 1 - i))."""
+    p = inputs.paged_problem(61, 2, 3, 16, [40, 9], page_size=8, poison=False)
+    out, lse = oracle.paged_decode_exact(p)
+    cache = _e4m3_f64(p["cache"]).numpy()
+    q = _e4m3_f64(p["q"]).numpy()
+    H = 16
+    for b in range(2):
+        L = int(p["lengths"][b])
+        rows = np.stack([cache[p["block_table"][b, k // 8], k % 8] for k in range(L)])
+        K = torch.from_numpy(rows[:, :576])
+        V = torch.from_numpy(rows[:, :512])
+        Q = torch.from_numpy(q[3 * b:3 * b + 3])                   # [3, H, 576]
+        mask = torch.full((3, L), float("-inf"), dtype=torch.float64)
+        for i in range(3):
+            mask[i, :L - (3 - 1 - i)] = 0.0
+        for h in range(H):
+            o = torch.nn.functional.scaled_dot_product_attention(
+                Q[:, h][None], K[None], V[None], attn_mask=mask[None], scale=p["bmm1"])[0]
+            ls = torch.logsumexp(p["bmm1"] * (Q[:, h] @ K.T) + mask, dim=1)
+            for i in range(3):
+                u = (3 * b + i) * H + h
+                np.testing.assert_allclose(out[u], p["bmm2"] * o[i].numpy(), rtol=1e-10,
+                                           atol=1e-12)
+                assert abs(lse[u] - float(ls[i])) < 1e-10
+
+
+def test_paged_rows_without_keys_are_zero_and_lse_minus_inf():
+    """A request with fewer keys than query rows leaves its early rows without keys; a request
+    with length 0 has none at all: +0.0 output and LSE -inf."""
+    p = inputs.paged_problem(62, 2, 4, 16, [2, 0], page_size=16)
+    out, lse = oracle.paged_decode_exact(p)
+    # request 0 (length 2): rows i = 0, 1 see 2 - (3 - i) <= 0 keys; rows 2, 3 see 1 and 2
+    for t in (0, 1, 4, 5, 6, 7):
+        assert np.all(out[t * 16:(t + 1) * 16] == 0.0)
+        assert np.all(lse[t * 16:(t + 1) * 16] == -np.inf)
+    assert np.all(np.isfinite(lse[2 * 16:4 * 16]))
