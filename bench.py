@@ -68,6 +68,11 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def plan_str(plan) -> str:
+    merge = "spread" if plan.merge == 1 and plan.splits > 1 else "last"
+    return f"splits={plan.splits},tiles={plan.tiles},merge={merge}"
+
+
 def kernel_name(plan) -> str:
     return "decode_g64_kernel" if plan.tiles == 2 else "decode_kernel"
 
@@ -185,7 +190,7 @@ def small_batch(smla, inputs, replays):
                      "cold_pool_bytes": copies * pool_bytes, "T": T, "H": H, "W": W,
                      "gathered_bytes": gathered,
                      "gathered_gbs_cold": round(gathered / (uc * 1e-6) / 1e9, 1),
-                     "plan": f"splits={plan.splits},tiles={plan.tiles}",
+                     "plan": plan_str(plan),
                      "workgroups": T * (-(-((H + 31) // 32) // plan.tiles)) * plan.splits}
         log(f"latency {name}: warm {uw:.2f} us, cold {uc:.2f} us ({copies} pool copies)")
         del pools
@@ -265,7 +270,7 @@ def paged_leg(smla, inputs, replays):
     gbs = gathered / (us * 1e-6) / 1e9
     log(f"paged decode: {us:.2f} us, {gbs:.0f} GB/s")
     return {"workload": "B=32 requests x 1 q row, H=128, 4096-token contexts, 64-row pages",
-            "plan": f"splits={plan.splits},tiles={plan.tiles}", "us_per_call": round(us, 2),
+            "plan": plan_str(plan), "us_per_call": round(us, 2),
             "gathered_bytes": gathered, "gathered_gbs": round(gbs, 1),
             "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
             "timing": f"20 calls in one HIP graph, median of {replays} replays"}
@@ -409,8 +414,7 @@ def main():
         "data": "synthetic (seeded; pool N(0,1) per-tensor scaled to E4M3, 8 rotating index sets)",
         "config": {"workload": "large-batch sparse MLA decode: T=64 tokens, H=128 heads, 2048 "
                                "active 576-byte E4M3 rows per token from a 1,048,576-row pool",
-                   "p_terms": 1 if args.one_term else 2, "plan": f"splits={plan.splits},"
-                   f"tiles={plan.tiles}", "us_per_call": round(ms * 1e3, 2),
+                   "p_terms": 1 if args.one_term else 2, "plan": plan_str(plan), "us_per_call": round(ms * 1e3, 2),
                    "us_per_call_replays": [round(x * 1e3, 2) for x in reps],
                    "us_per_call_eager": round(ms_eager * 1e3, 2),
                    f"us_per_call_{'two' if args.one_term else 'one'}_term":

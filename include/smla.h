@@ -59,10 +59,9 @@ typedef int32_t smla_status;
  * group of `tiles` 32-head tiles (heads padded up to a multiple of 32) and one of `splits`
  * contiguous ranges of the token's clamped count (range s = [min(n, s*per), +min(n - first,
  * per)), per = ceil(n / splits), as the attn_sparse page's key split); the ranges run in chunks
- * of `chunk` columns and, when splits > 1, the last range of a (token, head group) to finish
- * merges the FP32 partials of all of them (each range's FP32 accumulators with its frame and
- * sum; the attn_sparse page's module docstring, "Precision": the split partials merge in
- * FP32). */
+ * of `chunk` columns and, when splits > 1, their partials (FP32 accumulators with the range's
+ * running maximum m and sum l) are merged in FP32, in range order, with weights 2^(m_s - M)
+ * (the attn_sparse page's module docstring, "Precision", and its merge method). */
 typedef struct smla_plan {
     int32_t splits; /* 1 .. 64 */
     int32_t tiles;  /* 32-head tiles per workgroup: 1 (32 heads, rows loaded into registers) or
@@ -70,13 +69,32 @@ typedef struct smla_plan {
                        when ceil(H / 32) is odd; ranges of at most 2048 columns,
                        ceil(W / splits) <= 2048, else SMLA_EUNSUPPORTED) */
     int32_t chunk;  /* columns per gathered chunk (64 in this build; output only) */
-    int32_t reserved;
+    int32_t merge;  /* how the split partials are merged (ignored when splits == 1):
+                       SMLA_MERGE_LAST: the last range of a (token, head group) to finish merges
+                       every column; any grid size.
+                       SMLA_MERGE_SPREAD: range s merges output columns [s, s+1) * 512 / splits
+                       of every head, so the merge's reads are spread over all the ranges'
+                       workgroups.  The ranges of a (token, head group) wait for each other
+                       (a bounded wait, as under sparse_mla_decode), so every workgroup must be
+                       resident at once: tiles must be 2 (the 64-head kernel; the 32-head
+                       kernel has no spread merge), splits 2, 4, 8 or 16 and the grid, tokens x
+                       head groups x splits, at most the device's compute-unit count (one
+                       workgroup fits per compute unit), else SMLA_EUNSUPPORTED.  Kernels that
+                       run concurrently on other streams may delay some of the workgroups until
+                       they finish; a kernel that itself waits on this call's results while
+                       holding compute units could make the wait give up. */
 } smla_plan;
 
-/* The plan sparse_mla_decode uses for these sizes when it is given none: 64 heads per
- * workgroup when that needs at most two key ranges, else 32; one range when a token has at
- * most 6 chunks of columns, else enough ranges to cover the device's compute units (queried
- * once per device), at most 4.  Returns SMLA_EINVAL for bad sizes, SMLA_EHIP if the device
+#define SMLA_MERGE_LAST 0
+#define SMLA_MERGE_SPREAD 1
+
+/* The plan sparse_mla_decode uses for these sizes when it is given none.  One range when a
+ * token has at most 6 chunks of columns.  Else, when the tokens' 64-head groups fill at most a
+ * quarter of the device's compute units (queried once per device): 64 heads per workgroup,
+ * SMLA_MERGE_SPREAD over the most ranges (2, 4 or 8) that keep at least two chunks per range
+ * and the grid within the compute units.  Else the last-arriver merge: 64 heads per workgroup
+ * when that needs at most two ranges to cover the compute units, otherwise 32 heads per
+ * workgroup and up to 4 ranges.  Returns SMLA_EINVAL for bad sizes, SMLA_EHIP if the device
  * cannot be queried. */
 smla_status smla_decode_plan(int32_t T, int32_t H, int32_t W, int32_t row_bytes, uint32_t flags,
                              smla_plan *plan);

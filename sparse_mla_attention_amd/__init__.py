@@ -22,6 +22,7 @@ SMLA_ESCRATCH = 5
 NOALLOC_SCRATCH_BYTES = 48 << 20
 SMLA_LSE_LOG2 = 0x1
 SMLA_P_ONE_TERM = 0x2
+SMLA_MERGE_LAST, SMLA_MERGE_SPREAD = 0, 1
 
 
 class SmlaError(RuntimeError):
@@ -32,10 +33,11 @@ class SmlaError(RuntimeError):
 
 class Plan(ctypes.Structure):
     _fields_ = [("splits", ctypes.c_int32), ("tiles", ctypes.c_int32),
-                ("chunk", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("chunk", ctypes.c_int32), ("merge", ctypes.c_int32)]
 
     def __repr__(self):
-        return f"Plan(splits={self.splits}, tiles={self.tiles}, chunk={self.chunk})"
+        return (f"Plan(splits={self.splits}, tiles={self.tiles}, chunk={self.chunk}, "
+                f"merge={self.merge})")
 
 
 _lib = None
@@ -142,8 +144,8 @@ def testing_set_merge_wait(max_polls: int = 0, unreachable: bool = False) -> Non
         raise SmlaError(st, "smla_testing_set_merge_wait")
 
 
-def make_plan(splits: int, tiles: int) -> Plan:
-    return Plan(splits, tiles, 64, 0)
+def make_plan(splits: int, tiles: int, merge: int = SMLA_MERGE_LAST) -> Plan:
+    return Plan(splits, tiles, 64, merge)
 
 
 def _decode_args(q, kv_a, indices, lens, bmm1_scale, bmm2_scale, out, lse, kv_b, split_col,

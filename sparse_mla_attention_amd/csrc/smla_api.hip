@@ -17,6 +17,7 @@ constexpr int kMaxSplits = 64;
 constexpr int kChunk = 64;
 constexpr int kDefaultMaxSplits = 4;
 constexpr int kFewChunks = 6;
+constexpr int kMaxSpreadSplits = 8;
 constexpr int32_t kDefaultWaitPolls = 1 << 24;
 std::atomic<int> g_cu_count[kMaxDevices];
 // bound of the 64-head kernel's split-merge wait, and the test hook that makes it unreachable
@@ -86,8 +87,29 @@ bool plan_ok(const smla_plan *p, int32_t H)
         return false;
     if (p->tiles != 1 && p->tiles != 2)
         return false;
+    if (p->merge != SMLA_MERGE_LAST && p->merge != SMLA_MERGE_SPREAD)
+        return false;
     (void)H;
     return true;
+}
+
+// A spread merge needs 512 / splits output columns per range in whole 32-column tiles and a
+// grid of at most one workgroup per compute unit, so that every workgroup is resident at once
+// (each waits for the others of its token and head group).
+smla_status spread_ok(const smla_plan *p, int32_t T, int32_t H)
+{
+    if (p->merge != SMLA_MERGE_SPREAD || p->splits == 1)
+        return SMLA_OK;
+    if (p->tiles != 2)
+        return SMLA_EUNSUPPORTED;  // built into the 64-head kernel only
+    if (p->splits != 2 && p->splits != 4 && p->splits != 8 && p->splits != 16)
+        return SMLA_EUNSUPPORTED;
+    int cus = 0;
+    if (current_cu_count(&cus) != hipSuccess)
+        return SMLA_EHIP;
+    if ((int64_t)T * head_groups(H, p->tiles) * p->splits > cus)
+        return SMLA_EUNSUPPORTED;
+    return SMLA_OK;
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -161,10 +183,28 @@ smla_status smla_decode_plan(int32_t T, int32_t H, int32_t W, int32_t row_bytes,
     int cus = 0;
     if (current_cu_count(&cus) != hipSuccess)
         return SMLA_EHIP;
-    // 64 heads per workgroup (the last group padded when the 32-head tiles do not pair up)
-    // unless that needs more than two key ranges: its split exchange is built for two ranges
-    // at a full grid; more ranges go to the 32-head kernel, whose store-first exchange suits
-    // the few workgroups of small batches.
+    // Small batches with long rows: 64 heads per workgroup and a spread merge over the most
+    // ranges (a power of two, at most kMaxSpreadSplits) that keep at least two chunks per range
+    // and the grid within the compute units; it needs at most a quarter of the compute units
+    // for the tokens' head groups alone.
+    const int64_t chunks = (W + kChunk - 1) / kChunk;
+    const int64_t units64 = (int64_t)T * head_groups(H, 2);
+    if (chunks > kFewChunks && units64 * 4 <= cus) {
+        int s = kMaxSpreadSplits;
+        while (s > 2 && (units64 * s > cus || 2 * s > chunks))
+            s /= 2;
+        if ((W + s - 1) / s <= smla::G64_MAX_RANGE) {
+            plan->tiles = 2;
+            plan->splits = s;
+            plan->chunk = kChunk;
+            plan->merge = SMLA_MERGE_SPREAD;
+            return SMLA_OK;
+        }
+    }
+    // Otherwise 64 heads per workgroup (the last group padded when the 32-head tiles do not
+    // pair up) unless that needs more than two key ranges: its last-arriver exchange is built
+    // for two ranges at a full grid; more ranges go to the 32-head kernel, whose store-first
+    // exchange suits the few workgroups of small batches.
     const int s64 = default_splits(T, head_groups(H, 2), W, cus, 2);
     if (s64 <= 2) {
         plan->tiles = 2;
@@ -174,7 +214,7 @@ smla_status smla_decode_plan(int32_t T, int32_t H, int32_t W, int32_t row_bytes,
         plan->splits = default_splits(T, head_groups(H, 1), W, cus, 1);
     }
     plan->chunk = kChunk;
-    plan->reserved = 0;
+    plan->merge = SMLA_MERGE_LAST;
     return SMLA_OK;
 }
 
@@ -241,6 +281,11 @@ smla_status decode_impl(const void *q, int64_t q_stride_t, int64_t q_stride_h,
     }
     if (chosen.tiles == 2 && (W + chosen.splits - 1) / chosen.splits > smla::G64_MAX_RANGE)
         return SMLA_EUNSUPPORTED;  // the 64-head kernel stages a range's indices in LDS
+    {
+        const smla_status st = spread_ok(&chosen, T, H);
+        if (st != SMLA_OK)
+            return st;
+    }
     const size_t need = smla_decode_workspace_size(&chosen, T, H);
     if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
         return SMLA_EWORKSPACE;
@@ -266,6 +311,7 @@ smla_status decode_impl(const void *q, int64_t q_stride_t, int64_t q_stride_h,
     p.lse_log2 = (flags & SMLA_LSE_LOG2) ? 1 : 0;
     p.splits = chosen.splits;
     p.groups = head_groups(H, chosen.tiles);
+    p.merge = chosen.merge;
     p.ws_o = nullptr;
     p.ws_ml = nullptr;
     p.counters = nullptr;
@@ -330,7 +376,7 @@ smla_status smla_paged_decode_plan(int32_t B, int32_t q_len, int32_t H, int32_t 
     if (plan->splits > kMaxSplits)
         return SMLA_EUNSUPPORTED;
     plan->chunk = kChunk;
-    plan->reserved = 0;
+    plan->merge = SMLA_MERGE_LAST;
     return SMLA_OK;
 }
 
@@ -371,6 +417,11 @@ smla_status paged_mla_decode(const void *q, int64_t q_stride_t, int64_t q_stride
     const int32_t T = B * q_len;
     if (T == 0)
         return SMLA_OK;
+    {
+        const smla_status st = spread_ok(&chosen, T, H);
+        if (st != SMLA_OK)
+            return st;
+    }
     if (q == nullptr || cache == nullptr || block_table == nullptr || lengths == nullptr ||
         out == nullptr)
         return SMLA_EINVAL;
@@ -402,6 +453,7 @@ smla_status paged_mla_decode(const void *q, int64_t q_stride_t, int64_t q_stride
     p.lse_log2 = (flags & SMLA_LSE_LOG2) ? 1 : 0;
     p.splits = chosen.splits;
     p.groups = head_groups(H, 2);
+    p.merge = chosen.merge;
     p.wait_polls = g_wait_polls.load(std::memory_order_relaxed);
     p.wait_extra = g_wait_extra.load(std::memory_order_relaxed);
     p.paged = 1;

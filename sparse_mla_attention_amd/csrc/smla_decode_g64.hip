@@ -45,6 +45,7 @@
 
 #include "smla_device.h"
 #include "smla_internal.h"
+#include "smla_spread.h"
 
 namespace smla {
 namespace {
@@ -80,6 +81,7 @@ struct LdsG {
     static constexpr int TOTAL = MISC + 16;
     static constexpr int OUT_TILE = HG * 1024;                 // BF16 [64][512], after the loop
     static_assert(OUT_TILE <= P, "output tile must fit in the slots");
+    static_assert(OUT_TILE + 16 * HG * 8 <= P, "(m, l) of 16 ranges must fit past the tile");
     static_assert(TOTAL <= 160 * 1024, "LDS budget");
 };
 
@@ -113,7 +115,7 @@ __device__ inline uint32_t lds_addr(const uint8_t *p)
     return (uint32_t)(uintptr_t)(const SMLA_LDS(uint8_t) *)p;
 }
 
-template <int RB, int QK, bool TWO>
+template <int RB, int QK, bool TWO, bool DIST>
 __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
 {
     constexpr bool TAIL = QK == 576;               // a fifth, 64-byte QK step (rope)
@@ -206,7 +208,38 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
                                                      0x00020000);
         };
         bool failed = false;
-        if (a.splits > 1) {
+        if (DIST && a.splits > 1) {
+            // Spread merge: every range stores its whole partial, then merges its own column
+            // slice of all of them and writes it (smla_spread.h).
+            const int64_t ui = tg * a.splits + split;
+            if (!qk_wave) {
+                const auto rs = part_rsrc(ui);
+#pragma unroll
+                for (int ct = 0; ct < NCT; ct++)
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; h2++)
+#pragma unroll
+                        for (int j = 0; j < 4; j++)
+                            __builtin_amdgcn_raw_buffer_store_b128(
+                                v4i{__float_as_int(acc[ct][h2][4 * j]),
+                                    __float_as_int(acc[ct][h2][4 * j + 1]),
+                                    __float_as_int(acc[ct][h2][4 * j + 2]),
+                                    __float_as_int(acc[ct][h2][4 * j + 3])},
+                                rs, part_off(ct, h2, j), 0, SC1);
+            }
+            if (wave == 4 && u == 0) {
+#pragma unroll
+                for (int h2 = 0; h2 < 2; h2++) {
+                    store_device(a.ws_ml + (ui * HG + 32 * h2 + hl) * 2 + 0, g_h[h2]);
+                    store_device(a.ws_ml + (ui * HG + 32 * h2 + hl) * 2 + 1, l_h[h2]);
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(0);  // this wave's stores have completed
+            __syncthreads();
+            spread_merge<HG>(a, lds, reinterpret_cast<int *>(lds + L::MISC) + 2, t, hg, tg, split,
+                             tid);
+            return;
+        } else if (!DIST && a.splits > 1) {
             // Split merge.  Each range takes an arrival ticket first.  Every range but the last
             // writes its partial (FP32 accumulators in register order, then (m, l) per head)
             // with device-scope (write-through) stores, waits for them to complete and bumps
@@ -786,7 +819,12 @@ template <int RB, int QK, bool TWO>
 hipError_t launch_g64_one(const DecodeParams &p, hipStream_t stream)
 {
     const unsigned blocks = (unsigned)p.T * (unsigned)p.groups * (unsigned)p.splits;
-    hipLaunchKernelGGL((decode_g64_kernel<RB, QK, TWO>), dim3(blocks), dim3(NT), 0, stream, p);
+    // the spread merge's ranges wait for each other: its grid is at most one workgroup per
+    // compute unit (checked on the host), so every workgroup is resident at once
+    if (p.merge == 1 && p.splits > 1)
+        hipLaunchKernelGGL((decode_g64_kernel<RB, QK, TWO, true>), dim3(blocks), dim3(NT), 0, stream, p);
+    else
+        hipLaunchKernelGGL((decode_g64_kernel<RB, QK, TWO, false>), dim3(blocks), dim3(NT), 0, stream, p);
     return hipGetLastError();
 }
 

@@ -34,6 +34,8 @@ struct DecodeParams {
     int32_t wait_extra;         // 0; 1 makes that wait unreachable (a test hook)
     int32_t splits;             // key ranges per (token, head group)
     int32_t groups;             // head groups per token = ceil(ceil(H / 32) / tiles)
+    int32_t merge;              // 0: the last range to arrive merges; 1: distributed (each
+                                // range merges 512 / splits columns; cooperative launch)
     // paged addressing (64-head kernel only): when set, `lens` holds one context length per
     // request of q_len rows, row t = b q_len + i sees the first lens[b] - (q_len - 1 - i) keys,
     // and key k is row k % page_size of page block_table[b][k / page_size] of kv_a

@@ -43,17 +43,41 @@ def _operands(line):
     return op, dst, src
 
 
+def _blocks(lines):
+    """(label, first line, end line, comment) of every basic block, in layout order."""
+    starts = [i for i, l in enumerate(lines)
+              if re.match(r"^(\.LBB\S+:|; %bb\.\d+:)", l)]
+    out = []
+    for k, i in enumerate(starts):
+        end = starts[k + 1] if k + 1 < len(starts) else len(lines)
+        lab = lines[i].split(":")[0].strip().lstrip(";").strip()
+        # ".LBB0_20" is annotated as "Header=BB0_20"
+        out.append((lab[2:] if lab.startswith(".L") else lab, i, end, lines[i]))
+    return out
+
+
 def _asm_loop(body):
+    """The lines of the loop that holds the inline-assembly row loads: its header block and
+    every block the compiler annotates as in that loop (or in a loop nested in it), in layout
+    order (a rotated loop may place its latch before the header)."""
     lines = body.split("\n")
-    for h, l in enumerate(lines):
-        if "Loop Header" not in l:
+    blocks = _blocks(lines)
+    for lab, i, end, head in blocks:
+        if "Loop Header" not in head:
             continue
-        lab = l.split(":")[0].strip()
-        ends = [i for i, x in enumerate(lines)
-                if re.search(r"s_c?branch\S*\s+" + re.escape(lab) + r"$", x.strip())]
-        if not ends:
-            continue
-        seg = lines[h:max(ends) + 1]
+        members = {lab}
+        grew = True
+        while grew:
+            grew = False
+            for name, _, _, c in blocks:
+                m = re.search(r"Header=(\S+)", c)
+                if name not in members and m and m.group(1) in members:
+                    members.add(name)
+                    grew = True
+        seg = []
+        for l2, a, b, c in blocks:
+            if l2 in members:
+                seg.extend(lines[a:b])
         if any("ASMSTART" in x for x in seg) and any("global_load_dwordx4" in x for x in seg):
             return seg
     return None
@@ -112,7 +136,9 @@ def test_async_row_loads_are_never_touched_in_flight():
         if r.returncode != 0:
             pytest.fail(r.stdout + r.stderr)
         text = open(out).read()
-    kernels = re.findall(r"^(_ZN\S*decode_kernel\S*):[^\n]*\n(.*?)s_endpgm", text, re.S | re.M)
+    # a kernel's body runs to its end label (an early return puts an s_endpgm before the loop)
+    kernels = re.findall(r"^(_ZN\S*decode_kernel\S*):[^\n]*\n(.*?)^\.Lfunc_end", text,
+                         re.S | re.M)
     assert len(kernels) == 6  # 3 row shapes x one/two-term P
     for name, body in kernels:
         blocks, problems = _check(body)
