@@ -6,9 +6,10 @@ heads, 2048 gathered 576-byte FP8 rows per token from a 1M-row pool), inputs res
 rotating 8 index sets across calls so the gathered rows are not served from the caches of the
 previous call.  The metric is gathered-KV bytes per second (the rows the method must move:
 active columns x 576 bytes) and microseconds per call.  Beside it: the small-batch shapes (1, 5
-and 12 tokens) in microseconds per call, warm and cold; lse_merge at its workload shape in
-GB/s; an empty-kernel launch baseline measured the same way; and the FP64 CPU oracle's rate on
-the host cores.
+and 12 tokens) in microseconds per call, warm and cold; lse_merge, mla_value and
+paged_mla_decode at their workload shapes in GB/s; an empty-kernel launch baseline measured the
+same way; and the FP64 CPU oracle's rate on the host cores.  Before the warm-up steps the device
+runs the decode untimed for --settle-ms (clock and translation-cache ramp).
 
 Prints ONE JSON line.  N > 1 GPUs is not supported (one rank's share runs on one GPU).
 """
@@ -32,7 +33,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_throughput_traffic.json")
 CSRC = os.path.join(ROOT, "sparse_mla_attention_amd", "csrc")
 # the sources of the decode kernels: the traffic counters are valid only for these exact files
 DECODE_SRCS = [os.path.join(CSRC, f) for f in
-               ("smla_decode.hip", "smla_decode_g64.hip", "smla_device.h", "smla_internal.h")]
+               ("smla_decode.hip", "smla_decode_g64.hip", "smla_device.h", "smla_internal.h",
+                "smla_spread.h")]
 COLD_POOL_BYTES = 512 << 20    # pool copies rotated across calls for the cold small-batch runs
 
 
@@ -43,14 +45,19 @@ def log(msg):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="milliseconds of untimed decode calls run before the warm-up steps, so "
+                         "that the device's clocks and translation caches reach steady state")
     ap.add_argument("--replays", type=int, default=7,
                     help="timed replays of the K-step graph; the median is reported")
     ap.add_argument("--one-term", action="store_true",
                     help="make the headline the one-term E4M3-P recipe (default: two-term)")
     ap.add_argument("--splits", type=int, default=0, help="override the plan's split count")
     ap.add_argument("--tiles", type=int, default=0, help="override the plan's tiles per WG")
+    ap.add_argument("--merge", type=int, default=-1,
+                    help="override the plan's merge mode (0 last-arriver, 1 spread)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-latency", action="store_true", help="skip the small-batch timings")
     ap.add_argument("--no-merge", action="store_true", help="skip the lse_merge leg")
@@ -86,7 +93,7 @@ def traffic_for(plan, one_term):
         return None
     if d.get("source_sha") != source_hash():
         return None
-    key = f"splits={plan.splits},tiles={plan.tiles},one_term={int(one_term)}"
+    key = f"{plan_str(plan)},one_term={int(one_term)}"
     e = d.get("entries", {}).get(key)
     return None if e is None else e.get("hbm_bytes_per_call")
 
@@ -103,6 +110,31 @@ def time_calls(fn, n, stream):
     end.record(stream)
     torch.cuda.synchronize()
     return start.elapsed_time(end) / n  # ms per call
+
+
+def settle(fn, ms):
+    """Run the decode for about `ms` milliseconds before anything is timed: measured on the
+    large-batch call, the first milliseconds of work on an idle device run up to 15% slower
+    than the steady state (clock and translation-cache ramp).  Returns what was run."""
+    import torch
+    if ms <= 0:
+        return {"ms": 0.0, "calls": 0}
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn(0, s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for i in range(50):
+            fn(i, s)
+    torch.cuda.synchronize()
+    t0, reps = time.perf_counter(), 0
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        g.replay()
+        torch.cuda.synchronize()
+        reps += 1
+    return {"ms": round((time.perf_counter() - t0) * 1e3, 1), "calls": 50 * reps}
 
 
 def graph_replays(fn, calls, replays):
@@ -366,8 +398,9 @@ def main():
     out = torch.empty((T, H, 512), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((T, H), dtype=torch.float32, device="cuda")
     plan = smla.plan_for(T, H, W, ROW_BYTES)
-    if args.splits or args.tiles:
-        plan = smla.make_plan(args.splits or plan.splits, args.tiles or plan.tiles)
+    if args.splits or args.tiles or args.merge >= 0:
+        plan = smla.make_plan(args.splits or plan.splits, args.tiles or plan.tiles,
+                              plan.merge if args.merge < 0 else args.merge)
     ws = smla.new_workspace(plan, T, H)
     sets = w["index_sets"]
 
@@ -382,6 +415,7 @@ def main():
                                     lse, one_term=args.one_term, plan=plan, workspace=ws,
                                     stream=stream) for idx in sets]
 
+    settled = settle(call, args.settle_ms)
     for i in range(args.warmup):
         call(i)
     torch.cuda.synchronize()
@@ -414,13 +448,15 @@ def main():
         "data": "synthetic (seeded; pool N(0,1) per-tensor scaled to E4M3, 8 rotating index sets)",
         "config": {"workload": "large-batch sparse MLA decode: T=64 tokens, H=128 heads, 2048 "
                                "active 576-byte E4M3 rows per token from a 1,048,576-row pool",
-                   "p_terms": 1 if args.one_term else 2, "plan": plan_str(plan), "us_per_call": round(ms * 1e3, 2),
+                   "p_terms": 1 if args.one_term else 2, "plan": plan_str(plan),
+                   "us_per_call": round(ms * 1e3, 2),
                    "us_per_call_replays": [round(x * 1e3, 2) for x in reps],
                    "us_per_call_eager": round(ms_eager * 1e3, 2),
                    f"us_per_call_{'two' if args.one_term else 'one'}_term":
                        round(ms_other * 1e3, 2),
                    "timing": f"K calls captured in one HIP graph; median of {args.replays} "
-                             "timed replays"},
+                             "timed replays",
+                   "settle": settled},
         "roofline": roof,
     }
     result["launch_baseline"] = empty_kernel_baseline(args.replays)
