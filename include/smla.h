@@ -108,8 +108,11 @@ smla_status smla_decode_plan(int32_t T, int32_t H, int32_t W, int32_t row_bytes,
  *                   zero-filled (0 in normal operation; see sparse_mla_decode);
  *   bytes [16, ..)  arrival counters, two int32 per token and head group, then padding to a
  *                   multiple of 256 bytes;
- *   then            FP32 partials [T, groups, splits, 32 tiles, 512] and FP32 (frame, sum) pairs
- *                   [T, groups, splits, 32 tiles, 2], groups = ceil(ceil(H / 32) / tiles).
+ *   then            FP32 partials [T, groups, splits, 32 tiles, 512] (each range's accumulators
+ *                   at 448 of its running maximum, not normalized, in the kernel's register
+ *                   order) and FP32 (m, l) pairs [T, groups, splits, 32 tiles, 2] (running
+ *                   maximum in base 2, sum of the unquantized P), groups = ceil(ceil(H / 32) /
+ *                   tiles).
  * Returns 0 for a bad plan. */
 size_t smla_decode_workspace_size(const smla_plan *plan, int32_t T, int32_t H);
 
@@ -141,22 +144,22 @@ size_t smla_decode_workspace_size(const smla_plan *plan, int32_t T, int32_t H);
  *                its first use: its first bytes hold a status word and arrival counters that
  *                must start at zero, and every call leaves them at zero again (the partials are
  *                overwritten before they are read).  Calls that share a workspace must be
- *                stream-ordered.  With 64 heads per workgroup (plan tiles = 2) the range that
- *                merges waits for the others' partials with a bounded poll (2^24 polls, about
- *                half a second); if the bound runs out it adds 1 to the status word, writes NaN
- *                to its heads' outputs and LSEs and leaves the counters non-zero: a caller that
- *                finds the status word non-zero must treat those outputs as failed and zero-fill
- *                the workspace again before its next use.
+ *                stream-ordered.  With 64 heads per workgroup (plan tiles = 2) a range that
+ *                merges waits for other ranges with a bounded poll (2^24 polls, about half a
+ *                second): the last-arriver merge's last range for the others' partials, every
+ *                range of a spread merge for the others' arrivals.  If the bound runs out the
+ *                range adds 1 to the status word, writes NaN to the outputs and LSEs it owns and
+ *                leaves the counters non-zero: a caller that finds the status word non-zero
+ *                must treat those outputs as failed and zero-fill the workspace again before
+ *                its next use.  (The 32-head kernel's merge never waits: every range stores
+ *                first and the last to arrive merges.)
  *
- * P anchoring: within a key range, the first chunk with an active column fixes the frame G
- * (its running maximum) and each chunk quantizes P = 2^(s2 - F + log2 448) at F = G +
- * ceil(m - G) >= m, m the running maximum, so P <= 448 as in the recipe while the chunk's
- * products enter the FP32 accumulator with the exact weight 2^(F - G) (the matrix
- * instruction's E8M0 block scale) instead of rescaling the accumulator.  If some head's
- * offset F - G would exceed 96 (scores that rise by more than 96 binades within a range),
- * the workgroup computes its range a second time with that head's G preset to the head's
- * maximum over the range (offsets F - G <= 0, floored at -120), so no accumulator is ever
- * rescaled.
+ * Softmax (the attn_sparse page's recipe, module docstring): per head, chunk by chunk of 64
+ * columns, the running maximum m of the base-2 scores s2 = s log2(e) rises to m' = max(m,
+ * chunk maximum); everything accumulated so far (FP32 output accumulators and the FP32 sum l of
+ * the unquantized P) is rescaled by alpha = 2^(m - m'); the chunk's P = 2^(s2 - m' + log2 448)
+ * <= 448 is rounded to E4M3 (two terms by default, see SMLA_P_ONE_TERM) for the P.V product,
+ * and its unquantized value is added to l.  Split partials merge in FP32 as smla_plan states.
  *
  * T == 0 is a no-op returning SMLA_OK after the size, flag and plan checks (the pointers are
  * not examined: empty tensors may have null data).  Errors: SMLA_EINVAL (null required

@@ -118,7 +118,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // waiting), counters [T, groups, 2] int32 from byte 16 (arrival ticket and ready count, zero
 // between calls), padded to 256 bytes; then FP32 partials: one block of 32 tiles x 512 floats per
 // (token, head group, range), in the order the kernel's accumulator registers are stored (16-byte
-// runs per lane); then (frame, sum) [T, groups, splits, 32 tiles heads, 2].
+// runs per lane); then (m, l) [T, groups, splits, 32 tiles heads, 2].
 struct WsLayout {
     size_t status, counters, partials, ml, total;
 };

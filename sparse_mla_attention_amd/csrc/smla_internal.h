@@ -26,7 +26,7 @@ struct DecodeParams {
     int32_t lse_log2;           // 1: base-2 LSE
     float *ws_o;                // FP32 partials: a block of (heads per group) x 512 floats per
                                 // (token, group, range), in the kernel's register order
-    float *ws_ml;               // (frame, sum) [T, groups, splits, heads per group, 2]
+    float *ws_ml;               // (m, l) [T, groups, splits, heads per group, 2]
     int32_t *counters;          // [T, groups, 2]: arrival ticket, ready count; zero between
                                 // calls (splits > 1)
     int32_t *status;            // workspace status word: merges that gave up waiting

@@ -36,7 +36,7 @@ def test_workspace_size_formula():
         groups = -(-((H + 31) // 32) // tiles)
         # status word, counters from byte 16, padded to 256
         counters = (16 + T * groups * 2 * 4 + 255) // 256 * 256
-        # FP32 partials (512 per head) and FP32 (frame, sum) pairs
+        # FP32 partials (512 per head) and FP32 (m, l) pairs
         return counters + T * groups * splits * 32 * tiles * (512 + 2) * 4
     for splits, tiles, T, H in [(2, 1, 7, 128), (3, 1, 7, 96), (64, 1, 3, 16), (5, 1, 2, 48),
                                 (2, 2, 7, 128), (4, 2, 3, 64), (3, 2, 2, 48), (2, 2, 7, 96),
