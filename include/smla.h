@@ -91,7 +91,7 @@ typedef struct smla_plan {
 /* The plan sparse_mla_decode uses for these sizes when it is given none.  One range when a
  * token has at most 6 chunks of columns.  Else, when the tokens' 64-head groups fill at most a
  * quarter of the device's compute units (queried once per device): 64 heads per workgroup,
- * SMLA_MERGE_SPREAD over the most ranges (2, 4 or 8) that keep at least two chunks per range
+ * SMLA_MERGE_SPREAD over the most ranges (2, 4 or 8) that keep at least one chunk per range
  * and the grid within the compute units.  Else the last-arriver merge: 64 heads per workgroup
  * when that needs at most two ranges to cover the compute units, otherwise 32 heads per
  * workgroup and up to 4 ranges.  Returns SMLA_EINVAL for bad sizes, SMLA_EHIP if the device
@@ -145,8 +145,8 @@ size_t smla_decode_workspace_size(const smla_plan *plan, int32_t T, int32_t H);
  *                must start at zero, and every call leaves them at zero again (the partials are
  *                overwritten before they are read).  Calls that share a workspace must be
  *                stream-ordered.  With 64 heads per workgroup (plan tiles = 2) a range that
- *                merges waits for other ranges with a bounded poll (2^24 polls, about half a
- *                second): the last-arriver merge's last range for the others' partials, every
+ *                merges waits for other ranges with a bounded poll (2^20 polls, each a
+ *                device-memory round trip: one to two seconds in all): the last-arriver merge's last range for the others' partials, every
  *                range of a spread merge for the others' arrivals.  If the bound runs out the
  *                range adds 1 to the status word, writes NaN to the outputs and LSEs it owns and
  *                leaves the counters non-zero: a caller that finds the status word non-zero
@@ -298,7 +298,7 @@ smla_status mla_value(const void *partials, const float *lse2, int32_t S, int32_
 const char *smla_strerror(smla_status status);
 
 /* Test hook, not for production callers: bounds the 64-head kernel's split-merge wait to
- * max_polls polls (0 restores the default, 2^24) and, with unreachable = 1, makes the merging
+ * max_polls polls (0 restores the default, 2^20) and, with unreachable = 1, makes the merging
  * range wait for one partial more than exists, so every such wait gives up after max_polls polls
  * and takes the failure path described under sparse_mla_decode while every kernel still exits
  * normally.  Process-wide; not thread-safe against concurrent calls.  SMLA_EINVAL for

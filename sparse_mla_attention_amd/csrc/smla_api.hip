@@ -18,7 +18,7 @@ constexpr int kChunk = 64;
 constexpr int kDefaultMaxSplits = 4;
 constexpr int kFewChunks = 6;
 constexpr int kMaxSpreadSplits = 8;
-constexpr int32_t kDefaultWaitPolls = 1 << 24;
+constexpr int32_t kDefaultWaitPolls = 1 << 20;
 std::atomic<int> g_cu_count[kMaxDevices];
 // bound of the 64-head kernel's split-merge wait, and the test hook that makes it unreachable
 std::atomic<int32_t> g_wait_polls{kDefaultWaitPolls};
@@ -184,14 +184,14 @@ smla_status smla_decode_plan(int32_t T, int32_t H, int32_t W, int32_t row_bytes,
     if (current_cu_count(&cus) != hipSuccess)
         return SMLA_EHIP;
     // Small batches with long rows: 64 heads per workgroup and a spread merge over the most
-    // ranges (a power of two, at most kMaxSpreadSplits) that keep at least two chunks per range
+    // ranges (a power of two, at most kMaxSpreadSplits) that keep at least one chunk per range
     // and the grid within the compute units; it needs at most a quarter of the compute units
     // for the tokens' head groups alone.
     const int64_t chunks = (W + kChunk - 1) / kChunk;
     const int64_t units64 = (int64_t)T * head_groups(H, 2);
     if (chunks > kFewChunks && units64 * 4 <= cus) {
         int s = kMaxSpreadSplits;
-        while (s > 2 && (units64 * s > cus || 2 * s > chunks))
+        while (s > 2 && (units64 * s > cus || s > chunks))
             s /= 2;
         if ((W + s - 1) / s <= smla::G64_MAX_RANGE) {
             plan->tiles = 2;

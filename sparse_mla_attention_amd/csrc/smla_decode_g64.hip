@@ -209,15 +209,19 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
         };
         bool failed = false;
         if (DIST && a.splits > 1) {
-            // Spread merge: every range stores its whole partial, then merges its own column
-            // slice of all of them and writes it (smla_spread.h).
+            // Spread merge: every range stores its whole partial (the group's real heads only:
+            // padding heads past H are never merged), then merges its own column slice of all
+            // of them and writes it (smla_spread.h).
             const int64_t ui = tg * a.splits + split;
+            const int heads_here = min(HG, a.H - hg * HG);
             if (!qk_wave) {
                 const auto rs = part_rsrc(ui);
 #pragma unroll
                 for (int ct = 0; ct < NCT; ct++)
 #pragma unroll
-                    for (int h2 = 0; h2 < 2; h2++)
+                    for (int h2 = 0; h2 < 2; h2++) {
+                        if (32 * h2 + hl >= heads_here)
+                            continue;
 #pragma unroll
                         for (int j = 0; j < 4; j++)
                             __builtin_amdgcn_raw_buffer_store_b128(
@@ -226,10 +230,13 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
                                     __float_as_int(acc[ct][h2][4 * j + 2]),
                                     __float_as_int(acc[ct][h2][4 * j + 3])},
                                 rs, part_off(ct, h2, j), 0, SC1);
+                    }
             }
             if (wave == 4 && u == 0) {
 #pragma unroll
                 for (int h2 = 0; h2 < 2; h2++) {
+                    if (32 * h2 + hl >= heads_here)
+                        continue;
                     store_device(a.ws_ml + (ui * HG + 32 * h2 + hl) * 2 + 0, g_h[h2]);
                     store_device(a.ws_ml + (ui * HG + 32 * h2 + hl) * 2 + 1, l_h[h2]);
                 }

@@ -1,4 +1,4 @@
-// The spread split merge shared by both decode kernels (plan merge = SMLA_MERGE_SPREAD).
+// The spread split merge of the 64-head decode kernel (plan merge = SMLA_MERGE_SPREAD).
 //
 // Method (the attn_sparse page's merge method and module docstring, "Precision"): the S range
 // partials of a (token, head group) merge in FP32, in range order, with weights 2^(m_s - M),
@@ -7,8 +7,9 @@
 // the two merges give the same bits.
 //
 // Decomposition.  Before calling spread_merge, every range has stored its whole partial (FP32
-// accumulators in register order, then (m, l) per head) with device-scope stores and waited for
-// them to complete.  Range s then writes output columns [s, s+1) * 512 / S of the group's heads:
+// accumulators in register order, then (m, l) per head) for the group's real heads (padding
+// heads past H are neither stored nor read) with device-scope stores and waited for them to
+// complete.  Range s then writes output columns [s, s+1) * 512 / S of the group's heads:
 //   1. arrival: one atomic add on the (token, head group)'s arrival counter, then a bounded
 //      wait until all S ranges have arrived (the grid holds at most one workgroup per compute
 //      unit, so every range is resident);
@@ -51,7 +52,13 @@ __device__ __attribute__((always_inline)) inline void spread_merge_s(
     constexpr int PP = NPOS >= NT ? NPOS / NT : 1; // positions per thread
     static_assert(NPOS % NT == 0 || NPOS < NT, "positions split evenly over the threads");
     const int lane = tid & 63;
-    const bool active = tid < NPOS;
+    const int heads_here = min(HG, a.H - hg * HG); // real heads of the group
+    // positions tid + NT i share lane and head tile: one head per thread
+    const int h2 = (tid >> 8) % H2;
+    const int hl = lane & 31;
+    const int hloc = 32 * h2 + hl;                 // head within the group
+    const int head = hg * HG + hloc;
+    const bool active = tid < NPOS && hloc < heads_here;
     int *ctr = a.counters + 2 * tg;                // [0] arrivals, [1] departures
 
     // ---- 1. arrival and bounded wait ---------------------------------------------------
@@ -84,7 +91,7 @@ __device__ __attribute__((always_inline)) inline void spread_merge_s(
     for (int k = 0; k < NML; k++) {
         const int i = tid + NT * k;
         ml[k] = float2{0.0f, 0.0f};
-        if (i < S * HG) {
+        if (i < S * HG && i % HG < heads_here) {
             const float *m = a.ws_ml + ((tg * S + i / HG) * HG + i % HG) * 2;
             ml[k] = float2{load_device(m), load_device(m + 1)};
         }
@@ -113,11 +120,6 @@ __device__ __attribute__((always_inline)) inline void spread_merge_s(
     lds_barrier();  // orders LDS only: the partial loads stay in flight
 
     // ---- 3. this thread's head: M, L, weights, normalization; sums -----------------------
-    // positions tid + NT i share lane and h2 (NT is a multiple of 64 H2... of 256 H2 / 2)
-    const int h2 = (tid >> 8) % H2;
-    const int hl = lane & 31;
-    const int hloc = 32 * h2 + hl;                 // head within the group
-    const int head = hg * HG + hloc;
     float big_g = -INFINITY;
 #pragma unroll
     for (int r = 0; r < S; r++)
@@ -168,7 +170,6 @@ __device__ __attribute__((always_inline)) inline void spread_merge_s(
 
     // ---- 4. row stores of the slice, departure ---------------------------------------------
     constexpr int PARTS = 64 / S;                  // 16-byte parts of a row in the slice
-    const int heads_here = min(HG, a.H - hg * HG);
     for (int x = tid; x < heads_here * PARTS; x += NT) {
         const int row = x / PARTS, part = split * PARTS + x % PARTS;
         const v4i o = lds_load<v4i>(tile, tile_off(row, 16 * part));
