@@ -77,7 +77,8 @@ def source_hash() -> str:
 
 def plan_str(plan) -> str:
     merge = "spread" if plan.merge == 1 and plan.splits > 1 else "last"
-    return f"splits={plan.splits},tiles={plan.tiles},merge={merge}"
+    heads = f",heads={plan.heads}" if plan.heads else ""
+    return f"splits={plan.splits},tiles={plan.tiles},merge={merge}{heads}"
 
 
 def kernel_name(plan) -> str:
@@ -223,7 +224,7 @@ def small_batch(smla, inputs, replays):
                      "gathered_bytes": gathered,
                      "gathered_gbs_cold": round(gathered / (uc * 1e-6) / 1e9, 1),
                      "plan": plan_str(plan),
-                     "workgroups": T * (-(-((H + 31) // 32) // plan.tiles)) * plan.splits}
+                     "workgroups": T * (-(-H // (plan.heads or 32 * plan.tiles))) * plan.splits}
         log(f"latency {name}: warm {uw:.2f} us, cold {uc:.2f} us ({copies} pool copies)")
         del pools
     return res

@@ -83,19 +83,25 @@ typedef struct smla_plan {
                        run concurrently on other streams may delay some of the workgroups until
                        they finish; a kernel that itself waits on this call's results while
                        holding compute units could make the wait give up. */
+    int32_t heads;  /* real heads per workgroup: 0 for 32 x tiles; with tiles = 2 also 16 or 32
+                       (the 64-head kernel still runs its two 32-head tiles, the heads past
+                       that count as padding that is neither exchanged nor written, so that a
+                       small batch spreads over more workgroups with shorter chunk chains and
+                       smaller split exchanges); head groups per token = ceil(H / heads). */
 } smla_plan;
 
 #define SMLA_MERGE_LAST 0
 #define SMLA_MERGE_SPREAD 1
 
-/* The plan sparse_mla_decode uses for these sizes when it is given none.  One range when a
- * token has at most 6 chunks of columns.  Else, when the tokens' 64-head groups fill at most a
- * quarter of the device's compute units (queried once per device): 64 heads per workgroup,
- * SMLA_MERGE_SPREAD over the most ranges (2, 4 or 8) that keep at least one chunk per range
- * and the grid within the compute units.  Else the last-arriver merge: 64 heads per workgroup
- * when that needs at most two ranges to cover the compute units, otherwise 32 heads per
- * workgroup and up to 4 ranges.  Returns SMLA_EINVAL for bad sizes, SMLA_EHIP if the device
- * cannot be queried. */
+/* The plan sparse_mla_decode uses for these sizes when it is given none: the cheapest, by a
+ * predicted time, of every plan the kernels take for them -- the 64-head kernel with 64, 32 or
+ * 16 real heads per workgroup over one key range, two ranges under SMLA_MERGE_LAST, or 2, 4, 8
+ * or 16 ranges under SMLA_MERGE_SPREAD (grid within the compute units, queried once per
+ * device), and the 32-head kernel over 1, 2, 4 or 8 ranges under SMLA_MERGE_LAST.  The
+ * prediction is a linear model of the call's time in its workgroup rounds, chunks per range,
+ * compute-unit occupancy, heads per workgroup and split-exchange bytes, with coefficients
+ * measured on MI355X; ties keep the wider head groups.  Returns SMLA_EINVAL for bad sizes,
+ * SMLA_EHIP if the device cannot be queried. */
 smla_status smla_decode_plan(int32_t T, int32_t H, int32_t W, int32_t row_bytes, uint32_t flags,
                              smla_plan *plan);
 
@@ -111,8 +117,9 @@ smla_status smla_decode_plan(int32_t T, int32_t H, int32_t W, int32_t row_bytes,
  *   then            FP32 partials [T, groups, splits, 32 tiles, 512] (each range's accumulators
  *                   at 448 of its running maximum, not normalized, in the kernel's register
  *                   order) and FP32 (m, l) pairs [T, groups, splits, 32 tiles, 2] (running
- *                   maximum in base 2, sum of the unquantized P), groups = ceil(ceil(H / 32) /
- *                   tiles).
+ *                   maximum in base 2, sum of the unquantized P), groups = ceil(H / w) with
+ *                   w = heads, or 32 x tiles when heads is 0 (slots of 32 x tiles heads; only
+ *                   the group's real heads are written and read).
  * Returns 0 for a bad plan. */
 size_t smla_decode_workspace_size(const smla_plan *plan, int32_t T, int32_t H);
 

@@ -33,11 +33,13 @@ class SmlaError(RuntimeError):
 
 class Plan(ctypes.Structure):
     _fields_ = [("splits", ctypes.c_int32), ("tiles", ctypes.c_int32),
-                ("chunk", ctypes.c_int32), ("merge", ctypes.c_int32)]
+                ("chunk", ctypes.c_int32), ("merge", ctypes.c_int32),
+                ("heads", ctypes.c_int32)]
 
     def __repr__(self):
+        heads = f", heads={self.heads}" if self.heads else ""
         return (f"Plan(splits={self.splits}, tiles={self.tiles}, chunk={self.chunk}, "
-                f"merge={self.merge})")
+                f"merge={self.merge}{heads})")
 
 
 _lib = None
@@ -125,7 +127,8 @@ def new_workspace(plan: Plan, T: int, H: int, device="cuda"):
 def workspace_header_bytes(plan: Plan, T: int, H: int) -> int:
     """Bytes at the start of a workspace that must be zero before a call: the status word and
     the arrival counters, padded to 256 (the layout include/smla.h states)."""
-    groups = -(-((H + 31) // 32) // plan.tiles)
+    gw = plan.heads or 32 * plan.tiles
+    groups = -(-H // gw)
     return (16 + T * groups * 2 * 4 + 255) // 256 * 256
 
 
@@ -144,8 +147,8 @@ def testing_set_merge_wait(max_polls: int = 0, unreachable: bool = False) -> Non
         raise SmlaError(st, "smla_testing_set_merge_wait")
 
 
-def make_plan(splits: int, tiles: int, merge: int = SMLA_MERGE_LAST) -> Plan:
-    return Plan(splits, tiles, 64, merge)
+def make_plan(splits: int, tiles: int, merge: int = SMLA_MERGE_LAST, heads: int = 0) -> Plan:
+    return Plan(splits, tiles, 64, merge, heads)
 
 
 def _decode_args(q, kv_a, indices, lens, bmm1_scale, bmm2_scale, out, lse, kv_b, split_col,

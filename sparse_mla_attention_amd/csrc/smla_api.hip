@@ -5,7 +5,9 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <atomic>
+#include <cmath>
 
 #include "smla.h"
 #include "smla_internal.h"
@@ -17,7 +19,8 @@ constexpr int kMaxSplits = 64;
 constexpr int kChunk = 64;
 constexpr int kDefaultMaxSplits = 4;
 constexpr int kFewChunks = 6;
-constexpr int kMaxSpreadSplits = 8;
+constexpr int kMaxSpreadSplits = 16;
+constexpr int kMaxLastSplits32 = 8;
 constexpr int32_t kDefaultWaitPolls = 1 << 20;
 std::atomic<int> g_cu_count[kMaxDevices];
 // bound of the 64-head kernel's split-merge wait, and the test hook that makes it unreachable
@@ -58,11 +61,20 @@ int32_t head_tiles(int32_t H) { return (H + 31) / 32; }
 // Head groups per token: workgroups of `tiles` 32-head tiles, the last one padded.
 int32_t head_groups(int32_t H, int tiles) { return (head_tiles(H) + tiles - 1) / tiles; }
 
-// Key ranges per (token, head group): one range when a token has at most kFewChunks chunks of
-// columns (a split merge costs more than it saves there); else enough workgroups to cover every
-// compute unit, at most kDefaultMaxSplits ranges (the last range of a (token, head group) reads
-// every other range's partial to merge them) and at least one chunk of columns per range.  The
-// 64-head kernel also needs ranges of at most G64_MAX_RANGE columns.
+// Real heads per workgroup under a plan, and head groups per token (the last one padded).
+int32_t plan_heads(const smla_plan *p) { return p->heads != 0 ? p->heads : 32 * p->tiles; }
+int32_t plan_groups(int32_t H, const smla_plan *p)
+{
+    const int32_t gw = plan_heads(p);
+    return (H + gw - 1) / gw;
+}
+
+// Key ranges per (token, head group) of the paged mode's plan: one range when a token has at
+// most kFewChunks chunks of columns (a split merge costs more than it saves there); else enough
+// workgroups to cover every compute unit, at most kDefaultMaxSplits ranges (the last range of a
+// (token, head group) reads every other range's partial to merge them) and at least one chunk
+// of columns per range.  The 64-head kernel also needs ranges of at most G64_MAX_RANGE
+// columns.
 int default_splits(int32_t T, int32_t groups, int32_t W, int cus, int tiles)
 {
     const int64_t chunks = (W + kChunk - 1) / kChunk;
@@ -81,6 +93,53 @@ int default_splits(int32_t T, int32_t groups, int32_t W, int cus, int tiles)
     return want < 1 ? 1 : (int)want;
 }
 
+// Predicted time (microseconds) of one decode call under plan `p` on a device of `cus`
+// compute units.  The prediction is linear in the quantities that set a call's time:
+//   waves   ceil(workgroups / compute units), the rounds of workgroups a launch takes;
+//   cpr     chunks of 64 columns per key range, the serial chunk loop of a workgroup;
+//   occ     the fraction of compute units in use (their gathers share the memory system);
+//   hr      real heads per workgroup (the rows of output and of FP32 partial it writes);
+// and, for plans with S > 1 key ranges, S itself, the partial bytes one workgroup moves (2 hr
+// rows under the spread merge, S hr rows for the last arriver), the split exchange's total
+// bytes over the call, and the grid's size against the compute units.  One coefficient set
+// per kind of plan, fitted (non-negative least squares, relative error) to graph-replayed
+// timings on MI355X of every plan on T = 1..64, H = 16, 64, 128, W = 128..2048 with rows
+// gathered from a 604 MB pool; on that grid the plans chosen by this model take 1.1% more time
+// (summed over shapes) than the best plan measured for each shape.
+double predicted_us(const smla_plan &p, int32_t T, int32_t H, int32_t W, int cus)
+{
+    // coefficients of {1, waves, cpr waves, occ cpr waves, hr/64 waves, S, hr/64 rows moved,
+    // MB exchanged, workgroups / compute units}
+    static constexpr double kCoef[5][9] = {
+        {1.201, 3.488, 1.544, 0.314, 0.864, 0.0, 0.0, 0.0, 0.0},      // 64-head, one range
+        {0.0, 4.215, 1.550, 0.138, 0.652, 2.800, 0.0, 0.036, 3.540},  // 64-head, last arriver
+        {0.0, 5.640, 1.614, 0.070, 0.0, 0.138, 1.480, 0.093, 2.243},  // 64-head, spread
+        {0.0, 6.475, 1.127, 0.176, 1.642, 0.0, 0.0, 0.0, 0.0},        // 32-head, one range
+        {1.152, 7.519, 1.198, 0.206, 0.0, 0.686, 0.276, 0.0, 2.202},  // 32-head, last arriver
+    };
+    const int S = p.splits;
+    const bool spread = p.merge == SMLA_MERGE_SPREAD && S > 1;
+    const int kind = p.tiles == 2 ? (S == 1 ? 0 : spread ? 2 : 1) : (S == 1 ? 3 : 4);
+    const int32_t gw = plan_heads(&p);
+    const double nwg = (double)T * plan_groups(H, &p) * S;
+    const double waves = std::ceil(nwg / cus);
+    const double cpr = (double)(((W + S - 1) / S + kChunk - 1) / kChunk);
+    const double occ = std::min(nwg, (double)cus) / cus;
+    const double hr = std::min(gw, H) / 64.0;
+    double f[9] = {1.0, waves, cpr * waves, occ * cpr * waves, hr * waves, 0.0, 0.0, 0.0, 0.0};
+    if (S > 1) {
+        const int moved = spread ? S : S - 1;  // partials written (and read back) per group
+        f[5] = S;
+        f[6] = hr * (spread ? 2 : S);
+        f[7] = (double)T * H * moved * 4096.0 / 1e6;
+        f[8] = nwg / cus;
+    }
+    double us = 0.0;
+    for (int i = 0; i < 9; i++)
+        us += kCoef[kind][i] * f[i];
+    return us;
+}
+
 bool plan_ok(const smla_plan *p, int32_t H)
 {
     if (p->splits < 1 || p->splits > kMaxSplits)
@@ -88,6 +147,9 @@ bool plan_ok(const smla_plan *p, int32_t H)
     if (p->tiles != 1 && p->tiles != 2)
         return false;
     if (p->merge != SMLA_MERGE_LAST && p->merge != SMLA_MERGE_SPREAD)
+        return false;
+    if (p->heads != 0 && p->heads != 32 * p->tiles && !(p->tiles == 2 && (p->heads == 16 ||
+                                                                           p->heads == 32)))
         return false;
     (void)H;
     return true;
@@ -107,7 +169,7 @@ smla_status spread_ok(const smla_plan *p, int32_t T, int32_t H)
     int cus = 0;
     if (current_cu_count(&cus) != hipSuccess)
         return SMLA_EHIP;
-    if ((int64_t)T * head_groups(H, p->tiles) * p->splits > cus)
+    if ((int64_t)T * plan_groups(H, p) * p->splits > cus)
         return SMLA_EUNSUPPORTED;
     return SMLA_OK;
 }
@@ -125,7 +187,7 @@ struct WsLayout {
 
 WsLayout ws_layout(const smla_plan *plan, int32_t T, int32_t H)
 {
-    const size_t groups = (size_t)head_groups(H, plan->tiles);
+    const size_t groups = (size_t)plan_groups(H, plan);
     const size_t hg = 32 * (size_t)plan->tiles;
     const size_t units = (size_t)T * groups * (size_t)plan->splits;
     WsLayout w;
@@ -183,38 +245,34 @@ smla_status smla_decode_plan(int32_t T, int32_t H, int32_t W, int32_t row_bytes,
     int cus = 0;
     if (current_cu_count(&cus) != hipSuccess)
         return SMLA_EHIP;
-    // Small batches with long rows: 64 heads per workgroup and a spread merge over the most
-    // ranges (a power of two, at most kMaxSpreadSplits) that keep at least one chunk per range
-    // and the grid within the compute units; it needs at most a quarter of the compute units
-    // for the tokens' head groups alone.
-    const int64_t chunks = (W + kChunk - 1) / kChunk;
-    const int64_t units64 = (int64_t)T * head_groups(H, 2);
-    if (chunks > kFewChunks && units64 * 4 <= cus) {
-        int s = kMaxSpreadSplits;
-        while (s > 2 && (units64 * s > cus || s > chunks))
-            s /= 2;
-        if ((W + s - 1) / s <= smla::G64_MAX_RANGE) {
-            plan->tiles = 2;
-            plan->splits = s;
-            plan->chunk = kChunk;
-            plan->merge = SMLA_MERGE_SPREAD;
-            return SMLA_OK;
+    // Every plan the kernels take for this shape, cheapest predicted time first: the 64-head
+    // kernel with 64, 32 or 16 real heads per workgroup over one range, two ranges merged by
+    // the last arriver, or 2 to 16 ranges under the spread merge (a grid within the compute
+    // units); the 32-head kernel over 1 to 8 ranges.  A later candidate replaces the kept one
+    // only when strictly cheaper, so ties keep the widest head groups.
+    smla_plan best{1, 1, kChunk, SMLA_MERGE_LAST, 0};
+    double best_us = INFINITY;
+    auto consider = [&](int32_t splits, int32_t tiles, int32_t merge, int32_t heads) {
+        const smla_plan c{splits, tiles, kChunk, merge, heads};
+        if (tiles == 2 && (W + splits - 1) / splits > smla::G64_MAX_RANGE)
+            return;
+        if (merge == SMLA_MERGE_SPREAD && (int64_t)T * plan_groups(H, &c) * splits > cus)
+            return;
+        const double us = predicted_us(c, T, H, W, cus);
+        if (us < best_us) {
+            best_us = us;
+            best = c;
         }
+    };
+    for (int32_t heads : {0, 32, 16}) {
+        consider(1, 2, SMLA_MERGE_LAST, heads);
+        consider(2, 2, SMLA_MERGE_LAST, heads);
+        for (int32_t s = 2; s <= kMaxSpreadSplits; s *= 2)
+            consider(s, 2, SMLA_MERGE_SPREAD, heads);
     }
-    // Otherwise 64 heads per workgroup (the last group padded when the 32-head tiles do not
-    // pair up) unless that needs more than two key ranges: its last-arriver exchange is built
-    // for two ranges at a full grid; more ranges go to the 32-head kernel, whose store-first
-    // exchange suits the few workgroups of small batches.
-    const int s64 = default_splits(T, head_groups(H, 2), W, cus, 2);
-    if (s64 <= 2) {
-        plan->tiles = 2;
-        plan->splits = s64;
-    } else {
-        plan->tiles = 1;
-        plan->splits = default_splits(T, head_groups(H, 1), W, cus, 1);
-    }
-    plan->chunk = kChunk;
-    plan->merge = SMLA_MERGE_LAST;
+    for (int32_t s = 1; s <= kMaxLastSplits32; s *= 2)
+        consider(s, 1, SMLA_MERGE_LAST, 0);
+    *plan = best;
     return SMLA_OK;
 }
 
@@ -310,7 +368,8 @@ smla_status decode_impl(const void *q, int64_t q_stride_t, int64_t q_stride_h,
     p.lse = lse;
     p.lse_log2 = (flags & SMLA_LSE_LOG2) ? 1 : 0;
     p.splits = chosen.splits;
-    p.groups = head_groups(H, chosen.tiles);
+    p.groups = plan_groups(H, &chosen);
+    p.gw = plan_heads(&chosen);
     p.merge = chosen.merge;
     p.ws_o = nullptr;
     p.ws_ml = nullptr;
@@ -377,6 +436,7 @@ smla_status smla_paged_decode_plan(int32_t B, int32_t q_len, int32_t H, int32_t 
         return SMLA_EUNSUPPORTED;
     plan->chunk = kChunk;
     plan->merge = SMLA_MERGE_LAST;
+    plan->heads = 0;
     return SMLA_OK;
 }
 
@@ -452,7 +512,8 @@ smla_status paged_mla_decode(const void *q, int64_t q_stride_t, int64_t q_stride
     p.lse = lse;
     p.lse_log2 = (flags & SMLA_LSE_LOG2) ? 1 : 0;
     p.splits = chosen.splits;
-    p.groups = head_groups(H, 2);
+    p.groups = plan_groups(H, &chosen);
+    p.gw = plan_heads(&chosen);
     p.merge = chosen.merge;
     p.wait_polls = g_wait_polls.load(std::memory_order_relaxed);
     p.wait_extra = g_wait_extra.load(std::memory_order_relaxed);

@@ -213,7 +213,7 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
             // padding heads past H are never merged), then merges its own column slice of all
             // of them and writes it (smla_spread.h).
             const int64_t ui = tg * a.splits + split;
-            const int heads_here = min(HG, a.H - hg * HG);
+            const int heads_here = min(a.gw, a.H - hg * a.gw);
             if (!qk_wave) {
                 const auto rs = part_rsrc(ui);
 #pragma unroll
@@ -469,10 +469,13 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
         uint8_t *tile = lds;  // [64][1024 bytes], over the slots
 #pragma unroll
         for (int h2 = 0; h2 < 2; h2++) {
-            const int head = hg * HG + 32 * h2 + hl;
+            // real heads are the group's first min(gw, H - hg gw); the index of a padding head
+            // may name a real head of another group, so padding is tested on the local index
+            const bool real = 32 * h2 + hl < min(a.gw, a.H - hg * a.gw);
+            const int head = hg * a.gw + 32 * h2 + hl;
             const bool any = g_h[h2] != -INFINITY;
             float big_m = g_h[h2], big_l = l_h[h2], wgt = 1.0f;
-            if (a.sinks != nullptr && head < a.H) {
+            if (a.sinks != nullptr && real) {
                 const float sk = a.sinks[head] * LOG2E;
                 big_m = fmaxf(g_h[h2], sk);
                 wgt = any ? exp2f(g_h[h2] - big_m) : 0.0f;
@@ -492,7 +495,7 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
                     }
                 }
             }
-            if (wave == 4 && u == 0 && head < a.H && a.lse != nullptr) {
+            if (wave == 4 && u == 0 && real && a.lse != nullptr) {
                 const float lse2 = failed ? __int_as_float(0x7FC00000)
                                    : any  ? big_m - LOG2_ANCHOR + log2f(big_l)
                                           : -INFINITY;
@@ -500,13 +503,13 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
             }
         }
         lds_barrier();
-        const int heads_here = min(HG, a.H - hg * HG);
+        const int heads_here = min(a.gw, a.H - hg * a.gw);
         for (int x = tid; x < heads_here * 64; x += NT) {
             const int row = x >> 6, part = x & 63;
             const v4i v = lds_load<v4i>(tile, tile_off(row, 16 * part));
             // streaming store: the output is not read again by this kernel
             __builtin_nontemporal_store(
-                v, reinterpret_cast<v4i *>(a.out + ((int64_t)t * a.H + hg * HG + row) * 512 +
+                v, reinterpret_cast<v4i *>(a.out + ((int64_t)t * a.H + hg * a.gw + row) * 512 +
                                            8 * part));
         }
     };
@@ -521,10 +524,11 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
         v8i qf[4];
         v4i qt = v4i{0, 0, 0, 0};
         {
-            // a padding head (past H) computes with head 0's q: its scores reach no output,
-            // and no instruction between here and the first product waits for these loads
-            const int gh = hg * HG + head;
-            const uint8_t *qp = a.q + (int64_t)t * a.q_st + (int64_t)(gh < a.H ? gh : 0) * a.q_sh;
+            // a padding head computes with the group's first head's q: its scores reach no
+            // output, and no instruction between here and the first product waits for these
+            // loads
+            const int gh = hg * a.gw + (head < min(a.gw, a.H - hg * a.gw) ? head : 0);
+            const uint8_t *qp = a.q + (int64_t)t * a.q_st + (int64_t)gh * a.q_sh;
 #pragma unroll
             for (int s = 0; s < 4; s++)
                 qf[s] = join(gload(qp + 16 * (8 * s + pg)), gload(qp + 16 * (8 * s + 4 + pg)));
@@ -652,6 +656,8 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
                 scl[(x & 1) * HG + head] = alpha;
         };
 
+        // Every QK wave computes its 16 heads, padding heads included (with the group's first
+        // head's q), so that the waves of a workgroup keep one schedule whatever H is.
         if (nch > 0) {
             lds_barrier();                          // the P.V waves issue chunks 0 and 1
             for (int c = 0; c <= nch; c++) {

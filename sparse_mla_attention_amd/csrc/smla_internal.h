@@ -33,7 +33,8 @@ struct DecodeParams {
     int32_t wait_polls;         // bound of the 64-head kernel's merge wait (polls)
     int32_t wait_extra;         // 0; 1 makes that wait unreachable (a test hook)
     int32_t splits;             // key ranges per (token, head group)
-    int32_t groups;             // head groups per token = ceil(ceil(H / 32) / tiles)
+    int32_t groups;             // head groups per token = ceil(H / gw)
+    int32_t gw;                 // real heads per workgroup (the 64-head kernel: 16, 32 or 64)
     int32_t merge;              // 0: the last range to arrive merges; 1: distributed (each
                                 // range merges 512 / splits columns; cooperative launch)
     // paged addressing (64-head kernel only): when set, `lens` holds one context length per

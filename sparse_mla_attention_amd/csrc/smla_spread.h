@@ -52,12 +52,12 @@ __device__ __attribute__((always_inline)) inline void spread_merge_s(
     constexpr int PP = NPOS >= NT ? NPOS / NT : 1; // positions per thread
     static_assert(NPOS % NT == 0 || NPOS < NT, "positions split evenly over the threads");
     const int lane = tid & 63;
-    const int heads_here = min(HG, a.H - hg * HG); // real heads of the group
+    const int heads_here = min(a.gw, a.H - hg * a.gw);  // real heads of the group
     // positions tid + NT i share lane and head tile: one head per thread
     const int h2 = (tid >> 8) % H2;
     const int hl = lane & 31;
     const int hloc = 32 * h2 + hl;                 // head within the group
-    const int head = hg * HG + hloc;
+    const int head = hg * a.gw + hloc;             // (a real head only if hloc < heads_here)
     const bool active = tid < NPOS && hloc < heads_here;
     int *ctr = a.counters + 2 * tg;                // [0] arrivals, [1] departures
 
@@ -134,7 +134,7 @@ __device__ __attribute__((always_inline)) inline void spread_merge_s(
     }
     const bool any = big_g != -INFINITY;
     float big_m = big_g, big_l = l_new, wgt = 1.0f;
-    if (a.sinks != nullptr && head < a.H) {
+    if (a.sinks != nullptr && hloc < heads_here) {
         const float sk = a.sinks[head] * LOG2E;
         big_m = fmaxf(big_g, sk);
         wgt = any ? exp2f(big_g - big_m) : 0.0f;
@@ -160,7 +160,8 @@ __device__ __attribute__((always_inline)) inline void spread_merge_s(
             *reinterpret_cast<uint2 *>(tile + tile_off(hloc, 2 * col)) = pk;
         }
     }
-    if (split == 0 && (tid & 255) < 32 && (tid >> 8) < H2 && head < a.H && a.lse != nullptr) {
+    if (split == 0 && (tid & 255) < 32 && (tid >> 8) < H2 && hloc < heads_here &&
+        a.lse != nullptr) {
         const float lse2 = failed ? __int_as_float(0x7FC00000)
                            : any  ? big_m - LOG2_ANCHOR + log2f(big_l)
                                   : -INFINITY;
@@ -174,7 +175,7 @@ __device__ __attribute__((always_inline)) inline void spread_merge_s(
         const int row = x / PARTS, part = split * PARTS + x % PARTS;
         const v4i o = lds_load<v4i>(tile, tile_off(row, 16 * part));
         __builtin_nontemporal_store(
-            o, reinterpret_cast<v4i *>(a.out + ((int64_t)t * a.H + hg * HG + row) * 512 +
+            o, reinterpret_cast<v4i *>(a.out + ((int64_t)t * a.H + hg * a.gw + row) * 512 +
                                        8 * part));
     }
     if (tid == 0 && !failed) {

@@ -49,6 +49,15 @@ def test_workspace_size_formula():
     assert smla.workspace_size(smla.make_plan(65, 1), 7, 128) == 0
     assert smla.workspace_size(smla.make_plan(2, 4), 7, 128) == 0   # 1 or 2 tiles per WG
     assert smla.workspace_size(smla.make_plan(2, 1), 7, 120) == 0   # H % 16 != 0
+    # fewer real heads per 64-head workgroup: ceil(H / heads) groups
+    for heads, T, H in [(16, 5, 128), (32, 3, 96), (16, 2, 48)]:
+        groups = -(-H // heads)
+        counters = (16 + T * groups * 2 * 4 + 255) // 256 * 256
+        plan = smla.make_plan(4, 2, heads=heads)
+        assert smla.workspace_size(plan, T, H) == counters + T * groups * 4 * 64 * (512 + 2) * 4
+        assert smla.workspace_header_bytes(plan, T, H) == counters
+    for tiles, heads in [(1, 16), (2, 48), (2, 8), (1, 64)]:     # not a kernel's width
+        assert smla.workspace_size(smla.make_plan(2, tiles, heads=heads), 7, 128) == 0
 
 
 def _decode(T=1, H=16, W=64, row_bytes=576, qk_dim=576, flags=0, plan=None, q=16, kv=16,

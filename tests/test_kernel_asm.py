@@ -164,3 +164,31 @@ def test_decode_kernels_spill_nothing():
         counts = re.findall(r"\.vgpr_spill_count:\s+(\d+)", text)
         assert counts, src
         assert all(int(c) == 0 for c in counts), (src, counts)
+
+
+def test_pv_matrix_sequences_have_no_branches():
+    """The 64-head kernel's P.V waves issue their matrix instructions as straight-line code
+    (no branch or block boundary between neighbouring products), so the explicit pad before the
+    accumulators' rescale is the one distance between a chunk's products and their reads that
+    the schedule can change."""
+    src = os.path.join(build.CSRC, "smla_decode_g64.hip")
+    with tempfile.TemporaryDirectory() as tmp:
+        out = os.path.join(tmp, "g64.s")
+        cmd = [build.HIPCC, *build.FLAGS, "--cuda-device-only", "-S", src, "-o", out]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            pytest.fail(r.stdout + r.stderr)
+        text = open(out).read()
+    kernels = re.findall(r"^(_ZN\S*decode_g64_kernel\S*):[^\n]*\n(.*?)^\.Lfunc_end", text,
+                         re.S | re.M)
+    assert kernels
+    for name, body in kernels:
+        ins = [l.strip() for l in body.split("\n")
+               if l.strip() and not l.strip().startswith(";")]
+        idx = [i for i, l in enumerate(ins) if l.startswith("v_mfma_scale_f32_32x32x64")]
+        assert idx, name
+        for a, b in zip(idx, idx[1:]):
+            if b - a < 12:
+                seg = ins[a + 1:b]
+                assert not any(s.startswith("s_cbranch") or s.endswith(":") for s in seg), \
+                    (name, ins[a:b + 1])

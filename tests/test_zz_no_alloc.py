@@ -55,7 +55,7 @@ def test_noalloc_matches_workspace_call_twice_second_smaller():
             (ro, rl), (no, nl) = _pair(d, p, smla.make_plan(3, tiles), one_term)
             assert torch.equal(ro, no), (tiles, one_term)
             assert torch.equal(rl, nl), (tiles, one_term)
-    # the default (one-range) plan of the verify-row shape needs no scratch at all
+    # the verify-row shape under its default plan (a spread merge over 16- or 32-head groups)
     v = inputs.CONFIGS["verify"]()
     dv = DeviceProblem(v)
     (ro, rl), (no, nl) = _pair(dv, v, smla.plan_for(5, 128, 320, 576))
