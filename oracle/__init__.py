@@ -65,6 +65,8 @@ def lib():
         L.oracle_decode_exact.restype = ctypes.c_int
         L.oracle_decode_mimic.argtypes = common + [I32, I32, D, I32, I32, P, I32, P, P]
         L.oracle_decode_mimic.restype = ctypes.c_int
+        L.oracle_decode_chunk_local.argtypes = common + [I32, D, I32, I32, P, I32, P, P]
+        L.oracle_decode_chunk_local.restype = ctypes.c_int
         L.oracle_lse_merge.argtypes = [P, P, I32, I32, I32, I32, U32, P, P]
         L.oracle_lse_merge.restype = ctypes.c_int
         L.oracle_paged_decode_exact.argtypes = [P, I64, I64, P, I64, I32, I64, P, I32, P, I32,
@@ -150,6 +152,23 @@ def decode_mimic(p, splits, chunk, anchor=448.0, terms=1, quantize=True, lse_log
     _check(lib().oracle_decode_mimic(*args, LSE_LOG2 if lse_log2 else 0, int(splits), int(chunk),
                                      float(anchor), int(terms), 1 if quantize else 0,
                                      _ptr(u), n, _ptr(out), _ptr(lse)))
+    del keep
+    return out, lse
+
+
+def decode_chunk_local(p, width=128, anchor=256.0, terms=1, quantize=True, lse_log2=False,
+                       units=None):
+    """Chunk-local mode (the sparse_mla_cute page, "How."): one softmax per chunk of `width`
+    columns at the chunk's own maximum, P at `anchor` of it as E4M3, the chunks merged with
+    weights 2^(m_k - M) over the chunks and the sink."""
+    args, keep, T, H = _problem_args(p)
+    u, n = _units_array(units)
+    count = n if u is not None else T * H
+    out = np.empty((count, 512), dtype=np.float64)
+    lse = np.empty((count,), dtype=np.float64)
+    _check(lib().oracle_decode_chunk_local(*args, LSE_LOG2 if lse_log2 else 0, int(width),
+                                           float(anchor), int(terms), 1 if quantize else 0,
+                                           _ptr(u), n, _ptr(out), _ptr(lse)))
     del keep
     return out, lse
 

@@ -19,6 +19,10 @@
  *       split merge (weights exp2(max_c - max), BF16(sum*k_scale/total),
  *       LSE = max + log2(total/448)), the "Rows of count 0" rule, and
  *       SparseDcpDecode.kernel's contiguous key split of the clamped count.
+ *   [sparse_mla_cute page]  "How.": the chunk-local recipe (one softmax per
+ *       128-column chunk at its own maximum, P = 256 exp2(S - m_c) as FP8,
+ *       the chunks' partials weighted by exp2(m_c - M) / L over the chunks
+ *       and the sink).
  *   [dcp page]  DcpValue.merge: LSE-weighted merge of D sources, weights
  *       exp2(lse - top) / sum, empty sources weighted 0.
  *
@@ -29,10 +33,13 @@
  * Parity pins (tests, CPU only): E4M3 decode against torch.float8_e4m3fn for
  * all 256 codes; exact mode against dense float64 scaled-dot-product attention
  * on materialised rows; softmax invariants; the zero-count rule; mimic mode
- * reducing to exact mode when P is not quantized; lse_merge split consistency.
- * The E4M3-P recipe (mimic mode) has no printed worked values on the pages:
- * its quantization steps are pinned only through those reductions and
- * invariants ("parity unpinned" for the recipe's rounding details).
+ * and chunk-local mode reducing to exact mode when P is not quantized;
+ * lse_merge split consistency; chunk-local mode equal to lse_merge of its
+ * chunks computed one by one, and to a hand-worked two-chunk example.
+ * The E4M3-P recipes have no printed worked values on the pages: their
+ * quantization steps are pinned only through those reductions, invariants
+ * and the hand-worked example ("parity unpinned" for the recipes' rounding
+ * details beyond them).
  */
 #include <math.h>
 #include <stdint.h>
@@ -429,6 +436,150 @@ int oracle_decode_mimic(
             lse[u] *= log(2.0);
     }
     free(m_s); free(l_s); free(acc_s); free(s2); free(phat);
+    return status;
+}
+
+/* ---------------------------------------------------------------------------
+ * C2b: chunk-local mode, the sparse_mla_cute page's "How." recipe.
+ *
+ * Per (t, h): the clamped count n is cut into chunks of `width` consecutive
+ * columns, chunk k = [k * width, min((k + 1) * width, n)) (chunk 0 is the
+ * first `width` columns, the sliding-window columns at width 128).  Each
+ * chunk runs its own softmax in base 2, with no running maximum:
+ *   s2 = s * log2(e)  (-inf when the column is inactive)
+ *   m_k = max over the chunk of s2   (-inf when no column of it is active)
+ *   p = 2^(s2 - m_k + log2 anchor)   (double; anchor 256 on that page)
+ *   p_hat = E4M3(p)      (terms = 1: P as FP8)
+ *   p_hat = E4M3(p) + E4M3(16 (p - E4M3(p))) / 16   (terms = 2)
+ *   l_k = sum p  (the unquantized P);  acc_k = sum p_hat v
+ * then the chunks merge with the sink: M = max(max_k m_k, sink2),
+ * w_k = 2^(m_k - M), L = sum w_k l_k (+ anchor * 2^(sink2 - M)),
+ * out = bmm2 * sum w_k acc_k / L, LSE2 = M - log2 anchor + log2 L.
+ * With `quantize` = 0, p_hat = p, which reduces to exact mode.
+ * ------------------------------------------------------------------------- */
+int oracle_decode_chunk_local(
+    const uint8_t *q, int64_t q_stride_t, int64_t q_stride_h,
+    const uint8_t *kv_a, int64_t rows_a,
+    const uint8_t *kv_b, int64_t rows_b, int32_t split_col,
+    int32_t row_bytes, int32_t qk_dim,
+    const int32_t *indices, const int32_t *lens,
+    int32_t T, int32_t H, int32_t W,
+    double bmm1, double bmm2, const float *sinks, uint32_t flags,
+    int32_t width, double anchor, int32_t terms, int32_t quantize,
+    const int32_t *units, int32_t n_units,
+    double *out, double *lse)
+{
+    problem p = {q, q_stride_t, q_stride_h, kv_a, rows_a, kv_b, rows_b, split_col,
+                 row_bytes, qk_dim, indices, lens, T, H, W, bmm1, bmm2, sinks};
+    const double log2e = 1.0 / log(2.0);
+    int status = check_problem(&p);
+    int count = units ? n_units : T * H;
+    double *s2, *acc_k;
+    if (status != ORACLE_OK)
+        return status;
+    if (width < 1 || !(anchor > 0) || terms < 1 || terms > 2)
+        return ORACLE_EBADARG;
+    s2 = (double *)malloc(sizeof(double) * (size_t)width);
+    acc_k = (double *)malloc(sizeof(double) * V_DIM);
+    if (!s2 || !acc_k) {
+        free(s2); free(acc_k);
+        return ORACLE_EBADARG;
+    }
+    for (int u = 0; u < count && status == ORACLE_OK; u++) {
+        int t = units ? units[2 * u] : u / H;
+        int h = units ? units[2 * u + 1] : u % H;
+        int n, any = 0;
+        double big_m = -INFINITY, big_l = 0.0, sink2 = -INFINITY;
+        double *o = out + (int64_t)u * V_DIM;
+        if (t < 0 || t >= T || h < 0 || h >= H) {
+            status = ORACLE_EBADARG;
+            break;
+        }
+        n = active_count(&p, t);
+        /* pass 1: every chunk's maximum, hence M (the merge needs it before any weight) */
+        for (int base = 0; base < n && status == ORACLE_OK; base += width) {
+            int cnt = n - base < width ? n - base : width;
+            for (int i = 0; i < cnt; i++) {
+                if (is_active(&p, t, base + i, n)) {
+                    const uint8_t *row = row_of(&p, t, base + i, &status);
+                    double v;
+                    if (!row)
+                        break;
+                    v = bmm1 * dot_qk(&p, t, h, row, &status) * log2e;
+                    any = 1;
+                    if (v > big_m)
+                        big_m = v;
+                }
+            }
+        }
+        if (status != ORACLE_OK)
+            break;
+        for (int j = 0; j < V_DIM; j++)
+            o[j] = 0.0;
+        if (!any) { /* zero-count rule */
+            lse[u] = -INFINITY;
+            continue;
+        }
+        if (sinks) {
+            sink2 = (double)sinks[h] * log2e;
+            if (sink2 > big_m)
+                big_m = sink2;
+        }
+        /* pass 2: each chunk's softmax at its own maximum, its P.V, and its weighted share */
+        for (int base = 0; base < n && status == ORACLE_OK; base += width) {
+            int cnt = n - base < width ? n - base : width;
+            double m_k = -INFINITY, l_k = 0.0, w_k;
+            for (int i = 0; i < cnt; i++) {
+                s2[i] = -INFINITY;
+                if (is_active(&p, t, base + i, n)) {
+                    const uint8_t *row = row_of(&p, t, base + i, &status);
+                    if (!row)
+                        break;
+                    s2[i] = bmm1 * dot_qk(&p, t, h, row, &status) * log2e;
+                }
+                if (s2[i] > m_k)
+                    m_k = s2[i];
+            }
+            if (status != ORACLE_OK || m_k == -INFINITY)
+                continue; /* a chunk with no active column adds nothing */
+            for (int j = 0; j < V_DIM; j++)
+                acc_k[j] = 0.0;
+            for (int i = 0; i < cnt; i++) {
+                double pv, ph, hi;
+                const uint8_t *row;
+                if (s2[i] == -INFINITY)
+                    continue;
+                pv = exp2(s2[i] - m_k + log2(anchor));
+                l_k += pv;
+                ph = pv;
+                if (quantize) {
+                    hi = oracle_e4m3_value(oracle_e4m3_encode(pv));
+                    ph = hi;
+                    if (terms == 2)
+                        ph += oracle_e4m3_value(oracle_e4m3_encode(16.0 * (pv - hi))) / 16.0;
+                }
+                if (ph == 0.0)
+                    continue;
+                row = row_of(&p, t, base + i, &status);
+                for (int j = 0; j < V_DIM; j++)
+                    acc_k[j] += ph * oracle_e4m3_value(row[j]);
+            }
+            w_k = exp2(m_k - big_m);
+            big_l += w_k * l_k;
+            for (int j = 0; j < V_DIM; j++)
+                o[j] += w_k * acc_k[j];
+        }
+        if (status != ORACLE_OK)
+            break;
+        if (sinks)
+            big_l += anchor * exp2(sink2 - big_m);
+        for (int j = 0; j < V_DIM; j++)
+            o[j] = bmm2 * o[j] / big_l;
+        lse[u] = big_m - log2(anchor) + log2(big_l); /* base 2 */
+        if (!(flags & ORACLE_LSE_LOG2))
+            lse[u] *= log(2.0);
+    }
+    free(s2); free(acc_k);
     return status;
 }
 

@@ -392,6 +392,122 @@ def test_mimic_anchor_holds_the_running_max_exactly():
 
 
 # ---------------------------------------------------------------------------
+# chunk-local mode (the sparse_mla_cute page, "How.": one softmax per 128-column chunk at the
+# chunk's own maximum, P = 256 exp2(S - m_c) as FP8, chunks merged by exp2(m_c - M) / L)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("width", [128, 7, 1])
+def test_chunk_local_without_quantization_is_exact(width):
+    p = inputs.random_problem(40, 3, 16, 300, pool_rows=900, neg_frac=0.2, lens=[300, 129, 0],
+                              sinks=True, two_pools=True, split_col=128, rows_b=700)
+    out, lse = oracle.decode_exact(p)
+    oc, lc = oracle.decode_chunk_local(p, width=width, quantize=False)
+    np.testing.assert_allclose(oc, out, rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(lc[np.isfinite(lse)], lse[np.isfinite(lse)], rtol=1e-12)
+    assert np.all(oc[~np.isfinite(lse)] == 0) and np.all(lc[~np.isfinite(lse)] == -np.inf)
+
+
+def test_chunk_local_is_the_lse_merge_of_its_chunks():
+    """Each chunk's output is its own quantized P.V over its own unquantized sum, so decoding
+    every chunk alone (the other columns masked) and combining the results by their LSEs
+    (out = sum_k 2^(lse_k - M) out_k / sum_k 2^(lse_k - M), lse = M + log2 sum_k 2^(lse_k - M))
+    gives the whole call, P rounding included; a mistake in a chunk's weight, its maximum, the
+    anchor's place in the LSE or the chunk boundaries breaks the identity."""
+    p = inputs.random_problem(41, 2, 16, 300, pool_rows=900, neg_frac=0.1, lens=[300, 200])
+    for terms in (1, 2):
+        whole, whole_lse = oracle.decode_chunk_local(p, terms=terms, lse_log2=True)
+        outs, lses = [], []
+        for lo in (0, 128, 256):
+            q = dict(p)
+            idx = np.full_like(p["indices"], -1)
+            idx[:, lo:lo + 128] = p["indices"][:, lo:lo + 128]
+            q["indices"] = idx
+            o, l = oracle.decode_chunk_local(q, terms=terms, lse_log2=True)
+            outs.append(o)
+            lses.append(l)
+        lses = np.stack(lses)                   # [3, T*H]
+        top = lses.max(axis=0)
+        wgt = np.where(np.isfinite(lses), np.exp2(lses - top), 0.0)
+        merged = (wgt[:, :, None] * np.stack(outs)).sum(axis=0) / wgt.sum(axis=0)[:, None]
+        np.testing.assert_allclose(merged, whole, rtol=1e-11, atol=1e-13)
+        np.testing.assert_allclose(top + np.log2(wgt.sum(axis=0)), whole_lse, rtol=1e-12)
+
+
+def _rows_problem(dots, markers, c=2.0 / 3.0):
+    """One head, q = e_0, row r holds dots[r] at column 0 (base-2 score c * dots[r]) and 448 at
+    column col for each (row, col) in markers."""
+    def e4(x):
+        return int(torch.tensor([x], dtype=torch.float64).to(torch.float8_e4m3fn)
+                   .view(torch.uint8)[0])
+    n = len(dots)
+    q = np.zeros((1, 1, 576), np.uint8)
+    q[0, 0, 0] = e4(1.0)
+    kv = np.zeros((n, 576), np.uint8)
+    for r, x in enumerate(dots):
+        kv[r, 0] = e4(x)
+    for r, col in markers:
+        kv[r, col] = e4(448.0)
+    return dict(q=q, kv_a=kv, kv_b=None, split_col=n, qk_dim=576,
+                indices=np.arange(n, dtype=np.int32)[None], lens=np.array([n], np.int32),
+                sinks=None, bmm1=c * LN2, bmm2=1.0)
+
+
+def test_chunk_local_worked_example():
+    """Hand-worked chunk-local recipe, chunks of two columns, base-2 scores 3, 2.5 | 1.5, 0.5
+    (dot products 4.5, 3.75, 2.25, 0.75 at 2/3 per unit); row 1 has 448 at column 100, row 3
+    at column 200.
+      chunk 0: m = 3: P = 256 (exact), 256 * 2^-0.5 = 181.019 -> E4M3 176 (grid step 16 on
+               [128, 256)); l_0 = 437.019.
+      chunk 1: its own m = 1.5: P = 256, 128 (both exact); l_1 = 384; weight 2^(1.5 - 3).
+    L = 437.019 + 384 * 2^-1.5 = 572.784; out[100] = 176 * 448 / L; out[200] = 128 * 2^-1.5
+    * 448 / L (a running maximum would have rounded that P: 256 * 2^-2.5 = 45.25 -> 44);
+    LSE2 = 3 - log2(256) + log2(L).  At anchor 448 row 1's P is 448 * 2^-0.5 = 316.78 -> 320
+    (step 32).  Two terms: E4M3(16 (181.019 - 176)) = E4M3(80.31) = 80, so P = 176 + 5."""
+    p = _rows_problem([4.5, 3.75, 2.25, 0.75], [(1, 100), (3, 200)])
+    r = 2.0 ** -1.5
+    p1 = 256.0 * 2.0 ** -0.5
+    L = 256.0 + p1 + 384.0 * r
+    out, lse = oracle.decode_chunk_local(p, width=2, terms=1, lse_log2=True)
+    assert abs(out[0, 100] - 176.0 * 448.0 / L) < 1e-12
+    assert abs(out[0, 200] - 128.0 * r * 448.0 / L) < 1e-12
+    assert abs(out[0, 0] - (256.0 * 4.5 + 176.0 * 3.75 + r * (256.0 * 2.25 + 128.0 * 0.75)) / L) \
+        < 1e-12
+    assert abs(lse[0] - (3.0 - 8.0 + math.log2(L))) < 1e-12
+    out2, _ = oracle.decode_chunk_local(p, width=2, terms=2, lse_log2=True)
+    assert abs(out2[0, 100] - 181.0 * 448.0 / L) < 1e-12
+    out448, _ = oracle.decode_chunk_local(p, width=2, anchor=448.0, terms=1, lse_log2=True)
+    L448 = (256.0 + p1 + 384.0 * r) * 448.0 / 256.0
+    assert abs(out448[0, 100] - 320.0 * 448.0 / L448) < 1e-12
+    # the attn_sparse recipe (running maximum over chunks of two) rounds row 3's P
+    om, _ = oracle.decode_mimic(p, splits=1, chunk=2, anchor=256.0, terms=1, lse_log2=True)
+    assert abs(om[0, 200] - 44.0 * 448.0 / L) < 1e-12
+
+
+def test_chunk_local_single_chunk_matches_recipe_with_torch_quantizer():
+    """One chunk: P = 256 * 2^(s2 - max) quantized by torch's E4M3 cast, over the unquantized
+    sum."""
+    p = inputs.random_problem(42, 1, 16, 100, pool_rows=200)
+    rows = _e4m3_f64(p["kv_a"][p["indices"][0]]).numpy()
+    q = _e4m3_f64(p["q"][0]).numpy()
+    s2 = p["bmm1"] * (q @ rows[:, :576].T) / LN2
+    m = s2.max(axis=1, keepdims=True)
+    pv = np.exp2(s2 - m + 8.0)
+    phat = torch.from_numpy(pv).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    ref = p["bmm2"] * (phat @ rows[:, :512]) / pv.sum(1, keepdims=True)
+    ref_lse = (m[:, 0] - 8.0 + np.log2(pv.sum(1))) * LN2
+    oc, lc = oracle.decode_chunk_local(p, terms=1)
+    np.testing.assert_allclose(oc, ref, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(lc, ref_lse, rtol=1e-13)
+
+
+def test_chunk_local_zero_count_rule():
+    p = inputs.random_problem(43, 2, 16, 140, pool_rows=300, lens=[0, 140])
+    p["indices"][1, :] = -1
+    out, lse = oracle.decode_chunk_local(p)
+    assert np.all(out == 0) and np.all(lse == -np.inf)
+
+
+# ---------------------------------------------------------------------------
 # lse_merge
 # ---------------------------------------------------------------------------
 
