@@ -54,6 +54,17 @@ typedef int32_t smla_status;
                                 lo = E4M3(16 (P - hi)), which keeps the E4M3 quantization but
                                 reaches FP32-level accuracy (relative output error ~1e-3
                                 instead of ~2e-2). */
+#define SMLA_P_CHUNK_LOCAL 0x4u /* sparse_mla_decode: the chunk-local recipe of the
+                                sparse_mla_cute page ("How."): each 128-column window of a
+                                token's columns, [128 k, 128 k + 128) of its clamped count, is
+                                one key range with its own softmax, P = E4M3(256 x 2^(s2 - m_k))
+                                at the window's own maximum m_k (one E4M3 term; no running
+                                maximum), FP32 sums of the unquantized P; the windows then merge
+                                as split partials with weights 2^(m_k - M), the sink weighted
+                                256 x 2^(sink2 - M), LSE2 = M - 8 + log2 L.  The plan must
+                                have tiles = 2 and splits = ceil(W / 128) (smla_decode_plan
+                                gives such a plan when passed this flag), else
+                                SMLA_EUNSUPPORTED.  SMLA_P_ONE_TERM is implied. */
 
 /* The launch decomposition of one sparse_mla_decode call.  A workgroup takes one token, a
  * group of `tiles` 32-head tiles (heads padded up to a multiple of 32) and one of `splits`
@@ -72,12 +83,13 @@ typedef struct smla_plan {
     int32_t merge;  /* how the split partials are merged (ignored when splits == 1):
                        SMLA_MERGE_LAST: the last range of a (token, head group) to finish merges
                        every column; any grid size.
-                       SMLA_MERGE_SPREAD: range s merges output columns [s, s+1) * 512 / splits
-                       of every head, so the merge's reads are spread over all the ranges'
-                       workgroups.  The ranges of a (token, head group) wait for each other
+                       SMLA_MERGE_SPREAD: range s merges the output columns of 32-column tiles
+                       [16 s / splits, 16 (s + 1) / splits) of every head (512 / splits columns
+                       when splits divides 16), so the merge's reads are spread over all the
+                       ranges' workgroups.  The ranges of a (token, head group) wait for each other
                        (a bounded wait, as under sparse_mla_decode), so every workgroup must be
                        resident at once: tiles must be 2 (the 64-head kernel; the 32-head
-                       kernel has no spread merge), splits 2, 4, 8 or 16 and the grid, tokens x
+                       kernel has no spread merge), splits 2 to 16 and the grid, tokens x
                        head groups x splits, at most the device's compute-unit count (one
                        workgroup fits per compute unit), else SMLA_EUNSUPPORTED.  Kernels that
                        run concurrently on other streams may delay some of the workgroups until
@@ -143,7 +155,7 @@ size_t smla_decode_workspace_size(const smla_plan *plan, int32_t T, int32_t H);
  *   out          device BF16 [T, H, 512] (16-byte aligned), written for every (t, h).
  *   lse          device float32 [T, H] or NULL: ln(sum_c e^{s_c} + e^{sink}) (base 2 with
  *                SMLA_LSE_LOG2); -inf for a token with no active column, whose output is +0.
- *   flags        SMLA_LSE_LOG2 | SMLA_P_ONE_TERM.
+ *   flags        SMLA_LSE_LOG2 | SMLA_P_ONE_TERM | SMLA_P_CHUNK_LOCAL.
  *   plan         NULL for smla_decode_plan's, else an explicit decomposition (results are
  *                bit-identical from run to run for a fixed plan).
  *   workspace    device scratch of workspace_bytes >= smla_decode_workspace_size(plan, T, H),

@@ -22,6 +22,7 @@ SMLA_ESCRATCH = 5
 NOALLOC_SCRATCH_BYTES = 48 << 20
 SMLA_LSE_LOG2 = 0x1
 SMLA_P_ONE_TERM = 0x2
+SMLA_P_CHUNK_LOCAL = 0x4
 SMLA_MERGE_LAST, SMLA_MERGE_SPREAD = 0, 1
 
 
@@ -152,12 +153,13 @@ def make_plan(splits: int, tiles: int, merge: int = SMLA_MERGE_LAST, heads: int 
 
 
 def _decode_args(q, kv_a, indices, lens, bmm1_scale, bmm2_scale, out, lse, kv_b, split_col,
-                 sinks, qk_dim, lse_log2, one_term, plan, workspace, stream):
+                 sinks, qk_dim, lse_log2, one_term, plan, workspace, stream, chunk_local=False):
     T, H, qd = q.shape
     W = indices.shape[1]
     row_bytes = kv_a.shape[1]
     qk_dim = qd if qk_dim is None else qk_dim
-    flags = (SMLA_LSE_LOG2 if lse_log2 else 0) | (SMLA_P_ONE_TERM if one_term else 0)
+    flags = ((SMLA_LSE_LOG2 if lse_log2 else 0) | (SMLA_P_ONE_TERM if one_term else 0) |
+             (SMLA_P_CHUNK_LOCAL if chunk_local else 0))
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     return (_ptr(q), q.stride(0) * q.element_size(), q.stride(1) * q.element_size(),
             _ptr(kv_a), kv_a.shape[0],
@@ -171,7 +173,7 @@ def _decode_args(q, kv_a, indices, lens, bmm1_scale, bmm2_scale, out, lse, kv_b,
 
 def sparse_mla_decode(q, kv_a, indices, lens, bmm1_scale, bmm2_scale, out, lse=None, *,
                       kv_b=None, split_col=None, sinks=None, qk_dim=None, lse_log2=False,
-                      one_term=False, plan=None, workspace=None, stream=None):
+                      one_term=False, plan=None, workspace=None, stream=None, chunk_local=False):
     """Call sparse_mla_decode on device tensors.
 
     q: uint8 [T, H, qk_dim] (any strides with unit last stride, 16-byte multiples);
@@ -179,10 +181,11 @@ def sparse_mla_decode(q, kv_a, indices, lens, bmm1_scale, bmm2_scale, out, lse=N
     out bf16 [T, H, 512]; lse float32 [T, H] or None; sinks float32 [H] or None.
     workspace: a uint8 device tensor of at least workspace_size(plan, T, H) bytes when the plan
     splits the columns (None otherwise), zero-filled before its first use (see
-    new_workspace)."""
+    new_workspace).  chunk_local selects SMLA_P_CHUNK_LOCAL (the plan, if given, from
+    plan_for(..., flags=SMLA_P_CHUNK_LOCAL))."""
     st = _load().sparse_mla_decode(*_decode_args(
         q, kv_a, indices, lens, bmm1_scale, bmm2_scale, out, lse, kv_b, split_col, sinks,
-        qk_dim, lse_log2, one_term, plan, workspace, stream))
+        qk_dim, lse_log2, one_term, plan, workspace, stream, chunk_local))
     if st != SMLA_OK:
         raise SmlaError(st, "sparse_mla_decode")
     return out, lse
@@ -190,11 +193,11 @@ def sparse_mla_decode(q, kv_a, indices, lens, bmm1_scale, bmm2_scale, out, lse=N
 
 def sparse_mla_decode_noalloc(q, kv_a, indices, lens, bmm1_scale, bmm2_scale, out, lse=None, *,
                               kv_b=None, split_col=None, sinks=None, qk_dim=None, lse_log2=False,
-                              one_term=False, plan=None, stream=None):
+                              one_term=False, plan=None, stream=None, chunk_local=False):
     """sparse_mla_decode without a workspace argument: the library's static per-device scratch
     serves as the workspace (no allocation anywhere; calls that overlap on one GPU race)."""
     a = _decode_args(q, kv_a, indices, lens, bmm1_scale, bmm2_scale, out, lse, kv_b, split_col,
-                     sinks, qk_dim, lse_log2, one_term, plan, None, stream)
+                     sinks, qk_dim, lse_log2, one_term, plan, None, stream, chunk_local)
     st = _load().sparse_mla_decode_noalloc(*a[:22], a[24])
     if st != SMLA_OK:
         raise SmlaError(st, "sparse_mla_decode_noalloc")
@@ -203,14 +206,15 @@ def sparse_mla_decode_noalloc(q, kv_a, indices, lens, bmm1_scale, bmm2_scale, ou
 
 def prepare_decode(q, kv_a, indices, lens, bmm1_scale, bmm2_scale, out, lse=None, *,
                    kv_b=None, split_col=None, sinks=None, qk_dim=None, lse_log2=False,
-                   one_term=False, plan=None, workspace=None, stream=None):
+                   one_term=False, plan=None, workspace=None, stream=None, chunk_local=False):
     """The same call with its arguments converted once, for loops that launch it repeatedly on
     the same buffers: returns a function of no arguments that launches it (on `stream`, else on
     the stream current when this was called) and raises SmlaError on a bad status.  The tensors
     must stay alive and in place while the function is used."""
     f = _load().sparse_mla_decode
     args = _decode_args(q, kv_a, indices, lens, bmm1_scale, bmm2_scale, out, lse, kv_b,
-                        split_col, sinks, qk_dim, lse_log2, one_term, plan, workspace, stream)
+                        split_col, sinks, qk_dim, lse_log2, one_term, plan, workspace, stream,
+                        chunk_local)
     keep = (q, kv_a, indices, lens, out, lse, kv_b, sinks, plan, workspace)
 
     def launch():

@@ -21,6 +21,7 @@ constexpr int kDefaultMaxSplits = 4;
 constexpr int kFewChunks = 6;
 constexpr int kMaxSpreadSplits = 16;
 constexpr int kMaxLastSplits32 = 8;
+constexpr int kWindow = 128;                       // columns per range of the chunk-local recipe
 constexpr int32_t kDefaultWaitPolls = 1 << 20;
 std::atomic<int> g_cu_count[kMaxDevices];
 // bound of the 64-head kernel's split-merge wait, and the test hook that makes it unreachable
@@ -155,16 +156,16 @@ bool plan_ok(const smla_plan *p, int32_t H)
     return true;
 }
 
-// A spread merge needs 512 / splits output columns per range in whole 32-column tiles and a
-// grid of at most one workgroup per compute unit, so that every workgroup is resident at once
-// (each waits for the others of its token and head group).
+// A spread merge needs at least one of the sixteen 32-column output tiles per range (2 to 16
+// ranges) and a grid of at most one workgroup per compute unit, so that every workgroup is
+// resident at once (each waits for the others of its token and head group).
 smla_status spread_ok(const smla_plan *p, int32_t T, int32_t H)
 {
     if (p->merge != SMLA_MERGE_SPREAD || p->splits == 1)
         return SMLA_OK;
     if (p->tiles != 2)
         return SMLA_EUNSUPPORTED;  // built into the 64-head kernel only
-    if (p->splits != 2 && p->splits != 4 && p->splits != 8 && p->splits != 16)
+    if (p->splits < 2 || p->splits > 16)
         return SMLA_EUNSUPPORTED;
     int cus = 0;
     if (current_cu_count(&cus) != hipSuccess)
@@ -240,7 +241,7 @@ smla_status smla_decode_plan(int32_t T, int32_t H, int32_t W, int32_t row_bytes,
         return SMLA_EINVAL;
     if (row_bytes != 512 && row_bytes != 576)
         return SMLA_EINVAL;
-    if (flags & ~(SMLA_LSE_LOG2 | SMLA_P_ONE_TERM))
+    if (flags & ~(SMLA_LSE_LOG2 | SMLA_P_ONE_TERM | SMLA_P_CHUNK_LOCAL))
         return SMLA_EINVAL;
     int cus = 0;
     if (current_cu_count(&cus) != hipSuccess)
@@ -264,6 +265,20 @@ smla_status smla_decode_plan(int32_t T, int32_t H, int32_t W, int32_t row_bytes,
             best = c;
         }
     };
+    if (flags & SMLA_P_CHUNK_LOCAL) {
+        // the chunk-local recipe fixes the ranges (one per 128-column window) and the kernel;
+        // the head groups and the merge are chosen as above
+        const int64_t s = (W + kWindow - 1) / kWindow;
+        if (s > kMaxSplits)
+            return SMLA_EUNSUPPORTED;
+        for (int32_t heads : {0, 32, 16}) {
+            consider((int32_t)s, 2, SMLA_MERGE_LAST, heads);
+            if (s >= 2 && s <= 16)
+                consider((int32_t)s, 2, SMLA_MERGE_SPREAD, heads);
+        }
+        *plan = best;
+        return SMLA_OK;
+    }
     for (int32_t heads : {0, 32, 16}) {
         consider(1, 2, SMLA_MERGE_LAST, heads);
         consider(2, 2, SMLA_MERGE_LAST, heads);
@@ -303,7 +318,7 @@ smla_status decode_impl(const void *q, int64_t q_stride_t, int64_t q_stride_h,
     // ---- validation (host only) ----------------------------------------------------------
     if (T < 0 || H <= 0 || H % 16 != 0 || W < 1)
         return SMLA_EINVAL;
-    if (flags & ~(SMLA_LSE_LOG2 | SMLA_P_ONE_TERM))
+    if (flags & ~(SMLA_LSE_LOG2 | SMLA_P_ONE_TERM | SMLA_P_CHUNK_LOCAL))
         return SMLA_EINVAL;
     if (row_bytes != 512 && row_bytes != 576)
         return SMLA_EINVAL;
@@ -339,6 +354,9 @@ smla_status decode_impl(const void *q, int64_t q_stride_t, int64_t q_stride_h,
     }
     if (chosen.tiles == 2 && (W + chosen.splits - 1) / chosen.splits > smla::G64_MAX_RANGE)
         return SMLA_EUNSUPPORTED;  // the 64-head kernel stages a range's indices in LDS
+    const bool chunk_local = (flags & SMLA_P_CHUNK_LOCAL) != 0;
+    if (chunk_local && (chosen.tiles != 2 || chosen.splits != (W + kWindow - 1) / kWindow))
+        return SMLA_EUNSUPPORTED;  // one range per 128-column window, on the 64-head kernel
     {
         const smla_status st = spread_ok(&chosen, T, H);
         if (st != SMLA_OK)
@@ -393,7 +411,7 @@ smla_status decode_impl(const void *q, int64_t q_stride_t, int64_t q_stride_h,
             return SMLA_EHIP;
     }
     const hipError_t e = smla::launch_decode(p, chosen.tiles, row_bytes, qk_dim,
-                                             (flags & SMLA_P_ONE_TERM) == 0, stream);
+                                             (flags & SMLA_P_ONE_TERM) == 0, chunk_local, stream);
     return e == hipSuccess ? SMLA_OK : SMLA_EHIP;
 }
 
@@ -532,7 +550,7 @@ smla_status paged_mla_decode(const void *q, int64_t q_stride_t, int64_t q_stride
         p.ws_ml = reinterpret_cast<float *>(base + w.ml);
     }
     const hipError_t e = smla::launch_decode_g64(p, 576, 576, (flags & SMLA_P_ONE_TERM) == 0,
-                                                 stream);
+                                                 false, stream);
     return e == hipSuccess ? SMLA_OK : SMLA_EHIP;
 }
 

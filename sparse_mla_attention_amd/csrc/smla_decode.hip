@@ -668,11 +668,11 @@ hipError_t launch_shape(const DecodeParams &p, int row_bytes, int qk_dim, hipStr
 }  // namespace
 
 hipError_t launch_decode(const DecodeParams &p, int tiles, int row_bytes, int qk_dim,
-                         bool two_term, hipStream_t stream)
+                         bool two_term, bool chunk_local, hipStream_t stream)
 {
     if (tiles == 2)
-        return launch_decode_g64(p, row_bytes, qk_dim, two_term, stream);
-    if (tiles != 1)
+        return launch_decode_g64(p, row_bytes, qk_dim, two_term, chunk_local, stream);
+    if (tiles != 1 || chunk_local)
         return hipErrorInvalidValue;
     return two_term ? launch_shape<true>(p, row_bytes, qk_dim, stream)
                     : launch_shape<false>(p, row_bytes, qk_dim, stream);

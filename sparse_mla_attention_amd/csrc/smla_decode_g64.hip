@@ -115,11 +115,19 @@ __device__ inline uint32_t lds_addr(const uint8_t *p)
     return (uint32_t)(uintptr_t)(const SMLA_LDS(uint8_t) *)p;
 }
 
-template <int RB, int QK, bool TWO, bool DIST>
+// CLA: the chunk-local recipe (the sparse_mla_cute page, "How."): every key range is one
+// 128-column window of the token's columns, [128 s, 128 s + 128) for range s, whose P is
+// anchored at 256 of the window's own maximum (one softmax over both 64-column chunks, no
+// running maximum); the ranges then merge as split partials.  Otherwise the attn_sparse
+// page's recipe: contiguous ranges of ceil(n / splits) columns, P at 448 of the running
+// maximum.
+template <int RB, int QK, bool TWO, bool DIST, bool CLA>
 __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
 {
     constexpr bool TAIL = QK == 576;               // a fifth, 64-byte QK step (rope)
     constexpr int NDMA = TAIL ? 9 : 8;             // loads per P.V wave and chunk
+    constexpr float AN = CLA ? 256.0f : ANCHOR;    // P anchor
+    constexpr float LOG2_AN = CLA ? 8.0f : LOG2_ANCHOR;
     using L = LdsG<TAIL>;
 
     __shared__ __attribute__((aligned(16))) uint8_t lds[L::TOTAL];
@@ -141,7 +149,7 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
     if (a.paged)
         n -= a.q_len - 1 - (t - req * a.q_len);
     n = n < 0 ? 0 : (n > a.W ? a.W : n);
-    const int per = (n + a.splits - 1) / a.splits;
+    const int per = CLA ? 2 * CHUNK : (n + a.splits - 1) / a.splits;
     const int first = min(n, split * per);
     // the host keeps every range within the staging buffer; the clamp only keeps LDS accesses
     // in bounds
@@ -244,7 +252,7 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
             __builtin_amdgcn_s_waitcnt(0);  // this wave's stores have completed
             __syncthreads();
             spread_merge<HG>(a, lds, reinterpret_cast<int *>(lds + L::MISC) + 2, t, hg, tg, split,
-                             tid);
+                             tid, AN, LOG2_AN);
             return;
         } else if (!DIST && a.splits > 1) {
             // Split merge.  Each range takes an arrival ticket first.  Every range but the last
@@ -479,7 +487,7 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
                 const float sk = a.sinks[head] * LOG2E;
                 big_m = fmaxf(g_h[h2], sk);
                 wgt = any ? exp2f(g_h[h2] - big_m) : 0.0f;
-                big_l = wgt * l_h[h2] + ANCHOR * exp2f(sk - big_m);
+                big_l = wgt * l_h[h2] + AN * exp2f(sk - big_m);
             }
             const float inv = failed ? __int_as_float(0x7FC00000) : any ? a.bmm2 * wgt / big_l : 0.0f;
             if (!qk_wave) {
@@ -497,7 +505,7 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
             }
             if (wave == 4 && u == 0 && real && a.lse != nullptr) {
                 const float lse2 = failed ? __int_as_float(0x7FC00000)
-                                   : any  ? big_m - LOG2_ANCHOR + log2f(big_l)
+                                   : any  ? big_m - LOG2_AN + log2f(big_l)
                                           : -INFINITY;
                 a.lse[(int64_t)t * a.H + head] = a.lse_log2 ? lse2 : lse2 * LN2;
             }
@@ -548,13 +556,9 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
 
         float m_run = -INFINITY, l_lane[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 
-        // QK and softmax of chunk x (the attn_sparse page's recipe): scores of this lane's head
-        // (keys 16 kt + 4 g + i), the chunk maximum over all 64 keys, the running maximum m, the
-        // rescale factor alpha = 2^(m_old - m) of everything accumulated so far, P = 2^(s2 - m +
-        // log2 448) <= 448 as E4M3 (two-term by default) into the P buffer and alpha beside it;
-        // the sums of the unquantized P are rescaled and extended here, the P.V waves rescale
-        // their accumulators by alpha before adding the chunk.
-        auto qk_softmax = [&](int x) {
+        // QK of chunk x: the masked base-2 scores of this lane's head (keys 16 kt + 4 g + i) and
+        // their maximum over this lane's keys.
+        auto qk_scores = [&](int x, v4f(&sc)[4], float &mx) {
             // the K reads and products of the QK waves go ahead of the P.V waves' work on
             // the same SIMD; the softmax then runs at normal priority
             __builtin_amdgcn_s_setprio(3);
@@ -576,7 +580,6 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
                 for (int kt = 0; kt < 4; kt++)
                     rr[kt] = lds_load<v4i>(slot + kt * 1024, rb);
             }
-            v4f sc[4];
 #pragma unroll
             for (int kt = 0; kt < 4; kt++)
                 sc[kt] = v4f{0.f, 0.f, 0.f, 0.f};
@@ -602,7 +605,7 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
             const uint32_t word[2] = {(uint32_t)bits, (uint32_t)(bits >> 32)};
             mfma_result_pad();
             __builtin_amdgcn_s_setprio(0);
-            float mx = -INFINITY;
+            mx = -INFINITY;
 #pragma unroll
             for (int kt = 0; kt < 4; kt++) {
 #pragma unroll
@@ -615,7 +618,10 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
                     mx = fmaxf(mx, sc[kt][i]);
                 }
             }
-            // chunk maximum of this head: over the four lane groups (rows of 16 lanes)
+        };
+
+        // a head's maximum over the four lane groups (rows of 16 lanes) that hold its keys
+        auto head_max = [&](float mx) {
             {
                 const auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx),
                                                                   __float_as_uint(mx), false, false);
@@ -624,12 +630,13 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
                                                                   __float_as_uint(mx), false, false);
                 mx = fmaxf(__uint_as_float(p32[0]), __uint_as_float(p32[1]));
             }
-            const float m_new = fmaxf(m_run, mx);
-            // alpha = 1 while the range has no active column yet (m_new = -inf), 0 on the first
-            // chunk that has one (nothing accumulated)
-            const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-            m_run = m_new;
-            const float fb = m_new == -INFINITY ? 0.0f : m_new - LOG2_ANCHOR;
+            return mx;
+        };
+
+        // P of chunk x from its scores at fb = m - log2(anchor): E4M3 (two-term by default)
+        // into the P buffer, the rescale factor alpha of the accumulators beside it; this
+        // lane's sums of the unquantized P are rescaled by alpha and extended.
+        auto emit_p = [&](int x, const v4f(&sc)[4], float fb, float alpha) {
             uint8_t *pbase = lds + L::P + (x & 1) * L::PBUF;
 #pragma unroll
             for (int kt = 0; kt < 4; kt++) {
@@ -656,14 +663,53 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
                 scl[(x & 1) * HG + head] = alpha;
         };
 
+        // QK and softmax of chunk x (the attn_sparse page's recipe): the chunk maximum over all
+        // 64 keys, the running maximum m, the rescale factor alpha = 2^(m_old - m) of
+        // everything accumulated so far, P = 2^(s2 - m + log2 448) <= 448.
+        auto qk_softmax = [&](int x) {
+            v4f sc[4];
+            float mx;
+            qk_scores(x, sc, mx);
+            mx = head_max(mx);
+            const float m_new = fmaxf(m_run, mx);
+            // alpha = 1 while the range has no active column yet (m_new = -inf), 0 on the first
+            // chunk that has one (nothing accumulated)
+            const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+            m_run = m_new;
+            const float fb = m_new == -INFINITY ? 0.0f : m_new - LOG2_AN;
+            emit_p(x, sc, fb, alpha);
+        };
+
         // Every QK wave computes its 16 heads, padding heads included (with the group's first
         // head's q), so that the waves of a workgroup keep one schedule whatever H is.
         if (nch > 0) {
             lds_barrier();                          // the P.V waves issue chunks 0 and 1
-            for (int c = 0; c <= nch; c++) {
-                lds_barrier();                      // chunk c landed; P buffer c & 1 free
-                if (c < nch)
-                    qk_softmax(c);
+            if constexpr (CLA) {
+                // the window's one or two chunks: the scores of each as it lands, then one
+                // softmax at the window's maximum (P at 256 of it, no rescale) once the last
+                // has been scored; the P.V waves take both chunks after that
+                v4f s0[4], s1[4];
+                float mx0 = -INFINITY, mx1 = -INFINITY;
+                for (int c = 0; c <= nch; c++) {
+                    lds_barrier();                  // chunk c landed
+                    if (c == 0)
+                        qk_scores(0, s0, mx0);
+                    else if (c < nch)
+                        qk_scores(1, s1, mx1);
+                    if (c == nch - 1) {
+                        m_run = head_max(fmaxf(mx0, mx1));
+                        const float fb = m_run == -INFINITY ? 0.0f : m_run - LOG2_AN;
+                        emit_p(0, s0, fb, 1.0f);
+                        if (nch > 1)
+                            emit_p(1, s1, fb, 1.0f);
+                    }
+                }
+            } else {
+                for (int c = 0; c <= nch; c++) {
+                    lds_barrier();                  // chunk c landed; P buffer c & 1 free
+                    if (c < nch)
+                        qk_softmax(c);
+                }
             }
         }
 
@@ -803,20 +849,32 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
                 wait_dma<0>();
             for (int c = 0; c <= nch; c++) {
                 lds_barrier();                      // chunk c landed; P of chunk c-1 visible
-                // The loads of chunk c+2 go out before the products of chunk c-1: the QK
-                // waves' products of chunk c then reach the matrix units first, and these run
-                // during the QK waves' softmax.
-                Frags f;
-                if (c > 0)
-                    pv_read(c - 1, f);
-                if (c + 2 < nch) {
-                    // the wave's own reads of the slice it refills have completed
-                    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-                    issue(c + 2);
+                if constexpr (CLA) {
+                    // a window has at most two chunks, both in their slots from the start;
+                    // their P is ready once the QK waves have scored the last of them
+                    if (c == nch) {
+                        for (int x = 0; x < nch; x++) {
+                            Frags f;
+                            pv_read(x, f);
+                            pv_mma(f);
+                        }
+                    }
+                } else {
+                    // The loads of chunk c+2 go out before the products of chunk c-1: the QK
+                    // waves' products of chunk c then reach the matrix units first, and these
+                    // run during the QK waves' softmax.
+                    Frags f;
+                    if (c > 0)
+                        pv_read(c - 1, f);
+                    if (c + 2 < nch) {
+                        // the wave's own reads of the slice it refills have completed
+                        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+                        issue(c + 2);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);  // the products stay after the loads
+                    if (c > 0)
+                        pv_mma(f);
                 }
-                __builtin_amdgcn_sched_barrier(0);  // the products stay after the loads
-                if (c > 0)
-                    pv_mma(f);
                 if (c + 2 < nch)
                     wait_dma<NDMA>();               // chunk c+1
                 else
@@ -828,38 +886,43 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
     }
 }
 
-template <int RB, int QK, bool TWO>
+template <int RB, int QK, bool TWO, bool CLA>
 hipError_t launch_g64_one(const DecodeParams &p, hipStream_t stream)
 {
     const unsigned blocks = (unsigned)p.T * (unsigned)p.groups * (unsigned)p.splits;
     // the spread merge's ranges wait for each other: its grid is at most one workgroup per
     // compute unit (checked on the host), so every workgroup is resident at once
     if (p.merge == 1 && p.splits > 1)
-        hipLaunchKernelGGL((decode_g64_kernel<RB, QK, TWO, true>), dim3(blocks), dim3(NT), 0, stream, p);
+        hipLaunchKernelGGL((decode_g64_kernel<RB, QK, TWO, true, CLA>), dim3(blocks), dim3(NT), 0,
+                           stream, p);
     else
-        hipLaunchKernelGGL((decode_g64_kernel<RB, QK, TWO, false>), dim3(blocks), dim3(NT), 0, stream, p);
+        hipLaunchKernelGGL((decode_g64_kernel<RB, QK, TWO, false, CLA>), dim3(blocks), dim3(NT), 0,
+                           stream, p);
     return hipGetLastError();
 }
 
-template <bool TWO>
+template <bool TWO, bool CLA>
 hipError_t launch_g64_shape(const DecodeParams &p, int row_bytes, int qk_dim, hipStream_t stream)
 {
     if (row_bytes == 576 && qk_dim == 576)
-        return launch_g64_one<576, 576, TWO>(p, stream);
+        return launch_g64_one<576, 576, TWO, CLA>(p, stream);
     if (row_bytes == 576 && qk_dim == 512)
-        return launch_g64_one<576, 512, TWO>(p, stream);
+        return launch_g64_one<576, 512, TWO, CLA>(p, stream);
     if (row_bytes == 512 && qk_dim == 512)
-        return launch_g64_one<512, 512, TWO>(p, stream);
+        return launch_g64_one<512, 512, TWO, CLA>(p, stream);
     return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 hipError_t launch_decode_g64(const DecodeParams &p, int row_bytes, int qk_dim, bool two_term,
-                             hipStream_t stream)
+                             bool chunk_local, hipStream_t stream)
 {
-    return two_term ? launch_g64_shape<true>(p, row_bytes, qk_dim, stream)
-                    : launch_g64_shape<false>(p, row_bytes, qk_dim, stream);
+    // the chunk-local recipe quantizes P as one E4M3 term
+    if (chunk_local)
+        return launch_g64_shape<false, true>(p, row_bytes, qk_dim, stream);
+    return two_term ? launch_g64_shape<true, false>(p, row_bytes, qk_dim, stream)
+                    : launch_g64_shape<false, false>(p, row_bytes, qk_dim, stream);
 }
 
 }  // namespace smla

@@ -51,11 +51,12 @@ struct DecodeParams {
 constexpr int G64_MAX_RANGE = 2048;
 
 // Launch the decode (the split merge is fused into it) on `stream`: 32 heads per workgroup
-// (tiles = 1) or the 64-head kernel (tiles = 2).
+// (tiles = 1) or the 64-head kernel (tiles = 2).  chunk_local selects the chunk-local recipe
+// (64-head kernel only: one range per 128-column window, P at 256 of its own maximum).
 hipError_t launch_decode(const DecodeParams &p, int tiles, int row_bytes, int qk_dim,
-                         bool two_term, hipStream_t stream);
+                         bool two_term, bool chunk_local, hipStream_t stream);
 hipError_t launch_decode_g64(const DecodeParams &p, int row_bytes, int qk_dim, bool two_term,
-                             hipStream_t stream);
+                             bool chunk_local, hipStream_t stream);
 
 struct LseMergeParams {
     const uint16_t *partials;   // BF16 [S, T, H, D]

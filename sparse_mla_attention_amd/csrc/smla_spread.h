@@ -9,14 +9,14 @@
 // Decomposition.  Before calling spread_merge, every range has stored its whole partial (FP32
 // accumulators in register order, then (m, l) per head) for the group's real heads (padding
 // heads past H are neither stored nor read) with device-scope stores and waited for them to
-// complete.  Range s then writes output columns [s, s+1) * 512 / S of the group's heads:
+// complete.  Range s then writes the output columns of 32-column tiles [16 s / S, 16 (s + 1) /
+// S) of the group's heads (512 / S columns when S divides 16):
 //   1. arrival: one atomic add on the (token, head group)'s arrival counter, then a bounded
 //      wait until all S ranges have arrived (the grid holds at most one workgroup per compute
 //      unit, so every range is resident);
 //   2. one round of loads: (m, l) of every range and head into LDS, and this range's column
 //      slice of every range's partial, 16 bytes per load, all issued before any is used (the
-//      slice is a contiguous run of each partial: 512 / S columns are 16 / S whole 32-column
-//      tiles);
+//      slice, whole 32-column tiles, is a contiguous run of each partial);
 //   3. each thread holds positions of one head: it computes that head's M, L, weights and
 //      normalization from LDS, sums its positions over the ranges in range order, scales,
 //      rounds to BF16 into the LDS output tile;
@@ -43,14 +43,18 @@ namespace dev {
 template <int HG, int S>
 __device__ __attribute__((always_inline)) inline void spread_merge_s(
     const DecodeParams &a, uint8_t *lds, int *misc, int t, int hg, int64_t tg, int split,
-    int tid)
+    int tid, float anchor, float log2_anchor)
 {
     constexpr int NT = 512;
     constexpr int H2 = HG / 32;
     constexpr int SC1 = 16;                        // device-scope (write-through) accesses
-    constexpr int NPOS = 4096 * H2 / S;            // 16-byte positions of one range's slice
-    constexpr int PP = NPOS >= NT ? NPOS / NT : 1; // positions per thread
-    static_assert(NPOS % NT == 0 || NPOS < NT, "positions split evenly over the threads");
+    constexpr int TPOS = 256 * H2;                 // 16-byte positions of one 32-column tile
+    constexpr int MAXT = (16 + S - 1) / S;         // most tiles of one range's slice
+    constexpr int PP = MAXT * TPOS / NT;           // positions per thread
+    static_assert(TPOS % NT == 0 || NT % TPOS == 0, "positions split evenly over the threads");
+    static_assert(TPOS >= NT, "one head per thread needs a tile's positions to cover the threads");
+    const int tile0 = 16 * split / S;              // this range's tiles [tile0, tile0 + ntiles)
+    const int ntiles = 16 * (split + 1) / S - tile0;
     const int lane = tid & 63;
     const int heads_here = min(a.gw, a.H - hg * a.gw);  // real heads of the group
     // positions tid + NT i share lane and head tile: one head per thread
@@ -58,7 +62,7 @@ __device__ __attribute__((always_inline)) inline void spread_merge_s(
     const int hl = lane & 31;
     const int hloc = 32 * h2 + hl;                 // head within the group
     const int head = hg * a.gw + hloc;             // (a real head only if hloc < heads_here)
-    const bool active = tid < NPOS && hloc < heads_here;
+    const bool active = hloc < heads_here;
     int *ctr = a.counters + 2 * tg;                // [0] arrivals, [1] departures
 
     // ---- 1. arrival and bounded wait ---------------------------------------------------
@@ -96,8 +100,10 @@ __device__ __attribute__((always_inline)) inline void spread_merge_s(
             ml[k] = float2{load_device(m), load_device(m + 1)};
         }
     }
-    // this range's slice of every range's partial: positions base + tid + NT i
-    const int pbase = split * NPOS;
+    // this range's slice of every range's partial: positions pbase + tid + NT i, i below
+    // ntiles * TPOS / NT
+    const int pbase = tile0 * TPOS;
+    const int npp = ntiles * TPOS / NT;            // this range's positions per thread
     v4i v[PP][S];
 #pragma unroll
     for (int r = 0; r < S; r++) {
@@ -106,7 +112,7 @@ __device__ __attribute__((always_inline)) inline void spread_merge_s(
 #pragma unroll
         for (int i = 0; i < PP; i++) {
             v[i][r] = v4i{0, 0, 0, 0};
-            if (active)
+            if (active && i < npp)
                 v[i][r] = __builtin_amdgcn_raw_buffer_load_b128(
                     rs, (pbase + tid + NT * i) * 16, 0, SC1);
         }
@@ -138,13 +144,15 @@ __device__ __attribute__((always_inline)) inline void spread_merge_s(
         const float sk = a.sinks[head] * LOG2E;
         big_m = fmaxf(big_g, sk);
         wgt = any ? exp2f(big_g - big_m) : 0.0f;
-        big_l = wgt * l_new + ANCHOR * exp2f(sk - big_m);
+        big_l = wgt * l_new + anchor * exp2f(sk - big_m);
     }
     const float inv = failed ? __int_as_float(0x7FC00000) : any ? a.bmm2 * wgt / big_l : 0.0f;
     uint8_t *tile = lds;                           // BF16 [HG][1024 bytes]
     if (active) {
 #pragma unroll
         for (int i = 0; i < PP; i++) {
+            if (i >= npp)
+                break;
             const int p = pbase + tid + NT * i;
             const int j = (p >> 6) & 3, ptile = p / (256 * H2);
             float sum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -163,16 +171,16 @@ __device__ __attribute__((always_inline)) inline void spread_merge_s(
     if (split == 0 && (tid & 255) < 32 && (tid >> 8) < H2 && hloc < heads_here &&
         a.lse != nullptr) {
         const float lse2 = failed ? __int_as_float(0x7FC00000)
-                           : any  ? big_m - LOG2_ANCHOR + log2f(big_l)
+                           : any  ? big_m - log2_anchor + log2f(big_l)
                                   : -INFINITY;
         a.lse[(int64_t)t * a.H + head] = a.lse_log2 ? lse2 : lse2 * LN2;
     }
     __syncthreads();  // the tile is complete and every wave's loads have been used
 
     // ---- 4. row stores of the slice, departure ---------------------------------------------
-    constexpr int PARTS = 64 / S;                  // 16-byte parts of a row in the slice
-    for (int x = tid; x < heads_here * PARTS; x += NT) {
-        const int row = x / PARTS, part = split * PARTS + x % PARTS;
+    const int parts = 4 * ntiles;                  // 16-byte parts of a row in the slice
+    for (int x = tid; x < heads_here * parts; x += NT) {
+        const int row = x / parts, part = 4 * tile0 + x % parts;
         const v4i o = lds_load<v4i>(tile, tile_off(row, 16 * part));
         __builtin_nontemporal_store(
             o, reinterpret_cast<v4i *>(a.out + ((int64_t)t * a.H + hg * a.gw + row) * 512 +
@@ -188,20 +196,25 @@ __device__ __attribute__((always_inline)) inline void spread_merge_s(
     }
 }
 
-// The spread merge of range `split` of (token t, head group hg); S = a.splits in {2, 4, 8, 16}
+// The spread merge of range `split` of (token t, head group hg); S = a.splits in 2 .. 16
 // (checked on the host).  LDS: the BF16 output tile [HG][1024] at lds, the (m, l) of the
-// ranges [S][HG] float2 after it; `misc` one int of LDS.
+// ranges [S][HG] float2 after it; `misc` one int of LDS.  `anchor` is the recipe's P anchor
+// (the sink's weight and the LSE are in its units).
 template <int HG>
 __device__ __attribute__((always_inline)) inline void spread_merge(
     const DecodeParams &a, uint8_t *lds, int *misc, int t, int hg, int64_t tg, int split,
-    int tid)
+    int tid, float anchor, float log2_anchor)
 {
+#define SMLA_SPREAD_CASE(n)                                                                    \
+    case n: spread_merge_s<HG, n>(a, lds, misc, t, hg, tg, split, tid, anchor, log2_anchor); break;
     switch (a.splits) {
-    case 2: spread_merge_s<HG, 2>(a, lds, misc, t, hg, tg, split, tid); break;
-    case 4: spread_merge_s<HG, 4>(a, lds, misc, t, hg, tg, split, tid); break;
-    case 8: spread_merge_s<HG, 8>(a, lds, misc, t, hg, tg, split, tid); break;
-    default: spread_merge_s<HG, 16>(a, lds, misc, t, hg, tg, split, tid); break;
+        SMLA_SPREAD_CASE(2) SMLA_SPREAD_CASE(3) SMLA_SPREAD_CASE(4) SMLA_SPREAD_CASE(5)
+        SMLA_SPREAD_CASE(6) SMLA_SPREAD_CASE(7) SMLA_SPREAD_CASE(8) SMLA_SPREAD_CASE(9)
+        SMLA_SPREAD_CASE(10) SMLA_SPREAD_CASE(11) SMLA_SPREAD_CASE(12) SMLA_SPREAD_CASE(13)
+        SMLA_SPREAD_CASE(14) SMLA_SPREAD_CASE(15)
+    default: spread_merge_s<HG, 16>(a, lds, misc, t, hg, tg, split, tid, anchor, log2_anchor); break;
     }
+#undef SMLA_SPREAD_CASE
 }
 
 }  // namespace dev

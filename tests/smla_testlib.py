@@ -102,20 +102,22 @@ class DeviceProblem:
         ws[counters:].fill_(0xFF)
         return ws
 
-    def run(self, plan=None, one_term=False, lse_log2=None, poison_out=True):
+    def run(self, plan=None, one_term=False, lse_log2=None, poison_out=True, chunk_local=False):
         p = self.p
         if lse_log2 is None:
             lse_log2 = bool(p.get("lse_log2", False))
         if poison_out:  # outputs start as NaN: every element must be written
             self.out.view(torch.int16).fill_(0x7FC0)
             self.lse.fill_(float("nan"))
+        flags = smla.SMLA_P_CHUNK_LOCAL if chunk_local else 0
         use = plan if plan is not None else smla.plan_for(self.T, self.H, p["indices"].shape[1],
-                                                         self.kv_a.shape[1])
+                                                         self.kv_a.shape[1], flags)
         ws = self.workspace(use)
         smla.sparse_mla_decode(self.q, self.kv_a, self.indices, self.lens, p["bmm1"], p["bmm2"],
                                self.out, self.lse, kv_b=self.kv_b, split_col=p["split_col"],
                                sinks=self.sinks, qk_dim=p["qk_dim"], lse_log2=lse_log2,
-                               one_term=one_term, plan=use, workspace=ws)
+                               one_term=one_term, plan=use, workspace=ws,
+                               chunk_local=chunk_local)
         torch.cuda.synchronize()
         out = bf16_to_f64(self.out).reshape(self.T * self.H, 512)
         lse = self.lse.cpu().numpy().astype(np.float64).reshape(-1)

@@ -77,7 +77,7 @@ def _decode(T=1, H=16, W=64, row_bytes=576, qk_dim=576, flags=0, plan=None, q=16
 
 @pytest.mark.parametrize("kw", [
     dict(T=-1), dict(H=0), dict(H=24), dict(W=0), dict(row_bytes=640), dict(qk_dim=448),
-    dict(row_bytes=512, qk_dim=576), dict(flags=0x4), dict(bmm1=float("nan")),
+    dict(row_bytes=512, qk_dim=576), dict(flags=0x8), dict(bmm1=float("nan")),
     dict(bmm1=float("inf")), dict(plan=smla.make_plan(0, 1)), dict(plan=smla.make_plan(1, 3)),
     dict(plan=smla.make_plan(1, 0)), dict(plan=smla.make_plan(65, 2)),
     dict(q=0), dict(kv=0), dict(idx=0), dict(lens=0), dict(out=0), dict(rows_a=0),
@@ -87,6 +87,20 @@ def _decode(T=1, H=16, W=64, row_bytes=576, qk_dim=576, flags=0, plan=None, q=16
 ])
 def test_decode_rejects_bad_arguments(kw):
     assert _decode(**kw) == smla.SMLA_EINVAL
+
+
+def test_chunk_local_plans_are_checked():
+    """The chunk-local recipe runs the 64-head kernel with one range per 128-column window: any
+    other plan is refused before anything is launched; a matching plan gets as far as the
+    workspace check."""
+    cl = smla.SMLA_P_CHUNK_LOCAL
+    assert _decode(W=64, flags=cl, plan=smla.make_plan(1, 1)) == smla.SMLA_EUNSUPPORTED
+    assert _decode(W=64, flags=cl, plan=smla.make_plan(2, 2)) == smla.SMLA_EUNSUPPORTED
+    assert _decode(W=300, flags=cl, plan=smla.make_plan(2, 2)) == smla.SMLA_EUNSUPPORTED
+    assert _decode(W=300, flags=cl, plan=smla.make_plan(4, 2)) == smla.SMLA_EUNSUPPORTED
+    assert _decode(W=300, flags=cl, plan=smla.make_plan(3, 2)) == smla.SMLA_EWORKSPACE
+    assert _decode(W=300, flags=cl | smla.SMLA_P_ONE_TERM,
+                   plan=smla.make_plan(3, 2, heads=16)) == smla.SMLA_EWORKSPACE
 
 
 def test_64_head_plan_limits_the_range_length():

@@ -62,7 +62,7 @@ def test_spread_merge_equals_last_arriver_bitwise(name):
     tiles = 2
     d = DeviceProblem(p)
     for one_term in (False, True):
-        for splits in (2, 4, 8, 16):
+        for splits in (2, 3, 4, 5, 7, 8, 16):
             log(f"spread merge {name} tiles={tiles} splits={splits} one_term={one_term}")
             d.run(plan=smla.make_plan(splits, tiles, LAST), one_term=one_term)
             ref = _bits(d)
@@ -180,13 +180,12 @@ def test_spread_merge_paged_equals_last_arriver():
 
 def test_spread_merge_validation():
     """Spread plans the kernels cannot run are refused on the host before any launch: the
-    32-head kernel, split counts that do not divide the 512 output columns into whole 32-column
-    tiles, grids larger than the compute-unit count (every workgroup must be resident at
-    once), an unknown merge mode."""
+    32-head kernel, more ranges than the sixteen 32-column output tiles, grids larger than the
+    compute-unit count (every workgroup must be resident at once), an unknown merge mode."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     p = inputs.random_problem(713, 2, 64, 300, pool_rows=2000, lens=np.array([300, 200]))
     d = DeviceProblem(p)
-    for splits, tiles in ((3, 2), (5, 2), (32, 2), (2, 1), (4, 1)):
+    for splits, tiles in ((17, 2), (32, 2), (2, 1), (4, 1)):
         with pytest.raises(smla.SmlaError) as e:
             d.run(plan=smla.make_plan(splits, tiles, SPREAD))
         assert e.value.status == smla.SMLA_EUNSUPPORTED
