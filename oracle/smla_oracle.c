@@ -172,17 +172,41 @@ static int is_active(const problem *p, int t, int c, int n)
     return c < n && p->indices[(int64_t)t * p->W + c] >= 0;
 }
 
-/* q[t,h] . kv_row over the first qk_dim bytes, exactly (every E4M3 value and
- * every product is exact in double; the sum of at most 576 of them loses
- * nothing that matters at the tolerances used). */
+/* Element d of a row: with 576- or 512-byte rows, the E4M3 byte d.  With
+ * 656-byte fp8_ds_mla rows (the dsa_indexer page: a 656-byte MLA cache entry
+ * holding [kv_c_normed | k_pe], viewed as FP8, FP32 and BF16), read as bytes
+ * 0..511 the E4M3 latent, bytes 512..527 four FP32 scales (one per 128 latent
+ * elements), bytes 528..655 the 64-element rope in BF16: latent element d is
+ * E4M3(byte d) * scale[d / 128], rope element d - 512 is the BF16 value. */
+#define DS_MLA_ROW 656
+
+static double kv_value(const problem *p, const uint8_t *row, int d)
+{
+    if (p->row_bytes != DS_MLA_ROW)
+        return oracle_e4m3_value(row[d]);
+    if (d < 512) {
+        float scale;
+        memcpy(&scale, row + 512 + 4 * (d / 128), sizeof scale);
+        return oracle_e4m3_value(row[d]) * (double)scale;
+    } else {
+        uint16_t bits;
+        memcpy(&bits, row + 528 + 2 * (d - 512), sizeof bits);
+        return oracle_bf16_value(bits);
+    }
+}
+
+/* q[t,h] . kv_row over the first qk_dim elements, exactly (every E4M3 value and
+ * every product is exact in double, and so is a product with a BF16 or an FP32
+ * scaled value; the sum of at most 576 of them loses nothing that matters at
+ * the tolerances used). */
 static double dot_qk(const problem *p, int t, int h, const uint8_t *row, int *status)
 {
     const uint8_t *q = p->q + (int64_t)t * p->q_stride_t + (int64_t)h * p->q_stride_h;
     double acc = 0.0;
     for (int d = 0; d < p->qk_dim; d++) {
         double a = oracle_e4m3_value(q[d]);
-        double b = oracle_e4m3_value(row[d]);
-        if (isnan(a) || isnan(b))
+        double b = kv_value(p, row, d);
+        if (isnan(a) || isnan(b) || isinf(b))
             *status = ORACLE_ENAN;
         acc += a * b;
     }
@@ -196,6 +220,8 @@ static int check_problem(const problem *p)
     if (p->T < 0 || p->H <= 0 || p->W <= 0)
         return ORACLE_EBADARG;
     if (p->row_bytes < 512 || p->qk_dim < 1 || p->qk_dim > p->row_bytes)
+        return ORACLE_EBADARG;
+    if (p->row_bytes == DS_MLA_ROW && p->qk_dim != 576)
         return ORACLE_EBADARG;
     if (p->kv_b && (p->split_col < 0 || p->split_col > p->W))
         return ORACLE_EBADARG;
@@ -274,7 +300,7 @@ int oracle_decode_exact(
             w = exp(scores[c] - m);
             z += w;
             for (int j = 0; j < V_DIM; j++)
-                o[j] += w * oracle_e4m3_value(row[j]);
+                o[j] += w * kv_value(&p, row, j);
         }
         if (sinks)
             z += exp((double)sinks[h] - m);
@@ -400,7 +426,7 @@ int oracle_decode_mimic(
                         continue; /* inactive, or P rounded to zero */
                     row = row_of(&p, t, base + i, &status);
                     for (int j = 0; j < V_DIM; j++)
-                        acc[j] += phat[i] * oracle_e4m3_value(row[j]);
+                        acc[j] += phat[i] * kv_value(&p, row, j);
                 }
                 m_run = m_new;
             }
@@ -562,7 +588,7 @@ int oracle_decode_chunk_local(
                     continue;
                 row = row_of(&p, t, base + i, &status);
                 for (int j = 0; j < V_DIM; j++)
-                    acc_k[j] += ph * oracle_e4m3_value(row[j]);
+                    acc_k[j] += ph * kv_value(&p, row, j);
             }
             w_k = exp2(m_k - big_m);
             big_l += w_k * l_k;

@@ -6,7 +6,8 @@ imports neither the kernels nor the oracle, so both sides can take their inputs 
 
 A decode problem is a dict:
   q        uint8 [T, H, qk_dim]   E4M3 bytes
-  kv_a     uint8 [rows_a, row_bytes]   E4M3 bytes (pool A; the only pool when kv_b is None)
+  kv_a     uint8 [rows_a, row_bytes]   E4M3 bytes (pool A; the only pool when kv_b is None), or
+           656-byte fp8_ds_mla rows (ds_mla_rows)
   kv_b     uint8 [rows_b, row_bytes] or None   (pool B: columns >= split_col)
   split_col  int   (W when there is one pool)
   qk_dim   int   (576 with 512 latent + 64 rope bytes, or 512)
@@ -44,6 +45,26 @@ def bf16_bits(x) -> np.ndarray:
     return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
 
 
+DS_MLA_ROW_BYTES = 656
+
+
+def ds_mla_rows(latent, rope) -> np.ndarray:
+    """656-byte fp8_ds_mla rows of a latent [n, 512] and a rope [n, 64] (the dsa_indexer page's
+    MLA cache entry, read as: E4M3 latent bytes 0..511, four FP32 scales at 512..527, one per 128
+    latent elements, the BF16 rope at 528..655).  Each 128-element block is quantized the way a
+    cache writer does it: scale = its largest magnitude / 448 (FP32), bytes = E4M3(x / scale)."""
+    latent = np.asarray(latent, dtype=np.float32)
+    n = latent.shape[0]
+    out = np.zeros((n, DS_MLA_ROW_BYTES), dtype=np.uint8)
+    blocks = latent.reshape(n, 4, 128)
+    scale = (np.abs(blocks).max(axis=2) / np.float32(E4M3_MAX)).astype(np.float32)
+    scale = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
+    out[:, :512] = e4m3_bytes((blocks / scale[:, :, None]).reshape(n, 512))
+    out[:, 512:528] = np.ascontiguousarray(scale).view(np.uint8).reshape(n, 16)
+    out[:, 528:656] = np.ascontiguousarray(bf16_bits(rope)).view(np.uint8).reshape(n, 128)
+    return out
+
+
 def _poison_unused(pool: np.ndarray, used: np.ndarray) -> None:
     mask = np.ones(pool.shape[0], dtype=bool)
     mask[used] = False
@@ -69,11 +90,14 @@ def random_problem(seed: int, T: int, H: int, W: int, *, pool_rows: int = 4096,
     neg_frac: probability that an entry below lens is -1.  duplicates: draw rows with
     replacement (repeated rows count once per column)."""
     rng = np.random.default_rng(seed)
-    qk_dim = row_bytes if qk_dim is None else qk_dim
+    ds = row_bytes == DS_MLA_ROW_BYTES              # fp8_ds_mla rows: per-block scales
+    qk_dim = (576 if ds else row_bytes) if qk_dim is None else qk_dim
     q = e4m3_bytes(rng.standard_normal((T, H, qk_dim)) * value_scale)
     x = rng.standard_normal((pool_rows, row_bytes))
     k_scale = 1.0
-    if kv_scale_to_amax:
+    if ds:
+        kv_a = ds_mla_rows(x[:, :512] * value_scale, x[:, 512:576] * value_scale)
+    elif kv_scale_to_amax:
         k_scale = float(np.abs(x).max()) / E4M3_MAX
         kv_a = e4m3_bytes(x / k_scale)
     else:
@@ -81,7 +105,8 @@ def random_problem(seed: int, T: int, H: int, W: int, *, pool_rows: int = 4096,
     kv_b = None
     nb = rows_b if rows_b is not None else pool_rows
     if two_pools:
-        kv_b = e4m3_bytes(rng.standard_normal((nb, row_bytes)) * value_scale)
+        xb = rng.standard_normal((nb, row_bytes)) * value_scale
+        kv_b = ds_mla_rows(xb[:, :512], xb[:, 512:576]) if ds else e4m3_bytes(xb)
     else:
         split_col = W
     if lens is None:

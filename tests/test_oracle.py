@@ -508,6 +508,82 @@ def test_chunk_local_zero_count_rule():
 
 
 # ---------------------------------------------------------------------------
+# 656-byte fp8_ds_mla rows (E4M3 latent with an FP32 scale per 128 elements, BF16 rope)
+# ---------------------------------------------------------------------------
+
+def _ds_rows_f64(rows):
+    """Materialize fp8_ds_mla rows [n, 656] as K [n, 576] in float64 with numpy and torch
+    casts (a path independent of the oracle's decoder)."""
+    rows = np.ascontiguousarray(rows)
+    lat = _e4m3_f64(rows[:, :512]).numpy()
+    scale = rows[:, 512:528].copy().view(np.float32).astype(np.float64)
+    rope = torch.from_numpy(rows[:, 528:656].copy().view(np.int16)).view(torch.bfloat16)
+    k = np.empty((rows.shape[0], 576))
+    k[:, :512] = lat * np.repeat(scale, 128, axis=1)
+    k[:, 512:] = rope.to(torch.float64).numpy()
+    return k
+
+
+def test_ds_mla_exact_matches_dense_attention_on_materialized_rows():
+    p = inputs.random_problem(44, 2, 16, 90, pool_rows=300, row_bytes=656, neg_frac=0.2,
+                              lens=[90, 41], sinks=True)
+    out, lse = oracle.decode_exact(p)
+    q = _e4m3_f64(p["q"]).numpy()
+    for t in range(2):
+        n = int(p["lens"][t])
+        cols = [c for c in range(n) if p["indices"][t, c] >= 0]
+        k = _ds_rows_f64(p["kv_a"][p["indices"][t, cols]])
+        s = p["bmm1"] * (q[t] @ k.T)                     # [H, n]
+        s = np.concatenate([s, p["sinks"].astype(np.float64)[:, None]], axis=1)
+        m = s.max(axis=1, keepdims=True)
+        e = np.exp(s - m)
+        ref = p["bmm2"] * (e[:, :-1] @ k[:, :512]) / e.sum(1, keepdims=True)
+        np.testing.assert_allclose(out[t * 16:(t + 1) * 16], ref, rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(lse[t * 16:(t + 1) * 16],
+                                   m[:, 0] + np.log(e.sum(1)), rtol=1e-12)
+
+
+def test_ds_mla_rows_with_unit_scales_equal_the_576_byte_rows():
+    """A 656-byte row whose scales are 1 and whose BF16 rope holds the E4M3 rope's values (exact
+    in BF16) is the same row as the 576-byte one: every mode gives the same result."""
+    p = inputs.random_problem(45, 2, 16, 200, pool_rows=400, neg_frac=0.1, lens=[200, 150],
+                              sinks=True)
+    kv = p["kv_a"]
+    ds = np.zeros((kv.shape[0], 656), np.uint8)
+    ds[:, :512] = kv[:, :512]
+    ds[:, 512:528] = np.ones((kv.shape[0], 4), np.float32).view(np.uint8)
+    rope = _e4m3_f64(kv[:, 512:576]).numpy()
+    ds[:, 528:656] = inputs.bf16_bits(rope.astype(np.float32)).view(np.uint8).reshape(-1, 128)
+    pd = dict(p, kv_a=ds)
+    for f in (lambda x: oracle.decode_exact(x),
+              lambda x: oracle.decode_mimic(x, splits=3, chunk=64, terms=2),
+              lambda x: oracle.decode_chunk_local(x)):
+        a, la = f(p)
+        b, lb = f(pd)
+        np.testing.assert_array_equal(a, b)
+        np.testing.assert_array_equal(la, lb)
+
+
+def test_ds_mla_rows_quantize_each_block_at_its_own_scale():
+    """The generator's rows: each 128-element block's largest magnitude encodes as 448 times its
+    scale, so a block scaled by 2^k gets a scale 2^k larger and the same bytes."""
+    rng = np.random.default_rng(46)
+    lat = rng.standard_normal((3, 512)).astype(np.float32)
+    lat2 = lat.copy()
+    lat2[:, 128:256] *= 8.0
+    a = inputs.ds_mla_rows(lat, np.zeros((3, 64)))
+    b = inputs.ds_mla_rows(lat2, np.zeros((3, 64)))
+    np.testing.assert_array_equal(a[:, :512], b[:, :512])
+    sa, sb = a[:, 512:528].copy().view(np.float32), b[:, 512:528].copy().view(np.float32)
+    np.testing.assert_array_equal(sb[:, 1], 8 * sa[:, 1])
+    np.testing.assert_array_equal(sb[:, [0, 2, 3]], sa[:, [0, 2, 3]])
+    k = _ds_rows_f64(a)
+    for blk in range(4):
+        assert np.abs(k[:, 128 * blk:128 * (blk + 1)]).max(axis=1) == pytest.approx(
+            np.abs(lat[:, 128 * blk:128 * (blk + 1)]).max(axis=1), rel=1e-6)
+
+
+# ---------------------------------------------------------------------------
 # lse_merge
 # ---------------------------------------------------------------------------
 
