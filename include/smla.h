@@ -140,11 +140,18 @@ size_t smla_decode_workspace_size(const smla_plan *plan, int32_t T, int32_t H);
  *
  *   q            device, E4M3 bytes; head h of token t at q + t*q_stride_t + h*q_stride_h,
  *                qk_dim bytes.  16-byte aligned; both strides multiples of 16.
- *   kv_a, rows_a device, pool A: rows_a rows of row_bytes E4M3 bytes, 16-byte aligned.
+ *   kv_a, rows_a device, pool A: rows_a rows of row_bytes bytes, 16-byte aligned.
  *   kv_b, rows_b device, pool B (may be NULL: then every column uses pool A and split_col is
  *                ignored).  Columns c >= split_col use pool B.
- *   row_bytes    576 (512 latent + 64 rope) or 512.  V is bytes [0, 512) of a row.
- *   qk_dim       576 or 512, <= row_bytes: the bytes of q and of each row in the score.
+ *   row_bytes    576 (E4M3: 512 latent + 64 rope) or 512 (E4M3 latent): V is bytes
+ *                [0, 512) of a row.  Or 656: an fp8_ds_mla row (the dsa_indexer page's 656-byte
+ *                MLA cache entry of [kv_c_normed | k_pe], viewed as FP8, FP32 and BF16), read as
+ *                the E4M3 latent at bytes [0, 512), one FP32 scale per 128 latent elements at
+ *                [512, 528) and the 64-element BF16 rope at [528, 656): K = [latent x scale |
+ *                rope], V = latent x scale.  656-byte rows need qk_dim = 576 (q's 64 rope bytes
+ *                E4M3 as before) and tiles = 2 (else SMLA_EINVAL / SMLA_EUNSUPPORTED); their
+ *                P.V product runs in BF16 (V x scale rounded to BF16, P's E4M3 terms exact).
+ *   qk_dim       576 or 512, <= row_bytes: the elements of q and of each row in the score.
  *   indices      device int32 [T, W] row-major: storage rows, negative = unused column.
  *                Every active entry must be < the row count of its pool (precondition, not
  *                checked); entries at columns >= lens[t] are never read.

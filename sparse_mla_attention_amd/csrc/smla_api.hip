@@ -22,6 +22,7 @@ constexpr int kFewChunks = 6;
 constexpr int kMaxSpreadSplits = 16;
 constexpr int kMaxLastSplits32 = 8;
 constexpr int kWindow = 128;                       // columns per range of the chunk-local recipe
+constexpr int kDsMlaRow = 656;                     // bytes of an fp8_ds_mla row
 constexpr int32_t kDefaultWaitPolls = 1 << 20;
 std::atomic<int> g_cu_count[kMaxDevices];
 // bound of the 64-head kernel's split-merge wait, and the test hook that makes it unreachable
@@ -239,7 +240,7 @@ smla_status smla_decode_plan(int32_t T, int32_t H, int32_t W, int32_t row_bytes,
 {
     if (plan == nullptr || T < 0 || H <= 0 || H % 16 != 0 || W < 1)
         return SMLA_EINVAL;
-    if (row_bytes != 512 && row_bytes != 576)
+    if (row_bytes != 512 && row_bytes != 576 && row_bytes != kDsMlaRow)
         return SMLA_EINVAL;
     if (flags & ~(SMLA_LSE_LOG2 | SMLA_P_ONE_TERM | SMLA_P_CHUNK_LOCAL))
         return SMLA_EINVAL;
@@ -285,8 +286,9 @@ smla_status smla_decode_plan(int32_t T, int32_t H, int32_t W, int32_t row_bytes,
         for (int32_t s = 2; s <= kMaxSpreadSplits; s *= 2)
             consider(s, 2, SMLA_MERGE_SPREAD, heads);
     }
-    for (int32_t s = 1; s <= kMaxLastSplits32; s *= 2)
-        consider(s, 1, SMLA_MERGE_LAST, 0);
+    if (row_bytes != kDsMlaRow)  // the 32-head kernel reads E4M3 rows only
+        for (int32_t s = 1; s <= kMaxLastSplits32; s *= 2)
+            consider(s, 1, SMLA_MERGE_LAST, 0);
     *plan = best;
     return SMLA_OK;
 }
@@ -320,10 +322,12 @@ smla_status decode_impl(const void *q, int64_t q_stride_t, int64_t q_stride_h,
         return SMLA_EINVAL;
     if (flags & ~(SMLA_LSE_LOG2 | SMLA_P_ONE_TERM | SMLA_P_CHUNK_LOCAL))
         return SMLA_EINVAL;
-    if (row_bytes != 512 && row_bytes != 576)
+    if (row_bytes != 512 && row_bytes != 576 && row_bytes != kDsMlaRow)
         return SMLA_EINVAL;
     if ((qk_dim != 512 && qk_dim != 576) || qk_dim > row_bytes)
         return SMLA_EINVAL;
+    if (row_bytes == kDsMlaRow && qk_dim != 576)
+        return SMLA_EINVAL;  // an fp8_ds_mla row's score takes its latent and its rope
     if (!isfinite(bmm1_scale) || !isfinite(bmm2_scale))
         return SMLA_EINVAL;
     if (plan != nullptr && !plan_ok(plan, H))
@@ -354,6 +358,8 @@ smla_status decode_impl(const void *q, int64_t q_stride_t, int64_t q_stride_h,
     }
     if (chosen.tiles == 2 && (W + chosen.splits - 1) / chosen.splits > smla::G64_MAX_RANGE)
         return SMLA_EUNSUPPORTED;  // the 64-head kernel stages a range's indices in LDS
+    if (row_bytes == kDsMlaRow && chosen.tiles != 2)
+        return SMLA_EUNSUPPORTED;  // fp8_ds_mla rows are read by the 64-head kernel only
     const bool chunk_local = (flags & SMLA_P_CHUNK_LOCAL) != 0;
     if (chunk_local && (chosen.tiles != 2 || chosen.splits != (W + kWindow - 1) / kWindow))
         return SMLA_EUNSUPPORTED;  // one range per 128-column window, on the 64-head kernel

@@ -59,19 +59,53 @@ constexpr int SLOTS = 3;                           // gathered chunks in LDS
 constexpr int SLICE = CHUNK * 128;                 // one 128-column slice of a slot
 constexpr int NCT = 4;                             // 32-column P.V tiles per P.V wave
 
-// Masked columns gather this row, so their bytes are zero (0 * anything stays finite).
-__device__ __attribute__((aligned(16))) uint8_t g_zero_row_g64[576];
+// Masked columns gather this row, so their bytes are zero (0 * anything stays finite); it is as
+// long as the longest row (656 bytes).
+__device__ __attribute__((aligned(16))) uint8_t g_zero_row_g64[656];
 
 // Position swizzle of the 8 pieces of a latent row within its slice.
 __device__ inline int fsw(int k) { return (((k >> 1) & 3) << 1) | ((k >> 3) & 1); }
 
-// LDS carve-up (byte offsets); TAIL: 576-byte QK (a rope region per slot).
-template <bool TAIL>
+// Rope position swizzle of the 8 BF16 rope pieces of a 656-byte row.
+__device__ inline int rsw(int k) { return (k >> 1) & 7; }
+
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+// Eight E4M3 values (bytes of w0, then w1), each times its scale, rounded to BF16 (exact when
+// the scales are powers of two).
+__device__ inline v8bf e4m3x8_bf16(int w0, int w1, v4f s0, v4f s1)
+{
+    const v2f a = __builtin_amdgcn_cvt_pk_f32_fp8(w0, false);
+    const v2f b = __builtin_amdgcn_cvt_pk_f32_fp8(w0, true);
+    const v2f c = __builtin_amdgcn_cvt_pk_f32_fp8(w1, false);
+    const v2f d = __builtin_amdgcn_cvt_pk_f32_fp8(w1, true);
+    v8bf r;
+    r[0] = (__bf16)(a[0] * s0[0]);
+    r[1] = (__bf16)(a[1] * s0[1]);
+    r[2] = (__bf16)(b[0] * s0[2]);
+    r[3] = (__bf16)(b[1] * s0[3]);
+    r[4] = (__bf16)(c[0] * s1[0]);
+    r[5] = (__bf16)(c[1] * s1[1]);
+    r[6] = (__bf16)(d[0] * s1[2]);
+    r[7] = (__bf16)(d[1] * s1[3]);
+    return r;
+}
+
+__device__ inline v8bf as_bf16x8(v4i x) { return __builtin_bit_cast(v8bf, x); }
+
+// LDS carve-up (byte offsets); TAIL: 576-byte QK on E4M3 rows (an E4M3 rope region per slot);
+// DS: 656-byte fp8_ds_mla rows (a BF16 rope region of 64 rows x 128 bytes per slot, and the
+// chunks' [4 blocks][64 keys] FP32 scale tables in a ring of four past the slots, so that the
+// refill of a slot leaves the scales of the chunk it held for the P.V products that follow).
+template <bool TAIL, bool DS>
 struct LdsG {
     static constexpr int LAT = 4 * SLICE;                      // latent region of a slot
-    static constexpr int SLOTB = LAT + (TAIL ? CHUNK * 64 : 0);
+    static constexpr int DROPE = LAT;                          // DS: [64][128 bytes] rope
+    static constexpr int SLOTB = LAT + (DS ? CHUNK * 128 : TAIL ? CHUNK * 64 : 0);
     static constexpr int V = 0;                                // [SLOTS] slots
-    static constexpr int P = SLOTS * SLOTB;                    // [2 buf][2 term][64][64 keys]
+    static constexpr int DSR = SLOTS * SLOTB;                  // DS: [4][4][64] float scales
+    static constexpr int DSRB = 4 * CHUNK * 4;                 // DS: one chunk's table
+    static constexpr int P = DSR + (DS ? 4 * DSRB : 0);        // [2 buf][2 term][64][64 keys]
     static constexpr int PTERM = HG * 64;
     static constexpr int PBUF = 2 * PTERM;
     static constexpr int SCL = P + 2 * PBUF;                   // [2 buf][64] float: alpha
@@ -84,6 +118,14 @@ struct LdsG {
     static_assert(OUT_TILE + 16 * HG * 8 <= P, "(m, l) of 16 ranges must fit past the tile");
     static_assert(TOTAL <= 160 * 1024, "LDS budget");
 };
+
+// One LDS-direct load of 4 bytes per lane: lane l's bytes from `src` go to LDS byte m0 + 4 l.
+__device__ inline void lds_dma4(uint64_t src, uint32_t m0)
+{
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+                 :
+                 : "v"(src), "s"(m0));
+}
 
 // One LDS-direct load: each lane's 16 bytes from `src` go to LDS byte m0 + 16 * lane.  Issued
 // from inline assembly so that the compiler's wait counting does not see it (it would wait for
@@ -124,11 +166,15 @@ __device__ inline uint32_t lds_addr(const uint8_t *p)
 template <int RB, int QK, bool TWO, bool DIST, bool CLA>
 __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
 {
-    constexpr bool TAIL = QK == 576;               // a fifth, 64-byte QK step (rope)
-    constexpr int NDMA = TAIL ? 9 : 8;             // loads per P.V wave and chunk
+    // DS: 656-byte fp8_ds_mla rows (E4M3 latent with an FP32 scale per 128 elements, BF16
+    // rope): the QK products of each 128-element block are scaled per key, the rope product
+    // runs in BF16, and the P.V waves dequantize their 128 columns of V to BF16
+    constexpr bool DS = RB == 656;
+    constexpr bool TAIL = QK == 576 && !DS;        // a fifth, 64-byte E4M3 QK step (rope)
+    constexpr int NDMA = DS ? 11 : TAIL ? 9 : 8;   // loads per P.V wave and chunk
     constexpr float AN = CLA ? 256.0f : ANCHOR;    // P anchor
     constexpr float LOG2_AN = CLA ? 8.0f : LOG2_ANCHOR;
-    using L = LdsG<TAIL>;
+    using L = LdsG<TAIL, DS>;
 
     __shared__ __attribute__((aligned(16))) uint8_t lds[L::TOTAL];
 
@@ -531,6 +577,7 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
         // Q fragments, B operand of QK: lane (n, g) holds head 16 w + n.
         v8i qf[4];
         v4i qt = v4i{0, 0, 0, 0};
+        v8bf qrope[DS ? 2 : 1];                    // DS: the rope of q in BF16
         {
             // a padding head computes with the group's first head's q: its scores reach no
             // output, and no instruction between here and the first product waits for these
@@ -542,6 +589,15 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
                 qf[s] = join(gload(qp + 16 * (8 * s + pg)), gload(qp + 16 * (8 * s + 4 + pg)));
             if (TAIL)
                 qt = gload(qp + 16 * (32 + pr));
+            if constexpr (DS) {
+                // rope elements 8 (4 q2 + g) .. + 7 of this lane's head, in BF16 (exact)
+                const v4f one = v4f{1.0f, 1.0f, 1.0f, 1.0f};
+#pragma unroll
+                for (int q2 = 0; q2 < 2; q2++) {
+                    const uint2 w = *reinterpret_cast<const uint2 *>(qp + 512 + 8 * (4 * q2 + g));
+                    qrope[q2] = e4m3x8_bf16((int)w.x, (int)w.y, one, one);
+                }
+            }
         }
 
         // per-lane LDS offsets (loop invariant): pieces pg and 4 + pg of slice s of row 16 kt + r
@@ -549,6 +605,12 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
         const int kb0 = r * 128 + 16 * (pg ^ fsw(r));
         const int kb1 = r * 128 + 16 * ((4 + pg) ^ fsw(r));
         const int rb = L::LAT + r * 64 + 16 * (pr ^ ((r >> 2) & 3));
+        int rbd[2] = {0, 0};                       // DS: rope pieces 4 q2 + g of row 16 kt + r
+        if constexpr (DS) {
+#pragma unroll
+            for (int q2 = 0; q2 < 2; q2++)
+                rbd[q2] = L::DROPE + r * 128 + 16 * ((4 * q2 + g) ^ rsw(r));
+        }
         int pw[4];                                 // P bytes of key tile kt in a P buffer
 #pragma unroll
         for (int kt = 0; kt < 4; kt++)
@@ -565,40 +627,76 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
             const uint8_t *slot = lds + (x % SLOTS) * L::SLOTB;
             const uint8_t *ab = reinterpret_cast<const uint8_t *>(addr) + x * CHUNK * 8;
             const uint64_t mk = __ballot(lds_load<uint64_t>(ab, lane * 8) != zero);
-            // every K fragment of the chunk is read first (in the order the products use them),
-            // and the products run step-major over the four independent key-tile chains
-            v8i av[4][4];
-            v4i rr[4];
+            if constexpr (DS) {
+                // the rope product in BF16, then each 128-element latent block's product
+                // scaled per key by the block's FP32 scale (keys 16 kt + 4 g + i of this lane)
 #pragma unroll
-            for (int s = 0; s < 4; s++)
+                for (int kt = 0; kt < 4; kt++) {
+                    sc[kt] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kt = 0; kt < 4; kt++)
-                    av[s][kt] = join(lds_load<v4i>(slot + s * SLICE + kt * 2048, kb0),
-                                     lds_load<v4i>(slot + s * SLICE + kt * 2048, kb1));
-            if constexpr (TAIL) {
+                    for (int q2 = 0; q2 < 2; q2++)
+                        sc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            as_bf16x8(lds_load<v4i>(slot + kt * 2048, rbd[q2])), qrope[q2],
+                            sc[kt], 0, 0, 0);
+                }
 #pragma unroll
-                for (int kt = 0; kt < 4; kt++)
-                    rr[kt] = lds_load<v4i>(slot + kt * 1024, rb);
-            }
+                for (int s = 0; s < 4; s++) {
+                    v8i av[4];
+                    v4f sv[4], pr4[4];
 #pragma unroll
-            for (int kt = 0; kt < 4; kt++)
-                sc[kt] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < 4; s++)
-#pragma unroll
-                for (int kt = 0; kt < 4; kt++)
-                    sc[kt] = mfma16(av[s][kt], qf[s], sc[kt]);
-            if constexpr (TAIL) {
-#pragma unroll
-                for (int q2 = 0; q2 < 2; q2++)
+                    for (int kt = 0; kt < 4; kt++) {
+                        av[kt] = join(lds_load<v4i>(slot + s * SLICE + kt * 2048, kb0),
+                                      lds_load<v4i>(slot + s * SLICE + kt * 2048, kb1));
+                        sv[kt] = lds_load<v4f>(lds + L::DSR + (x & 3) * L::DSRB + 256 * s,
+                                               4 * (16 * kt + 4 * g));
+                    }
 #pragma unroll
                     for (int kt = 0; kt < 4; kt++)
-                        sc[kt] = mfma16k32(v2i{rr[kt][2 * q2], rr[kt][2 * q2 + 1]},
-                                           v2i{qt[2 * q2], qt[2 * q2 + 1]}, sc[kt]);
+                        pr4[kt] = mfma16(av[kt], qf[s], v4f{0.f, 0.f, 0.f, 0.f});
+                    mfma_result_pad();             // these products (and the rope's) landed
+#pragma unroll
+                    for (int kt = 0; kt < 4; kt++)
+#pragma unroll
+                        for (int i = 0; i < 4; i++)
+                            sc[kt][i] = __builtin_fmaf(sv[kt][i], pr4[kt][i], sc[kt][i]);
+                }
+            } else {
+                // every K fragment of the chunk is read first (in the order the products use
+                // them), and the products run step-major over the four independent key-tile
+                // chains
+                v8i av[4][4];
+                v4i rr[4];
+#pragma unroll
+                for (int s = 0; s < 4; s++)
+#pragma unroll
+                    for (int kt = 0; kt < 4; kt++)
+                        av[s][kt] = join(lds_load<v4i>(slot + s * SLICE + kt * 2048, kb0),
+                                         lds_load<v4i>(slot + s * SLICE + kt * 2048, kb1));
+                if constexpr (TAIL) {
+#pragma unroll
+                    for (int kt = 0; kt < 4; kt++)
+                        rr[kt] = lds_load<v4i>(slot + kt * 1024, rb);
+                }
+#pragma unroll
+                for (int kt = 0; kt < 4; kt++)
+                    sc[kt] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < 4; s++)
+#pragma unroll
+                    for (int kt = 0; kt < 4; kt++)
+                        sc[kt] = mfma16(av[s][kt], qf[s], sc[kt]);
+                if constexpr (TAIL) {
+#pragma unroll
+                    for (int q2 = 0; q2 < 2; q2++)
+#pragma unroll
+                        for (int kt = 0; kt < 4; kt++)
+                            sc[kt] = mfma16k32(v2i{rr[kt][2 * q2], rr[kt][2 * q2 + 1]},
+                                               v2i{qt[2 * q2], qt[2 * q2 + 1]}, sc[kt]);
+                }
+                // the scheduler keeps this order: every K read of the chunk, then the products
+                __builtin_amdgcn_sched_group_barrier(0x100, TAIL ? 36 : 32, 0);  // LDS reads
+                __builtin_amdgcn_sched_group_barrier(0x008, TAIL ? 24 : 16, 0);  // MFMA
             }
-            // the scheduler keeps this order: every K read of the chunk, then the products
-            __builtin_amdgcn_sched_group_barrier(0x100, TAIL ? 36 : 32, 0);  // LDS reads
-            __builtin_amdgcn_sched_group_barrier(0x008, TAIL ? 24 : 16, 0);  // MFMA
             // active-column bits of this lane's keys 16 kt + 4 g + i: bit 16 (kt & 1) + i of
             // word kt >> 1
             const uint64_t bits = mk >> (4 * g);
@@ -773,11 +871,28 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
                 src[m] = lds_load<uint64_t>(ab + 64 * m, skey8) + (uint32_t)soff[m & 1];
             if constexpr (TAIL)
                 src[8] = lds_load<uint64_t>(ab, rkey * 8) + (uint32_t)roff;
+            if constexpr (DS) {
+                // scale w of key `lane` (4 bytes), and rope instructions 2 w, 2 w + 1: key
+                // 8 i + lane / 8 at position lane % 8, holding rope piece (lane % 8) ^ rsw(key)
+                src[8] = lds_load<uint64_t>(ab, lane * 8) + (uint32_t)(512 + 4 * w);
+#pragma unroll
+                for (int i2 = 0; i2 < 2; i2++) {
+                    const int key = 8 * (2 * w + i2) + (lane >> 3);
+                    src[9 + i2] = lds_load<uint64_t>(ab, key * 8) +
+                                  (uint32_t)(528 + 16 * ((lane & 7) ^ rsw(key)));
+                }
+            }
 #pragma unroll
             for (int m = 0; m < 8; m++)
                 lds_dma16(src[m], sb + w * SLICE + 1024 * m);
             if constexpr (TAIL)
                 lds_dma16(src[8], sb + L::LAT + 1024 * w);
+            if constexpr (DS) {
+                lds_dma4(src[8], lds0 + L::DSR + (x & 3) * L::DSRB + 256 * w);
+#pragma unroll
+                for (int i2 = 0; i2 < 2; i2++)
+                    lds_dma16(src[9 + i2], sb + L::DROPE + 1024 * (2 * w + i2));
+            }
         };
 
         // P.V of chunk x over this wave's 4 column tiles and both 32-head tiles, in two
@@ -787,6 +902,8 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
             v8i vt[NCT];
             v8i bh[2], bl[2];
             float alpha[2];
+            int dsr;                               // DS: LDS offset of the chunk's scale table
+            int pb;                                // DS: LDS offset of the chunk's P buffer
         };
         auto pv_read = [&](int x, Frags &f) {
             const uint8_t *vs = lds + (x % SLOTS) * L::SLOTB;
@@ -794,13 +911,18 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
 #pragma unroll
             for (int h2 = 0; h2 < 2; h2++) {
                 f.alpha[h2] = scl[(x & 1) * HG + 32 * h2 + hl];
-                f.bh[h2] = join(lds_load<v4i>(pbuf + 2048 * h2, p_rd0),
-                                lds_load<v4i>(pbuf + 2048 * h2, p_rd1));
-                f.bl[h2] = f.bh[h2];
-                if constexpr (TWO)
-                    f.bl[h2] = join(lds_load<v4i>(pbuf + L::PTERM + 2048 * h2, p_rd0),
-                                    lds_load<v4i>(pbuf + L::PTERM + 2048 * h2, p_rd1));
+                if constexpr (!DS) {
+                    f.bh[h2] = join(lds_load<v4i>(pbuf + 2048 * h2, p_rd0),
+                                    lds_load<v4i>(pbuf + 2048 * h2, p_rd1));
+                    f.bl[h2] = f.bh[h2];
+                    if constexpr (TWO)
+                        f.bl[h2] = join(lds_load<v4i>(pbuf + L::PTERM + 2048 * h2, p_rd0),
+                                        lds_load<v4i>(pbuf + L::PTERM + 2048 * h2, p_rd1));
+                }
             }
+            // DS: the P fragments are read by the products themselves (the QK waves write the
+            // other P buffer meanwhile)
+            f.pb = L::P + (x & 1) * L::PBUF;
 #pragma unroll
             for (int ct = 0; ct < NCT; ct++) {
 #pragma unroll
@@ -811,6 +933,8 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
                     f.vt[ct][2 * rho + 1] = y[1];
                 }
             }
+            if constexpr (DS)
+                f.dsr = L::DSR + (x & 3) * L::DSRB + 256 * w + 4 * 32 * u;
         };
         // the accumulators rescaled to the chunk's running maximum, then its products
         auto pv_mma = [&](const Frags &f) {
@@ -820,13 +944,54 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
 #pragma unroll
                 for (int h2 = 0; h2 < 2; h2++)
                     acc[ct][h2] *= f.alpha[h2];
+            if constexpr (DS) {
+                // BF16 products over 16 keys at a time: step k takes bytes 8 k .. 8 k + 7 of
+                // each lane's V^T and P fragments (keys 32 u + 8 k + 0..7, the same keys on
+                // both sides), V times its key's block scale, P exact (E4M3 is a subset of
+                // BF16; the second term times 2^-4, still exact)
+                const v4f one = v4f{1.0f, 1.0f, 1.0f, 1.0f};
+                const v4f sixteenth = v4f{0.0625f, 0.0625f, 0.0625f, 0.0625f};
 #pragma unroll
-            for (int ct = 0; ct < NCT; ct++) {
+                for (int k = 0; k < 4; k++) {
+                    // P bytes 8 k .. 8 k + 7 of this lane's fragment: 8 (k & 1) into the 16-byte
+                    // piece at p_rd0 (k < 2) or p_rd1
+                    const int po = (k < 2 ? p_rd0 : p_rd1) + 8 * (k & 1);
+                    v8bf ph[2], pl[2];
 #pragma unroll
-                for (int h2 = 0; h2 < 2; h2++) {
-                    acc[ct][h2] = mfma32(f.vt[ct], f.bh[h2], acc[ct][h2], 127);
-                    if constexpr (TWO)  // the second term's 2^-4
-                        acc[ct][h2] = mfma32(f.vt[ct], f.bl[h2], acc[ct][h2], 127 - 4);
+                    for (int h2 = 0; h2 < 2; h2++) {
+                        const v2i hb = lds_load<v2i>(lds + f.pb + 2048 * h2, po);
+                        ph[h2] = e4m3x8_bf16(hb[0], hb[1], one, one);
+                        if constexpr (TWO) {
+                            const v2i lb = lds_load<v2i>(lds + f.pb + L::PTERM + 2048 * h2, po);
+                            pl[h2] = e4m3x8_bf16(lb[0], lb[1], sixteenth, sixteenth);
+                        }
+                    }
+                    // block w's scales of keys 32 u + 8 k + 0..7 (the ring keeps this chunk's
+                    // table while the slot is refilled)
+                    const v4f s0 = lds_load<v4f>(lds + f.dsr, 32 * k);
+                    const v4f s1 = lds_load<v4f>(lds + f.dsr, 32 * k + 16);
+#pragma unroll
+                    for (int ct = 0; ct < NCT; ct++) {
+                        const v8bf vb = e4m3x8_bf16(f.vt[ct][2 * k], f.vt[ct][2 * k + 1], s0, s1);
+#pragma unroll
+                        for (int h2 = 0; h2 < 2; h2++) {
+                            acc[ct][h2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                                vb, ph[h2], acc[ct][h2], 0, 0, 0);
+                            if constexpr (TWO)
+                                acc[ct][h2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                                    vb, pl[h2], acc[ct][h2], 0, 0, 0);
+                        }
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int ct = 0; ct < NCT; ct++) {
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; h2++) {
+                        acc[ct][h2] = mfma32(f.vt[ct], f.bh[h2], acc[ct][h2], 127);
+                        if constexpr (TWO)  // the second term's 2^-4
+                            acc[ct][h2] = mfma32(f.vt[ct], f.bl[h2], acc[ct][h2], 127 - 4);
+                    }
                 }
             }
         };
@@ -910,6 +1075,8 @@ hipError_t launch_g64_shape(const DecodeParams &p, int row_bytes, int qk_dim, hi
         return launch_g64_one<576, 512, TWO, CLA>(p, stream);
     if (row_bytes == 512 && qk_dim == 512)
         return launch_g64_one<512, 512, TWO, CLA>(p, stream);
+    if (row_bytes == 656 && qk_dim == 576)
+        return launch_g64_one<656, 576, TWO, CLA>(p, stream);
     return hipErrorInvalidValue;
 }
 

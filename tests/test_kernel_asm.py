@@ -185,7 +185,9 @@ def test_pv_matrix_sequences_have_no_branches():
     for name, body in kernels:
         ins = [l.strip() for l in body.split("\n")
                if l.strip() and not l.strip().startswith(";")]
-        idx = [i for i, l in enumerate(ins) if l.startswith("v_mfma_scale_f32_32x32x64")]
+        # the P.V products: FP8 on E4M3 rows, BF16 on 656-byte fp8_ds_mla rows
+        idx = [i for i, l in enumerate(ins)
+               if l.startswith(("v_mfma_scale_f32_32x32x64", "v_mfma_f32_32x32x16_bf16"))]
         assert idx, name
         for a, b in zip(idx, idx[1:]):
             if b - a < 12:
