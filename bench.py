@@ -186,19 +186,28 @@ def empty_kernel_baseline(replays):
 def small_batch(smla, inputs, replays):
     """Microseconds per call of the small-batch shapes: warm (the same pools every call) and
     cold (pool copies totalling more than 512 MB rotated across calls, so the rows come from
-    HBM, not from the 256 MB MALL or the L2s), 100 calls per graph, median of the replays."""
+    HBM, not from the 256 MB MALL or the L2s), 100 calls per graph, median of the replays.
+    Besides the three workloads: DeepSeek-V4 under the chunk-local recipe (SMLA_P_CHUNK_LOCAL)
+    and the verify-row shape on 656-byte fp8_ds_mla rows."""
     import numpy as np
     import torch
     res = {}
-    for name in ("tiny", "verify", "dsv4"):
-        p = inputs.CONFIGS[name](poison=False)
+    shapes = [("tiny", lambda: inputs.CONFIGS["tiny"](poison=False), False),
+              ("verify", lambda: inputs.CONFIGS["verify"](poison=False), False),
+              ("dsv4", lambda: inputs.CONFIGS["dsv4"](poison=False), False),
+              ("dsv4_chunk_local", lambda: inputs.CONFIGS["dsv4"](poison=False), True),
+              ("verify_fp8_ds_mla", lambda: inputs.random_problem(
+                  21, 5, 128, 320, pool_rows=65536, row_bytes=656, poison=False), False)]
+    for name, make, chunk_local in shapes:
+        p = make()
         d = {k: (torch.from_numpy(np.ascontiguousarray(v)).cuda() if isinstance(v, np.ndarray)
                  else v) for k, v in p.items()}
         T, H, _ = p["q"].shape
         W = p["indices"].shape[1]
         out = torch.empty((T, H, 512), dtype=torch.bfloat16, device="cuda")
         lse = torch.empty((T, H), dtype=torch.float32, device="cuda")
-        plan = smla.plan_for(T, H, W, p["kv_a"].shape[1])
+        plan = smla.plan_for(T, H, W, p["kv_a"].shape[1],
+                             smla.SMLA_P_CHUNK_LOCAL if chunk_local else 0)
         ws = smla.new_workspace(plan, T, H)
         pool_bytes = d["kv_a"].numel() + (0 if d["kv_b"] is None else d["kv_b"].numel())
         copies = max(4, -(-COLD_POOL_BYTES // pool_bytes))
@@ -211,7 +220,7 @@ def small_batch(smla, inputs, replays):
             smla.sparse_mla_decode(d["q"], a, d["indices"], d["lens"], p["bmm1"], p["bmm2"],
                                    out, lse, kv_b=b, split_col=p["split_col"], sinks=d["sinks"],
                                    qk_dim=p["qk_dim"], lse_log2=p["lse_log2"], plan=plan,
-                                   workspace=ws, stream=s)
+                                   workspace=ws, stream=s, chunk_local=chunk_local)
         warm = graph_replays(lambda i, s: call(i, s, lambda i: pools[0]), 100, replays)
         cold = graph_replays(lambda i, s: call(i, s, lambda i: pools[i % copies]), 100, replays)
         active = int(sum(((p["indices"][t, :int(np.clip(p["lens"][t], 0, W))] >= 0).sum())
