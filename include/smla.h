@@ -107,8 +107,8 @@ typedef struct smla_plan {
 
 /* The plan sparse_mla_decode uses for these sizes when it is given none: the cheapest, by a
  * predicted time, of every plan the kernels take for them -- the 64-head kernel with 64, 32 or
- * 16 real heads per workgroup over one key range, two ranges under SMLA_MERGE_LAST, or 2, 4, 8
- * or 16 ranges under SMLA_MERGE_SPREAD (grid within the compute units, queried once per
+ * 16 real heads per workgroup over one key range, two ranges under SMLA_MERGE_LAST, or 2 to 16
+ * ranges under SMLA_MERGE_SPREAD (grid within the compute units, queried once per
  * device), and the 32-head kernel over 1, 2, 4 or 8 ranges under SMLA_MERGE_LAST.  The
  * prediction is a linear model of the call's time in its workgroup rounds, chunks per range,
  * compute-unit occupancy, heads per workgroup and split-exchange bytes, with coefficients
@@ -284,8 +284,10 @@ smla_status paged_mla_decode(const void *q, int64_t q_stride_t, int64_t q_stride
                              uint32_t flags, const smla_plan *plan, void *workspace,
                              size_t workspace_bytes, hipStream_t stream);
 
-/* The plan paged_mla_decode uses when given none: 64 heads per workgroup, key ranges as
- * smla_decode_plan over the max_pages * page_size columns (at least ceil(columns / 2048)). */
+/* The plan paged_mla_decode uses when given none: 64 heads per workgroup; enough key ranges
+ * over the max_pages * page_size columns to cover the compute units (at most 4, at least
+ * ceil(columns / 2048), one range up to 6 chunks of 64 columns); SMLA_MERGE_SPREAD when the
+ * grid, rows x head groups x ranges, fits the compute units, else SMLA_MERGE_LAST. */
 smla_status smla_paged_decode_plan(int32_t B, int32_t q_len, int32_t H, int32_t max_pages,
                                    int32_t page_size, uint32_t flags, smla_plan *plan);
 

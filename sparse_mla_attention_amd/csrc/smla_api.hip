@@ -106,7 +106,7 @@ int default_splits(int32_t T, int32_t groups, int32_t W, int cus, int tiles)
 // bytes over the call, and the grid's size against the compute units.  One coefficient set
 // per kind of plan, fitted (non-negative least squares, relative error) to graph-replayed
 // timings on MI355X of every plan on T = 1..64, H = 16, 64, 128, W = 128..2048 with rows
-// gathered from a 604 MB pool; on that grid the plans chosen by this model take 1.1% more time
+// gathered from a 604 MB pool; on that grid the plans chosen by this model take 1.0% more time
 // (summed over shapes) than the best plan measured for each shape.
 double predicted_us(const smla_plan &p, int32_t T, int32_t H, int32_t W, int cus)
 {
@@ -250,7 +250,7 @@ smla_status smla_decode_plan(int32_t T, int32_t H, int32_t W, int32_t row_bytes,
     // Every plan the kernels take for this shape, cheapest predicted time first: the 64-head
     // kernel with 64, 32 or 16 real heads per workgroup over one range, two ranges merged by
     // the last arriver, or 2 to 16 ranges under the spread merge (a grid within the compute
-    // units); the 32-head kernel over 1 to 8 ranges.  A later candidate replaces the kept one
+    // units); the 32-head kernel over 1, 2, 4 or 8 ranges.  A later candidate replaces the kept one
     // only when strictly cheaper, so ties keep the widest head groups.
     smla_plan best{1, 1, kChunk, SMLA_MERGE_LAST, 0};
     double best_us = INFINITY;
@@ -283,7 +283,7 @@ smla_status smla_decode_plan(int32_t T, int32_t H, int32_t W, int32_t row_bytes,
     for (int32_t heads : {0, 32, 16}) {
         consider(1, 2, SMLA_MERGE_LAST, heads);
         consider(2, 2, SMLA_MERGE_LAST, heads);
-        for (int32_t s = 2; s <= kMaxSpreadSplits; s *= 2)
+        for (int32_t s = 2; s <= kMaxSpreadSplits; s++)
             consider(s, 2, SMLA_MERGE_SPREAD, heads);
     }
     if (row_bytes != kDsMlaRow)  // the 32-head kernel reads E4M3 rows only
@@ -459,8 +459,13 @@ smla_status smla_paged_decode_plan(int32_t B, int32_t q_len, int32_t H, int32_t 
     if (plan->splits > kMaxSplits)
         return SMLA_EUNSUPPORTED;
     plan->chunk = kChunk;
-    plan->merge = SMLA_MERGE_LAST;
     plan->heads = 0;
+    // the spread merge when the grid fits the compute units (every workgroup resident): its
+    // merge reads are spread over all the ranges instead of one range reading the others'
+    plan->merge = SMLA_MERGE_LAST;
+    if (plan->splits >= 2 && plan->splits <= kMaxSpreadSplits &&
+        (int64_t)B * q_len * head_groups(H, 2) * plan->splits <= cus)
+        plan->merge = SMLA_MERGE_SPREAD;
     return SMLA_OK;
 }
 

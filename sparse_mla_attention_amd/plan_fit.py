@@ -3,9 +3,9 @@
     python -m sparse_mla_attention_amd.plan_fit measure OUT.jsonl   (on the GPU)
     python -m sparse_mla_attention_amd.plan_fit fit OUT.jsonl       (anywhere)
 
-`measure` times every plan the kernels take on a grid of shapes (T in 1..64, H in 16, 64, 128,
-W in 128..2048, 576-byte rows, every column active) with rows gathered from a 604 MB pool, as
-graph replays of 40 back-to-back calls on one stream (median of 5 replays), rotating over 8
+`measure` times every plan smla_decode_plan considers on a grid of shapes (T in 1..64, H in
+16, 64, 128, W in 128..2048, 576-byte rows, every column active) with rows gathered from a
+604 MB pool, as graph replays of 40 back-to-back calls on one stream (median of 5 replays), rotating over 8
 index sets so that consecutive calls gather different rows.  Each line records the shape, the
 plan, the microseconds per call, and whether the plan is the one smla_decode_plan returns.
 
@@ -51,7 +51,7 @@ def candidates(T, H, W, cus=CUS):
     out = []
     for heads in (0, 32, 16):
         gw = heads or 64
-        for s, m in ((1, 0), (2, 0), (2, 1), (4, 1), (8, 1), (16, 1)):
+        for s, m in [(1, 0), (2, 0)] + [(s, 1) for s in range(2, 17)]:
             if -(-W // s) > 2048:
                 continue
             if m == 1 and T * (-(-H // gw)) * s > cus:
