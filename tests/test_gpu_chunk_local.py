@@ -103,6 +103,17 @@ def test_chunk_local_dsv4_workload():
     _check_parity(p, out, lse, f"dsv4 {plan}")
 
 
+def test_chunk_local_many_windows_under_the_last_arriver_merge():
+    """More than 16 windows (3,000 columns: 24 ranges) take the last-arriver merge."""
+    p = inputs.random_problem(906, 2, 16, 3000, pool_rows=8000, lens=np.array([3000, 1900]),
+                              sinks=True, neg_frac=0.05)
+    d = DeviceProblem(p)
+    out, lse, plan = d.run(chunk_local=True)
+    assert plan.splits == 24 and plan.merge == LAST
+    check_empty_rows_exact(d.out, d.lse, p)
+    _check_parity(p, out, lse, f"W=3000 {plan}")
+
+
 def test_chunk_local_is_deterministic():
     p = _problem("T1_W2048")
     d = DeviceProblem(p)

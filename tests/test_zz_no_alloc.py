@@ -12,16 +12,16 @@ from smla_testlib import DeviceProblem, log
 pytestmark = pytest.mark.gpu
 
 
-def _pair(d, p, plan, one_term=False):
+def _pair(d, p, plan, one_term=False, chunk_local=False):
     """(reference bytes with a caller workspace, no-alloc bytes), both out and LSE."""
-    d.run(plan=plan, one_term=one_term)
+    d.run(plan=plan, one_term=one_term, chunk_local=chunk_local)
     ref = d.out.view(torch.int16).clone(), d.lse.view(torch.int32).clone()
     d.out.view(torch.int16).fill_(0x7FC0)
     d.lse.fill_(float("nan"))
     smla.sparse_mla_decode_noalloc(d.q, d.kv_a, d.indices, d.lens, p["bmm1"], p["bmm2"], d.out,
                                    d.lse, kv_b=d.kv_b, split_col=p["split_col"], sinks=d.sinks,
                                    qk_dim=p["qk_dim"], lse_log2=bool(p.get("lse_log2", False)),
-                                   one_term=one_term, plan=plan)
+                                   one_term=one_term, plan=plan, chunk_local=chunk_local)
     torch.cuda.synchronize()
     return ref, (d.out.view(torch.int16).clone(), d.lse.view(torch.int32).clone())
 
@@ -60,6 +60,27 @@ def test_noalloc_matches_workspace_call_twice_second_smaller():
     dv = DeviceProblem(v)
     (ro, rl), (no, nl) = _pair(dv, v, smla.plan_for(5, 128, 320, 576))
     assert torch.equal(ro, no) and torch.equal(rl, nl)
+
+
+def test_noalloc_matches_for_the_chunk_local_recipe_and_fp8_ds_mla_rows():
+    """The same entry point under the chunk-local recipe (DeepSeek-V4 workload, five windows
+    under the spread merge) and on 656-byte rows (verify-row shape), default plans, two calls
+    each."""
+    p = inputs.CONFIGS["dsv4"]()
+    d = DeviceProblem(p)
+    plan = smla.plan_for(d.T, d.H, p["indices"].shape[1], 512, smla.SMLA_P_CHUNK_LOCAL)
+    log(f"no-alloc: chunk-local {plan}")
+    for _ in range(2):
+        (ro, rl), (no, nl) = _pair(d, p, plan, chunk_local=True)
+        assert torch.equal(ro, no) and torch.equal(rl, nl)
+    p = inputs.random_problem(702, 5, 128, 320, pool_rows=3000, row_bytes=656, neg_frac=0.1,
+                              sinks=True)
+    d = DeviceProblem(p)
+    plan = smla.plan_for(5, 128, 320, 656)
+    log(f"no-alloc: 656-byte rows {plan}")
+    for one_term in (False, True):
+        (ro, rl), (no, nl) = _pair(d, p, plan, one_term)
+        assert torch.equal(ro, no) and torch.equal(rl, nl)
 
 
 def test_noalloc_rejects_a_problem_beyond_its_scratch():
