@@ -273,6 +273,35 @@ def config_throughput_device(device, index_sets: int = 8):
                 bmm2=k_scale, lse_log2=False)
 
 
+def config_throughput_ds_device(device) -> dict:
+    """The large-batch shape on 656-byte fp8_ds_mla rows: T=64, H=128, a [1048576, 656] pool
+    (~688 MB) whose latent N(0,1) is quantized per 128-element block at amax / 448 and whose
+    rope is BF16(N(0,1)), drawn on the device with a seeded torch generator; 2048 distinct
+    indices per token, lens 2048, bmm1 = 1/24, bmm2 = 1."""
+    g = torch.Generator(device=device)
+    g.manual_seed(14)
+    rows = THROUGHPUT_ROWS
+    pool = torch.empty((rows, DS_MLA_ROW_BYTES), dtype=torch.uint8, device=device)
+    step = 1 << 16
+    for r0 in range(0, rows, step):
+        x = torch.randn((step, 4, 128), generator=g, device=device, dtype=torch.float32)
+        scale = (x.abs().amax(dim=2) / E4M3_MAX).clamp_min_(1e-30)
+        lat = (x / scale[:, :, None]).clamp_(-E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn)
+        pool[r0:r0 + step, :512] = lat.view(torch.uint8).reshape(step, 512)
+        pool[r0:r0 + step, 512:528] = scale.contiguous().view(torch.uint8).reshape(step, 16)
+        rope = torch.randn((step, 64), generator=g, device=device, dtype=torch.float32)
+        pool[r0:r0 + step, 528:] = rope.to(torch.bfloat16).view(torch.uint8).reshape(step, 128)
+    q = torch.randn((64, 128, 576), generator=g, device=device, dtype=torch.float32)
+    q = q.clamp_(-E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn).view(torch.uint8).contiguous()
+    rng = np.random.default_rng(41)
+    idx = np.stack([rng.choice(rows, size=2048, replace=False) for _ in range(64)])
+    return dict(name="throughput on fp8_ds_mla rows T=64 H=128 W=2048", q=q, kv_a=pool,
+                kv_b=None, split_col=2048, qk_dim=576,
+                indices=torch.from_numpy(idx.astype(np.int32)).to(device),
+                lens=torch.full((64,), 2048, dtype=torch.int32, device=device), sinks=None,
+                bmm1=1.0 / 24.0, bmm2=1.0, lse_log2=False)
+
+
 def config_merge() -> dict:
     """8 split-KV sources [8, T=32, H=128, 512] of BF16(N(0,1)) with base-2 LSEs ~ N(5,2);
     each (source, t, h) empty (-inf) with p=0.1; (t=0, h=0..3) empty in every source; the

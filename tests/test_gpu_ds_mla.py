@@ -11,8 +11,8 @@ import oracle
 import sparse_mla_attention_amd as smla
 from sparse_mla_attention_amd import inputs
 from smla_testlib import (EXACT_MAX_ABS, EXACT_REL_L2, LSE_ABS, MIMIC_MAX_ABS, MIMIC_REL_L2,
-                          ONE_TERM_EXACT_REL_L2, DeviceProblem, check_empty_rows_exact, flip_stats,
-                          log, lse_err, mimic_max_abs_ok, rel_l2)
+                          ONE_TERM_EXACT_REL_L2, DeviceProblem, bf16_to_f64, check_empty_rows_exact,
+                          flip_stats, log, lse_err, mimic_max_abs_ok, rel_l2)
 
 pytestmark = pytest.mark.gpu
 
@@ -118,3 +118,51 @@ def test_ds_mla_checks():
         smla.sparse_mla_decode(q512, d.kv_a, d.indices, d.lens, 0.1, 1.0, d.out, d.lse,
                                qk_dim=512, plan=plan, workspace=d.workspace(plan))
     assert e.value.status == smla.SMLA_EINVAL
+
+
+def _sampled_units(T, H, count=48, seed=8):
+    rng = np.random.default_rng(seed)
+    units = {(0, 0), (T - 1, H - 1), (0, H - 1), (T - 1, 0), (31, 64), (32, 63)}
+    while len(units) < count:
+        units.add((int(rng.integers(T)), int(rng.integers(H))))
+    return sorted(units)
+
+
+def test_ds_mla_throughput_shape_sampled_parity():
+    """The large-batch shape (T=64, H=128, 2048 columns over a 1M-row pool) on 656-byte rows,
+    under its default plan (two-term P, against the exact oracle) and under the chunk-local
+    recipe (against the oracle's chunk-local mode), on sampled (token, head) units."""
+    log("generating the throughput workload on 656-byte rows on the device")
+    w = inputs.config_throughput_ds_device("cuda")
+    T, H, W = 64, 128, 2048
+    out = torch.empty((T, H, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    host = dict(q=w["q"].cpu().numpy(), kv_a=w["kv_a"].cpu().numpy(), kv_b=None, split_col=W,
+                qk_dim=576, indices=w["indices"].cpu().numpy(), lens=w["lens"].cpu().numpy(),
+                sinks=None, bmm1=w["bmm1"], bmm2=w["bmm2"])
+    units = _sampled_units(T, H)
+    ex, ex_lse = oracle.decode_exact(host, units=units)
+    for chunk_local in (False, True):
+        flags = smla.SMLA_P_CHUNK_LOCAL if chunk_local else 0
+        plan = smla.plan_for(T, H, W, 656, flags)
+        smla.sparse_mla_decode(w["q"], w["kv_a"], w["indices"], w["lens"], w["bmm1"], w["bmm2"],
+                               out, lse, chunk_local=chunk_local, plan=plan,
+                               workspace=smla.new_workspace(plan, T, H))
+        torch.cuda.synchronize()
+        assert np.all(np.isfinite(bf16_to_f64(out)))
+        got = np.stack([bf16_to_f64(out[t, h]) for t, h in units])
+        got_lse = np.array([float(lse[t, h]) for t, h in units])
+        re, me, lee = rel_l2(got, ex), float(np.abs(got - ex).max()), lse_err(got_lse, ex_lse)
+        if chunk_local:
+            ref, ref_lse = oracle.decode_chunk_local(host, units=units)
+            r, le = rel_l2(got, ref), lse_err(got_lse, ref_lse)
+            log(f"656-byte throughput shape {plan} chunk-local: vs recipe rel_l2={r:.3e} "
+                f"lse={le:.3e} ({flip_stats(got, ref, MIMIC_MAX_ABS)}); vs exact rel_l2={re:.3e} "
+                f"max_abs={me:.3e} lse={lee:.3e} over {len(units)} units")
+            assert r <= MIMIC_REL_L2 and le <= LSE_ABS
+            assert mimic_max_abs_ok(got, ref, MIMIC_MAX_ABS, EXACT_MAX_ABS)
+            assert re <= ONE_TERM_EXACT_REL_L2 and me <= EXACT_MAX_ABS and lee <= LSE_ABS
+        else:
+            log(f"656-byte throughput shape {plan}: vs exact rel_l2={re:.3e} max_abs={me:.3e} "
+                f"lse={lee:.3e} over {len(units)} units")
+            assert re <= EXACT_REL_L2 and me <= EXACT_MAX_ABS and lee <= LSE_ABS
