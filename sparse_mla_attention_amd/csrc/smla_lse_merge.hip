@@ -2,8 +2,10 @@
 // valid sources (finite base-2 LSE) are weighted by 2^(lse_s - top) / sum_r 2^(lse_r - top),
 // their BF16 rows summed in FP32 and rounded to BF16 once; no valid source gives +0 and -inf.
 //
-// Pure HBM streaming.  One wave per (token, head) unit: the unit's S LSEs and weights are the
-// same for all its lanes (scalar loads, computed once), and each lane takes 16-byte runs of 8
+// Pure HBM streaming.  One wave per (token, head) unit, eight units per workgroup.  Lane s holds
+// source s's LSE (one vector load for all sources: the only access that precedes the partials'
+// loads); the top and the sum of 2^(lse_s - top) are wave reductions (butterfly order), and
+// lane s's weight reaches the other lanes by a shuffle.  Each lane then takes 16-byte runs of 8
 // columns, issuing the loads of a block of up to 8 valid sources back to back before summing
 // them in source order; one 16-byte store per run.
 #include <hip/hip_runtime.h>
@@ -30,8 +32,24 @@ __device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0
 // NaN and +-inf both mark an empty source.
 __device__ inline bool valid_lse(float x) { return __builtin_isfinite(x); }
 
-constexpr int WAVES = 4;   // units per workgroup
+constexpr int WAVES = 8;   // units per workgroup
 constexpr int SB = 8;      // sources loaded together
+
+__device__ inline float wave_max(float x)
+{
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+        x = fmaxf(x, __shfl_xor(x, o));
+    return x;
+}
+
+__device__ inline float wave_sum(float x)
+{
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+        x += __shfl_xor(x, o);
+    return x;
+}
 
 __global__ void __launch_bounds__(64 * WAVES) lse_merge_kernel(LseMergeParams p)
 {
@@ -42,13 +60,11 @@ __global__ void __launch_bounds__(64 * WAVES) lse_merge_kernel(LseMergeParams p)
     if (unit >= TH)
         return;
     const int per_unit = p.D / 8;
-    // the unit's weights (wave-uniform): top over the valid sources, 2^(lse - top) / sum
-    float top = -INFINITY;
-    for (int s = 0; s < p.S; s++) {
-        const float l = p.lse2[s * TH + unit];
-        if (valid_lse(l))
-            top = fmaxf(top, l);
-    }
+    // the unit's weights: lane s < S holds source s's LSE; top over the valid sources, then
+    // 2^(lse_s - top) / sum (the same values on every lane after the reductions)
+    const float l = lane < p.S ? p.lse2[lane * TH + unit] : -INFINITY;
+    const bool valid = valid_lse(l);
+    const float top = wave_max(valid ? l : -INFINITY);
     if (top == -INFINITY) {  // no valid source: +0 and -inf
         for (int k = lane; k < per_unit; k += 64)
             reinterpret_cast<uint4 *>(p.out)[unit * per_unit + k] = make_uint4(0, 0, 0, 0);
@@ -56,14 +72,15 @@ __global__ void __launch_bounds__(64 * WAVES) lse_merge_kernel(LseMergeParams p)
             p.lse_out[unit] = -INFINITY;
         return;
     }
-    float sum = 0.0f;
-    for (int s = 0; s < p.S; s++) {
-        const float l = p.lse2[s * TH + unit];
-        sum += valid_lse(l) ? exp2f(l - top) : 0.0f;
-    }
-    const float inv = 1.0f / sum;
+    const float e = valid ? exp2f(l - top) : 0.0f;
+    const float sum = wave_sum(e);
+    const float w_lane = e * (1.0f / sum);
     const uint4 *src = reinterpret_cast<const uint4 *>(p.partials) + unit * per_unit;
-    for (int k = lane; k < per_unit; k += 64) {
+    // the loop is wave-uniform (every lane runs each step, `on` guards the memory accesses), so
+    // that every lane is active at the shuffles that broadcast the weights
+    for (int k0 = 0; k0 < per_unit; k0 += 64) {
+        const int k = k0 + lane;
+        const bool on = k < per_unit;
         float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
         for (int s0 = 0; s0 < p.S; s0 += SB) {
             uint4 x[SB];
@@ -71,10 +88,10 @@ __global__ void __launch_bounds__(64 * WAVES) lse_merge_kernel(LseMergeParams p)
 #pragma unroll
             for (int j = 0; j < SB; j++) {
                 const int s = s0 + j;
-                const float l = s < p.S ? p.lse2[s * TH + unit] : -INFINITY;
-                wgt[j] = valid_lse(l) ? exp2f(l - top) * inv : 0.0f;
+                wgt[j] = __shfl(w_lane, s < p.S ? s : 0);
+                wgt[j] = s < p.S ? wgt[j] : 0.0f;
                 x[j] = make_uint4(0, 0, 0, 0);
-                if (wgt[j] != 0.0f)  // wave-uniform; an empty source is never read
+                if (on && wgt[j] != 0.0f)  // an empty source is never read
                     x[j] = src[s * TH * per_unit + k];
             }
 #pragma unroll
@@ -94,7 +111,8 @@ __global__ void __launch_bounds__(64 * WAVES) lse_merge_kernel(LseMergeParams p)
         res.y = bf16_bits(acc[2]) | (bf16_bits(acc[3]) << 16);
         res.z = bf16_bits(acc[4]) | (bf16_bits(acc[5]) << 16);
         res.w = bf16_bits(acc[6]) | (bf16_bits(acc[7]) << 16);
-        reinterpret_cast<uint4 *>(p.out)[unit * per_unit + k] = res;
+        if (on)
+            reinterpret_cast<uint4 *>(p.out)[unit * per_unit + k] = res;
     }
     if (lane == 0 && p.lse_out != nullptr) {
         const float lse2 = top + log2f(sum);
