@@ -1,12 +1,13 @@
 """Measure the decode plans on this GPU and fit the planner's cost model.
 
-    python -m sparse_mla_attention_amd.plan_fit measure OUT.jsonl   (on the GPU)
+    python -m sparse_mla_attention_amd.plan_fit measure OUT.jsonl [H ...]   (on the GPU)
     python -m sparse_mla_attention_amd.plan_fit fit OUT.jsonl       (anywhere)
 
 `measure` times every plan smla_decode_plan considers on a grid of shapes (T in 1..64, H in
-16, 64, 128, W in 128..2048, 576-byte rows, every column active) with rows gathered from a
-604 MB pool, as graph replays of 40 back-to-back calls on one stream (median of 5 replays), rotating over 8
-index sets so that consecutive calls gather different rows.  Each line records the shape, the
+16, 64, 128 or the head counts given, W in 128..2048: 198 shapes for the three head counts;
+576-byte rows, every column active) with rows gathered from a 604 MB pool, as graph replays of
+40 back-to-back calls on one stream (median of 5 replays), rotating over 8 index sets so that
+consecutive calls gather different rows.  Each line appended to OUT records the shape, the
 plan, the microseconds per call, and whether the plan is the one smla_decode_plan returns.
 
 `fit` fits one linear model per kind of plan (the features are those smla_decode_plan's
@@ -89,14 +90,14 @@ def _graph_us(fn, calls=40, reps=5):
     return statistics.median(ts)
 
 
-def measure(out_path):
+def measure(out_path, heads=(128, 64, 16)):
     import torch
     import sparse_mla_attention_amd as smla
     from sparse_mla_attention_amd import inputs
     w = inputs.config_throughput_device("cuda", index_sets=8)
-    shapes = [(T, H, W) for H in (128, 64, 16) for T in (1, 2, 4, 8, 16, 32, 64)
-              for W in (128, 320, 512, 1024, 2048)]
-    with open(out_path, "w") as f:
+    shapes = [(T, H, W) for H in heads for T in (1, 2, 3, 4, 5, 6, 8, 12, 16, 32, 64)
+              for W in (128, 320, 512, 640, 1024, 2048)]
+    with open(out_path, "a") as f:
         for T, H, W in shapes:
             q = w["q"][:T, :H]
             idx = [s[:T, :W].contiguous() for s in w["index_sets"]]
@@ -156,6 +157,9 @@ def fit(path):
 
 
 if __name__ == "__main__":
-    if len(sys.argv) != 3 or sys.argv[1] not in ("measure", "fit"):
+    if len(sys.argv) < 3 or sys.argv[1] not in ("measure", "fit"):
         sys.exit(__doc__)
-    measure(sys.argv[2]) if sys.argv[1] == "measure" else fit(sys.argv[2])
+    if sys.argv[1] == "measure":
+        measure(sys.argv[2], tuple(int(h) for h in sys.argv[3:]) or (128, 64, 16))
+    else:
+        fit(sys.argv[2])
