@@ -401,6 +401,12 @@ smla_status decode_impl(const void *q, int64_t q_stride_t, int64_t q_stride_h,
     p.status = nullptr;
     p.wait_polls = g_wait_polls.load(std::memory_order_relaxed);
     p.wait_extra = g_wait_extra.load(std::memory_order_relaxed);
+    {
+        int cus = 0;
+        if (current_cu_count(&cus) != hipSuccess)
+            return SMLA_EHIP;
+        p.spec_idx = (int64_t)T * p.groups * p.splits >= cus ? 1 : 0;
+    }
     if (need > 0) {
         const WsLayout w = ws_layout(&chosen, T, H);
         uint8_t *base = static_cast<uint8_t *>(workspace);

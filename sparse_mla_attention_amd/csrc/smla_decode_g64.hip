@@ -138,6 +138,19 @@ __device__ inline void lds_dma16(uint64_t src, uint32_t m0)
                  : "v"(src), "s"(m0));
 }
 
+// The same load at device scope (sc1: misses in the non-coherent caches), for the split
+// exchange's partials written by another compute unit.
+__device__ inline void lds_dma16_dev(uint64_t src, uint32_t m0)
+{
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off sc1"
+                 :
+                 : "v"(src), "s"(m0));
+}
+
+// LDS byte offset where the two-range spread merge lands the other range's half partial
+// (64 KB, past the BF16 output tile).
+constexpr int PAIR_LZ = 64 * 1024;
+
 template <int N>
 __device__ inline void wait_dma()
 {
@@ -163,7 +176,7 @@ __device__ inline uint32_t lds_addr(const uint8_t *p)
 // running maximum); the ranges then merge as split partials.  Otherwise the attn_sparse
 // page's recipe: contiguous ranges of ceil(n / splits) columns, P at 448 of the running
 // maximum.
-template <int RB, int QK, bool TWO, bool DIST, bool CLA>
+template <int RB, int QK, bool TWO, bool DIST, bool CLA, bool PAIR, bool SPI>
 __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
 {
     // DS: 656-byte fp8_ds_mla rows (E4M3 latent with an FP32 scale per 128 elements, BF16
@@ -177,6 +190,7 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
     using L = LdsG<TAIL, DS>;
 
     __shared__ __attribute__((aligned(16))) uint8_t lds[L::TOTAL];
+    static_assert(PAIR_LZ + 64 * 1024 <= L::TOTAL, "two-range spread landing zone");
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -188,6 +202,23 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
     const int hg = unit % a.groups;
     const int split = unit / a.groups;
 
+    const int32_t *idx_row = a.indices + (int64_t)t * a.W;
+    // SPI: the indices of every column this range can hold whatever the token's count turns
+    // out to be are loaded alongside the count rather than after it: columns [0, (split + 1)
+    // ceil(W / splits)), column tid + NT k in raw_s[k], when they are at most SPEC per thread
+    // (sparse mode).  Used for grids that fill the device (it saves a dependent load there;
+    // measured slower for small grids, which take the instantiation without it).
+    constexpr int SPEC = 4;
+    const int spec_hi = SPI ? min(a.W, (split + 1) * ((a.W + a.splits - 1) / a.splits)) : 0;
+    const bool spec = SPI && !a.paged && spec_hi <= SPEC * NT;
+    int raw_s[SPEC];
+    if constexpr (SPI) {
+#pragma unroll
+        for (int k = 0; k < SPEC; k++) {
+            const int c = tid + NT * k;
+            raw_s[k] = spec && c < spec_hi ? idx_row[c] : -1;
+        }
+    }
     // the token's active count: lens[t] (sparse), or its request's context length less the
     // causal offset of its row (paged)
     const int req = a.paged ? t / a.q_len : t;
@@ -201,7 +232,6 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
     // in bounds
     const int mine = min(min(n - first, per), G64_MAX_RANGE);
     const int nch = (mine + CHUNK - 1) / CHUNK;
-    const int32_t *idx_row = a.indices + (int64_t)t * a.W;
 
 
     const uint64_t *addr = reinterpret_cast<const uint64_t *>(lds + L::ADDR);
@@ -215,6 +245,21 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
         const uint8_t *pool_a = a.kv_a, *pool_b = a.kv_b != nullptr ? a.kv_b : a.kv_a;
         const int split_col = a.kv_b != nullptr ? a.split_col : a.W;
         uint64_t *ad = reinterpret_cast<uint64_t *>(lds + L::ADDR);
+        if (spec) {
+            // [first, first + mine) lies within the loaded columns; the tail of the last
+            // chunk reads the zero row
+#pragma unroll
+            for (int k = 0; k < SPEC; k++) {
+                const int c = tid + NT * k;
+                const int i = c - first;
+                if (i >= 0 && i < mine)
+                    ad[i] = raw_s[k] < 0 ? zero
+                                         : (uint64_t)(uintptr_t)((c >= split_col ? pool_b : pool_a) +
+                                                                 (int64_t)raw_s[k] * RB);
+            }
+            for (int i = mine + tid; i < nch * CHUNK; i += NT)
+                ad[i] = zero;
+        } else
         for (int i = tid; i < nch * CHUNK; i += NT) {
             uint64_t src = zero;
             if (i < mine) {
@@ -250,9 +295,9 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
         }
         const int64_t tg = (int64_t)t * a.groups + hg;
         // A range's partial: its FP32 accumulators as they stand (at 448 of the range's running
-        // maximum m, not normalized) and (m, l) per head (g_h holds m).  Byte offset of accumulator registers 4 j .. 4 j + 3 of tile
-        // (ct, h2): 16 bytes per lane, one 1 KB run per (tile, j) across the wave, so every store
-        // and load of the exchange is one 16-byte access per lane.
+        // maximum m, not normalized) and (m, l) per head.  Byte offset of accumulator registers
+        // 4 j .. 4 j + 3 of tile (ct, h2) of P.V wave w: 16 bytes per lane, one 1 KB run per (tile,
+        // j) across the wave, so every store and load of the exchange is one 16-byte access per lane.
         auto part_off = [&](int ct, int h2, int j) {
             return ((((NCT * w + ct) * 2 + h2) * 4 + j) * 64 + lane) * 16;
         };
@@ -261,8 +306,132 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
             return __builtin_amdgcn_make_buffer_rsrc(a.ws_o + unit * (HG * 512), 0, HG * 512 * 4,
                                                      0x00020000);
         };
+        // two-range spread merge: range s writes output columns 256 s .. 256 s + 255, the column
+        // tiles of P.V waves 2 s and 2 s + 1 (`merging`); the other two P.V waves store theirs
+        const bool pair = PAIR && a.splits == 2;
+        const bool merging = !qk_wave && (w >> 1) == split;
+        // the FP32 merge of two ranges' values in range order, x0 from range 0 (the last-arriver
+        // merge's operations: both two-range merges give the same bits)
+        auto merge2 = [](float w0, float x0, float w1, float x1) {
+            float sum = 0.0f;
+            sum += w0 * x0;
+            sum += w1 * x1;
+            return sum;
+        };
         bool failed = false;
-        if (DIST && a.splits > 1) {
+        if (pair) {
+            // Each range stores only the half of its partial that the other range merges (the
+            // column tiles of the other pair of P.V waves) and its (m, l), arrives, and waits
+            // (bounded) for the other range.  The other range's half for this range's columns
+            // then comes into LDS in one round of LDS-direct loads issued by all eight waves,
+            // and the P.V waves of this half merge it with their own accumulators in registers:
+            // the last-arriver merge's FP32 operations in the same order (range 0's term first),
+            // so the two merges give the same bits.
+            const int64_t ui = tg * 2 + split, uo = tg * 2 + (1 - split);
+            const int heads_here = min(a.gw, a.H - hg * a.gw);
+            int *misc = reinterpret_cast<int *>(lds + L::MISC);
+            int *ctr = a.counters + 2 * tg;        // [0] arrivals, [1] departures
+            if (!qk_wave && !merging) {
+                // (the accumulator stores went out right after the chunk loop)
+                if (w == 2 * (1 - split) && u == 0) {
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; h2++) {
+                        if (32 * h2 + hl >= heads_here)
+                            continue;
+                        store_device(a.ws_ml + (ui * HG + 32 * h2 + hl) * 2 + 0, g_h[h2]);
+                        store_device(a.ws_ml + (ui * HG + 32 * h2 + hl) * 2 + 1, l_h[h2]);
+                    }
+                }
+                __builtin_amdgcn_s_waitcnt(0);     // this wave's stores have completed
+            }
+            __syncthreads();
+            if (tid == 0) {
+                __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const int need = 2 + a.wait_extra;
+                int ready = 0;
+                for (int spin = 0;; spin++) {
+                    if (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >=
+                        need) {
+                        ready = 1;
+                        break;
+                    }
+                    if (spin >= a.wait_polls)
+                        break;
+                    __builtin_amdgcn_s_sleep(1);
+                }
+                misc[2] = ready;
+                if (!ready)
+                    __hip_atomic_fetch_add(a.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            __syncthreads();
+            failed = misc[2] == 0;
+            // the other range's (m, l) of this lane's heads, and its half for this range's
+            // columns: positions 4096 split .. 4096 split + 4095 of its block (64 runs of 1 KB,
+            // run k = (tile * 2 + h2) * 4 + j) into LDS at PAIR_LZ + 1024 k, eight runs a wave;
+            // runs of padding heads are not loaded
+            float og[2], ol[2];
+#pragma unroll
+            for (int h2 = 0; h2 < 2; h2++) {
+                const int64_t m = (uo * HG + 32 * h2 + hl) * 2;
+                og[h2] = 32 * h2 + hl < heads_here ? load_device(a.ws_ml + m) : -INFINITY;
+                ol[h2] = 32 * h2 + hl < heads_here ? load_device(a.ws_ml + m + 1) : 0.0f;
+            }
+            {
+                const uint64_t src = (uint64_t)(uintptr_t)(a.ws_o + uo * (HG * 512)) +
+                                     (uint64_t)(4096 * split + 64 * 8 * wave + lane) * 16;
+                const uint32_t dst = lds_addr(lds) + PAIR_LZ + 8192 * wave;
+#pragma unroll
+                for (int k = 0; k < 8; k++) {
+                    const int h2k = ((8 * wave + k) >> 2) & 1;
+                    if (32 * h2k + hl < heads_here)
+                        lds_dma16_dev(src + 1024 * k, dst + 1024 * k);
+                }
+                wait_dma<0>();
+            }
+            lds_barrier();
+            float w_s[2][2];  // [range][h2]: weight 2^(m_s - M) of the range's accumulators
+#pragma unroll
+            for (int h2 = 0; h2 < 2; h2++) {
+                const float gr[2] = {split == 0 ? g_h[h2] : og[h2], split == 1 ? g_h[h2] : og[h2]};
+                const float lr[2] = {split == 0 ? l_h[h2] : ol[h2], split == 1 ? l_h[h2] : ol[h2]};
+                g_h[h2] = fmaxf(fmaxf(-INFINITY, gr[0]), gr[1]);
+                l_h[h2] = 0.0f;
+#pragma unroll
+                for (int r = 0; r < 2; r++) {
+                    w_s[r][h2] = gr[r] == -INFINITY ? 0.0f : exp2f(gr[r] - g_h[h2]);
+                    l_h[h2] += w_s[r][h2] * lr[r];
+                }
+            }
+            if (merging) {
+                // run of tile (4 w + ct), head tile h2, registers 4 j .. 4 j + 3: k = ((4 (w & 1)
+                // + ct) * 2 + h2) * 4 + j of the landing zone; `own_first`: this range is range 0
+#pragma unroll
+                for (int ct = 0; ct < NCT; ct++) {
+                    v4i x[2][4];
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; h2++)
+#pragma unroll
+                        for (int j = 0; j < 4; j++)
+                            x[h2][j] = lds_load<v4i>(
+                                lds, PAIR_LZ + (((4 * (w & 1) + ct) * 2 + h2) * 4 + j) * 1024 +
+                                         16 * lane);
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; h2++)
+#pragma unroll
+                        for (int rr = 0; rr < 16; rr++) {
+                            const float xo = __int_as_float(x[h2][rr >> 2][rr & 3]);
+                            const float xs = acc[ct][h2][rr];
+                            // range order: range 0's term first
+                            const float x0 = split == 0 ? xs : xo;
+                            const float x1 = split == 1 ? xs : xo;
+                            acc[ct][h2][rr] = merge2(w_s[0][h2], x0, w_s[1][h2], x1);
+                        }
+                    // one column tile's reads at a time (they would not fit in registers
+                    // beside the accumulators all at once)
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        } else if (DIST && !PAIR && a.splits > 1) {
             // Spread merge: every range stores its whole partial (the group's real heads only:
             // padding heads past H are never merged), then merges its own column slice of all
             // of them and writes it (smla_spread.h).
@@ -433,10 +602,7 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
                                 const float xs = acc[ct][h2][rr];
                                 const float x0 = split == 0 ? xs : xo;
                                 const float x1 = split == 1 ? xs : xo;
-                                float sum = 0.0f;
-                                sum += w_s[0][h2] * x0;
-                                sum += w_s[1][h2] * x1;
-                                acc[ct][h2][rr] = sum;
+                                acc[ct][h2][rr] = merge2(w_s[0][h2], x0, w_s[1][h2], x1);
                             }
                         }
                         if (ct + 1 < NCT) {
@@ -536,7 +702,7 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
                 big_l = wgt * l_h[h2] + AN * exp2f(sk - big_m);
             }
             const float inv = failed ? __int_as_float(0x7FC00000) : any ? a.bmm2 * wgt / big_l : 0.0f;
-            if (!qk_wave) {
+            if (!qk_wave && (!pair || merging)) {
 #pragma unroll
                 for (int ct = 0; ct < NCT; ct++) {
 #pragma unroll
@@ -549,7 +715,7 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
                     }
                 }
             }
-            if (wave == 4 && u == 0 && real && a.lse != nullptr) {
+            if (wave == 4 && u == 0 && real && a.lse != nullptr && (!pair || split == 0)) {
                 const float lse2 = failed ? __int_as_float(0x7FC00000)
                                    : any  ? big_m - LOG2_AN + log2f(big_l)
                                           : -INFINITY;
@@ -558,13 +724,24 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
         }
         lds_barrier();
         const int heads_here = min(a.gw, a.H - hg * a.gw);
-        for (int x = tid; x < heads_here * 64; x += NT) {
-            const int row = x >> 6, part = x & 63;
+        // row parts (16 bytes) written: all 64, or this range's 32 under the two-range spread
+        const int np = pair ? 32 : 64, p0 = pair ? 32 * split : 0;
+        for (int x = tid; x < heads_here * np; x += NT) {
+            const int row = x / np, part = p0 + x % np;
             const v4i v = lds_load<v4i>(tile, tile_off(row, 16 * part));
             // streaming store: the output is not read again by this kernel
             __builtin_nontemporal_store(
                 v, reinterpret_cast<v4i *>(a.out + ((int64_t)t * a.H + hg * a.gw + row) * 512 +
                                            8 * part));
+        }
+        if (pair && tid == 0 && !failed) {
+            int *ctr = a.counters + 2 * ((int64_t)t * a.groups + hg);
+            const int left = __hip_atomic_fetch_add(ctr + 1, 1, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+            if (left == 1) {  // the last to leave: both ranges have read the arrival count
+                __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(ctr + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
         }
     };
 
@@ -1047,6 +1224,29 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
             }
         }
         mfma_result_pad();                          // the last products have landed
+        // two-range spread merge: the half of the partial that the other range merges goes
+        // out now; its (m, l) follows once the epilogue's barrier has published them
+        if (PAIR && a.splits == 2 && (w >> 1) != split) {
+            const int heads_here = min(a.gw, a.H - hg * a.gw);
+            const int64_t ui = ((int64_t)t * a.groups + hg) * 2 + split;
+            const auto rs = __builtin_amdgcn_make_buffer_rsrc(a.ws_o + ui * (HG * 512), 0,
+                                                              HG * 512 * 4, 0x00020000);
+#pragma unroll
+            for (int ct = 0; ct < NCT; ct++)
+#pragma unroll
+                for (int h2 = 0; h2 < 2; h2++) {
+                    if (32 * h2 + (lane & 31) >= heads_here)
+                        continue;
+#pragma unroll
+                    for (int j = 0; j < 4; j++)
+                        __builtin_amdgcn_raw_buffer_store_b128(
+                            v4i{__float_as_int(acc[ct][h2][4 * j]),
+                                __float_as_int(acc[ct][h2][4 * j + 1]),
+                                __float_as_int(acc[ct][h2][4 * j + 2]),
+                                __float_as_int(acc[ct][h2][4 * j + 3])},
+                            rs, ((((NCT * w + ct) * 2 + h2) * 4 + j) * 64 + lane) * 16, 0, 16);
+                }
+        }
         epilogue(acc);
     }
 }
@@ -1057,12 +1257,34 @@ hipError_t launch_g64_one(const DecodeParams &p, hipStream_t stream)
     const unsigned blocks = (unsigned)p.T * (unsigned)p.groups * (unsigned)p.splits;
     // the spread merge's ranges wait for each other: its grid is at most one workgroup per
     // compute unit (checked on the host), so every workgroup is resident at once
-    if (p.merge == 1 && p.splits > 1)
-        hipLaunchKernelGGL((decode_g64_kernel<RB, QK, TWO, true, CLA>), dim3(blocks), dim3(NT), 0,
-                           stream, p);
-    else
-        hipLaunchKernelGGL((decode_g64_kernel<RB, QK, TWO, false, CLA>), dim3(blocks), dim3(NT), 0,
-                           stream, p);
+    // grids that fill the device load their index rows speculatively (SPI)
+    bool spi = false;
+    if constexpr (!CLA)
+        spi = p.spec_idx != 0 && p.paged == 0;
+    if (p.merge == 1 && p.splits == 2) {
+        if constexpr (!CLA) {
+            if (spi) {
+                hipLaunchKernelGGL((decode_g64_kernel<RB, QK, TWO, true, CLA, true, true>),
+                                   dim3(blocks), dim3(NT), 0, stream, p);
+                return hipGetLastError();
+            }
+        }
+        hipLaunchKernelGGL((decode_g64_kernel<RB, QK, TWO, true, CLA, true, false>), dim3(blocks),
+                           dim3(NT), 0, stream, p);
+    } else if (p.merge == 1 && p.splits > 1) {
+        hipLaunchKernelGGL((decode_g64_kernel<RB, QK, TWO, true, CLA, false, false>),
+                           dim3(blocks), dim3(NT), 0, stream, p);
+    } else {
+        if constexpr (!CLA) {
+            if (spi) {
+                hipLaunchKernelGGL((decode_g64_kernel<RB, QK, TWO, false, CLA, false, true>),
+                                   dim3(blocks), dim3(NT), 0, stream, p);
+                return hipGetLastError();
+            }
+        }
+        hipLaunchKernelGGL((decode_g64_kernel<RB, QK, TWO, false, CLA, false, false>),
+                           dim3(blocks), dim3(NT), 0, stream, p);
+    }
     return hipGetLastError();
 }
 

@@ -44,6 +44,10 @@ struct DecodeParams {
     const int32_t *block_table; // [requests, max_pages]
     int32_t max_pages, page_size, q_len;
     int64_t page_stride;        // bytes
+    // 1: the 64-head kernel loads the indices of every column a range can hold alongside the
+    // token's count, not after it (the host sets it when the grid fills the device: measured
+    // faster there, slower for small grids)
+    int32_t spec_idx;
 };
 
 // Longest key range (columns) the 64-head kernel takes: its range's row indices are staged in

@@ -212,7 +212,7 @@ def test_spread_merge_wait_gives_up_loudly():
     p = inputs.random_problem(715, 3, 128, 600, pool_rows=3000, neg_frac=0.1, sinks=True,
                               lens=np.array([600, 170, 560]))
     d = DeviceProblem(p)
-    for splits in (4, 16):
+    for splits in (2, 4, 16):
         plan = smla.make_plan(splits, 2, SPREAD)
         ws = smla.new_workspace(plan, d.T, d.H)
 
