@@ -47,10 +47,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--settle-ms", type=float, default=300.0,
+    ap.add_argument("--settle-ms", type=float, default=1000.0,
                     help="milliseconds of untimed decode calls run before the warm-up steps, so "
                          "that the device's clocks and translation caches reach steady state")
-    ap.add_argument("--replays", type=int, default=7,
+    ap.add_argument("--replays", type=int, default=15,
                     help="timed replays of the K-step graph; the median is reported")
     ap.add_argument("--one-term", action="store_true",
                     help="make the headline the one-term E4M3-P recipe (default: two-term)")
