@@ -160,22 +160,46 @@ def test_spread_merge_paged_equals_last_arriver():
     cache = torch.from_numpy(pp["cache"]).cuda()
     bt = torch.from_numpy(pp["block_table"]).cuda()
     lens = torch.from_numpy(pp["lengths"]).cuda()
-    res = []
-    for merge in (LAST, SPREAD):
-        plan = smla.make_plan(4, 2, merge)
-        ws = smla.new_workspace(plan, T, 128)
-        out = torch.full((T, 128, 512), float("nan"), dtype=torch.bfloat16, device="cuda")
-        lse = torch.full((T, 128), float("nan"), dtype=torch.float32, device="cuda")
-        smla.paged_mla_decode(q, cache, bt, lens, 2, pp["bmm1"], pp["bmm2"], out, lse, plan=plan,
-                              workspace=ws)
-        torch.cuda.synchronize()
-        res.append((out.view(torch.int16).cpu(), lse.view(torch.int32).cpu()))
-    assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])
     ref, _ = oracle.paged_decode_exact(pp)
-    got = res[1][0].view(torch.bfloat16).to(torch.float64).numpy().reshape(ref.shape)
-    r = rel_l2(got, ref)
-    log(f"paged spread merge rel_l2={r:.3e}")
-    assert r <= EXACT_REL_L2
+    for splits in (4, 2):  # two ranges: the two-range spread merge
+        res = []
+        for merge in (LAST, SPREAD):
+            plan = smla.make_plan(splits, 2, merge)
+            ws = smla.new_workspace(plan, T, 128)
+            out = torch.full((T, 128, 512), float("nan"), dtype=torch.bfloat16, device="cuda")
+            lse = torch.full((T, 128), float("nan"), dtype=torch.float32, device="cuda")
+            smla.paged_mla_decode(q, cache, bt, lens, 2, pp["bmm1"], pp["bmm2"], out, lse,
+                                  plan=plan, workspace=ws)
+            torch.cuda.synchronize()
+            res.append((out.view(torch.int16).cpu(), lse.view(torch.int32).cpu()))
+        assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1]), splits
+        got = res[1][0].view(torch.bfloat16).to(torch.float64).numpy().reshape(ref.shape)
+        r = rel_l2(got, ref)
+        log(f"paged spread merge, {splits} ranges: rel_l2={r:.3e}")
+        assert r <= EXACT_REL_L2
+
+
+def test_two_range_spread_on_656_byte_rows_and_chunk_local():
+    """The two-range spread merge on fp8_ds_mla rows (656 bytes) and under the chunk-local
+    recipe with two 128-column windows: bit for bit the last-arriver merge of the same plan."""
+    cases = [
+        ("656-byte rows", inputs.random_problem(720, 3, 64, 300, pool_rows=3000, row_bytes=656,
+                                                lens=np.array([300, 77, 0]), neg_frac=0.1,
+                                                sinks=True), False),
+        ("chunk-local, two windows", inputs.random_problem(721, 3, 128, 256, pool_rows=3000,
+                                                           lens=np.array([256, 140, 100]),
+                                                           neg_frac=0.1, sinks=True), True),
+    ]
+    for label, p, cl in cases:
+        d = DeviceProblem(p)
+        bits = []
+        for merge in (LAST, SPREAD):
+            plan = smla.make_plan(2, 2, merge)
+            d.run(plan=plan, chunk_local=cl)
+            bits.append(_bits(d))
+        log(f"{label}: two ranges, spread vs last arriver")
+        assert torch.equal(bits[0][0], bits[1][0]) and torch.equal(bits[0][1], bits[1][1]), label
+        check_empty_rows_exact(d.out, d.lse, p)
 
 
 def test_spread_merge_validation():
