@@ -144,7 +144,8 @@ __device__ inline void lds_dma16_dev(uint64_t src, uint32_t m0)
 {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off sc1"
                  :
-                 : "v"(src), "s"(m0));
+                 : "v"(src), "s"(m0)
+                 : "m0");
 }
 
 // LDS byte offset where the two-range spread merge lands the other range's half partial
@@ -404,7 +405,7 @@ __global__ void __launch_bounds__(NT, 1) decode_g64_kernel(DecodeParams a)
             }
             if (merging) {
                 // run of tile (4 w + ct), head tile h2, registers 4 j .. 4 j + 3: k = ((4 (w & 1)
-                // + ct) * 2 + h2) * 4 + j of the landing zone; `own_first`: this range is range 0
+                // + ct) * 2 + h2) * 4 + j of the landing zone
 #pragma unroll
                 for (int ct = 0; ct < NCT; ct++) {
                     v4i x[2][4];
