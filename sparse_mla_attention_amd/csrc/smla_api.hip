@@ -103,21 +103,23 @@ int default_splits(int32_t T, int32_t groups, int32_t W, int cus, int tiles)
 //   hr      real heads per workgroup (the rows of output and of FP32 partial it writes);
 // and, for plans with S > 1 key ranges, S itself, the partial bytes one workgroup moves (2 hr
 // rows under the spread merge, S hr rows for the last arriver), the split exchange's total
-// bytes over the call, and the grid's size against the compute units.  One coefficient set
-// per kind of plan, fitted (non-negative least squares, relative error) to graph-replayed
-// timings on MI355X of every plan on T = 1..64, H = 16, 64, 128, W = 128..2048 with rows
-// gathered from a 604 MB pool; on that grid the plans chosen by this model take 1.0% more time
-// (summed over shapes) than the best plan measured for each shape.
+// bytes over the call, and the grid's size against the compute units; for the spread merge
+// also S x occ (its S ranges wait for one another, and the wait grows with the share of the
+// device the grid holds).  One coefficient set per kind of plan, fitted (non-negative least
+// squares, relative error) to graph-replayed timings on MI355X of every plan on T = 1..64,
+// H = 16, 64, 128, W = 128..2048 with rows gathered from a 604 MB pool; on that grid the plans
+// chosen by this model take 0.8% more time (summed over shapes) than the best plan measured
+// for each shape.
 double predicted_us(const smla_plan &p, int32_t T, int32_t H, int32_t W, int cus)
 {
     // coefficients of {1, waves, cpr waves, occ cpr waves, hr/64 waves, S, hr/64 rows moved,
-    // MB exchanged, workgroups / compute units}
-    static constexpr double kCoef[5][9] = {
-        {1.201, 3.488, 1.544, 0.314, 0.864, 0.0, 0.0, 0.0, 0.0},      // 64-head, one range
-        {0.0, 4.215, 1.550, 0.138, 0.652, 2.800, 0.0, 0.036, 3.540},  // 64-head, last arriver
-        {0.0, 5.640, 1.614, 0.070, 0.0, 0.138, 1.480, 0.093, 2.243},  // 64-head, spread
-        {0.0, 6.475, 1.127, 0.176, 1.642, 0.0, 0.0, 0.0, 0.0},        // 32-head, one range
-        {1.152, 7.519, 1.198, 0.206, 0.0, 0.686, 0.276, 0.0, 2.202},  // 32-head, last arriver
+    // MB exchanged, workgroups / compute units, S/16 occ}
+    static constexpr double kCoef[5][10] = {
+        {1.297, 3.166, 1.583, 0.241, 0.880, 0.0, 0.0, 0.0, 0.0, 0.0},      // 64-head, one range
+        {0.0, 4.064, 1.581, 0.060, 0.768, 2.780, 0.0, 0.026, 3.934, 0.0},  // 64-head, last arriver
+        {0.0, 6.172, 1.621, 0.196, 0.0, 0.084, 1.709, 0.086, 0.198, 4.583},  // 64-head, spread
+        {0.0, 6.484, 1.125, 0.164, 1.502, 0.0, 0.0, 0.0, 0.0, 0.0},        // 32-head, one range
+        {1.485, 7.198, 1.207, 0.171, 0.216, 0.691, 0.291, 0.0, 2.213, 0.0},  // 32-head, last arriver
     };
     const int S = p.splits;
     const bool spread = p.merge == SMLA_MERGE_SPREAD && S > 1;
@@ -128,16 +130,19 @@ double predicted_us(const smla_plan &p, int32_t T, int32_t H, int32_t W, int cus
     const double cpr = (double)(((W + S - 1) / S + kChunk - 1) / kChunk);
     const double occ = std::min(nwg, (double)cus) / cus;
     const double hr = std::min(gw, H) / 64.0;
-    double f[9] = {1.0, waves, cpr * waves, occ * cpr * waves, hr * waves, 0.0, 0.0, 0.0, 0.0};
+    double f[10] = {1.0, waves, cpr * waves, occ * cpr * waves, hr * waves,
+                    0.0, 0.0,   0.0,        0.0,              0.0};
     if (S > 1) {
         const int moved = spread ? S : S - 1;  // partials written (and read back) per group
         f[5] = S;
         f[6] = hr * (spread ? 2 : S);
         f[7] = (double)T * H * moved * 4096.0 / 1e6;
         f[8] = nwg / cus;
+        if (spread)
+            f[9] = S / 16.0 * occ;
     }
     double us = 0.0;
-    for (int i = 0; i < 9; i++)
+    for (int i = 0; i < 10; i++)
         us += kCoef[kind][i] * f[i];
     return us;
 }

@@ -39,11 +39,13 @@ def features(T, H, W, splits, tiles, merge, heads, cus=CUS):
     cpr = -(-(-(-W // splits)) // 64)
     occ = min(nwg, cus) / cus
     hr = min(gw, H) / 64.0
-    f = [1.0, waves, cpr * waves, occ * cpr * waves, hr * waves, 0.0, 0.0, 0.0, 0.0]
+    f = [1.0, waves, cpr * waves, occ * cpr * waves, hr * waves, 0.0, 0.0, 0.0, 0.0, 0.0]
     if splits > 1:
         spread = merge == 1
         moved = splits if spread else splits - 1
-        f[5:] = [splits, hr * (2 if spread else splits), T * H * moved * 4096.0 / 1e6, nwg / cus]
+        f[5:9] = [splits, hr * (2 if spread else splits), T * H * moved * 4096.0 / 1e6, nwg / cus]
+        if spread:
+            f[9] = splits / 16.0 * occ
     return f
 
 

@@ -20,6 +20,7 @@ SHAPES = [
     (2, 64, 900, dict(neg_frac=0.1)),
     (3, 128, 700, dict(lens=[700, 0, 333])),
     (5, 128, 320, {}),
+    (3, 128, 1024, dict(neg_frac=0.05)),
     (4, 128, 128, {}),
     (2, 48, 520, dict(sinks=True, lens=[520, 77])),
     (12, 16, 640, dict(row_bytes=512, two_pools=True, split_col=128, rows_b=3000)),
