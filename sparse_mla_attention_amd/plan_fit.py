@@ -49,6 +49,30 @@ def features(T, H, W, splits, tiles, merge, heads, cus=CUS):
     return f
 
 
+# The coefficients smla_decode_plan carries (predicted_us in csrc/smla_api.hip), one row per
+# kind of plan in KINDS' order: the last fit of this module on the MI355X grid.
+LIBRARY_COEF = [
+    [1.297, 3.166, 1.583, 0.241, 0.880, 0.0, 0.0, 0.0, 0.0, 0.0],
+    [0.0, 4.064, 1.581, 0.060, 0.768, 2.780, 0.0, 0.026, 3.934, 0.0],
+    [0.0, 6.172, 1.621, 0.196, 0.0, 0.084, 1.709, 0.086, 0.198, 4.583],
+    [0.0, 6.484, 1.125, 0.164, 1.502, 0.0, 0.0, 0.0, 0.0, 0.0],
+    [1.485, 7.198, 1.207, 0.171, 0.216, 0.691, 0.291, 0.0, 2.213, 0.0],
+]
+
+
+def library_plan(T, H, W, cus=CUS):
+    """The plan smla_decode_plan returns for E4M3 rows without flags, from this module's copy of
+    its model: the first candidate, in its order, with the least predicted time."""
+    best, best_us = None, float("inf")
+    for s, t, m, h in candidates(T, H, W, cus):
+        us = 0.0
+        for c, f in zip(LIBRARY_COEF[kind(t, s, m)], features(T, H, W, s, t, m, h, cus)):
+            us += c * f
+        if us < best_us:
+            best, best_us = (s, t, m, h), us
+    return best
+
+
 def candidates(T, H, W, cus=CUS):
     """Every plan smla_decode_plan considers, in its order: (splits, tiles, merge, heads)."""
     out = []

@@ -70,3 +70,25 @@ def test_default_plans_cover_every_kind(chosen):
     log("default plans: " + ", ".join(f"{k}: {v}" for k, v in chosen.items()))
     missing = [k for k, v in kinds.items() if not v]
     assert not missing, f"no shape took {missing}"
+
+
+def test_library_plan_matches_the_fitted_model():
+    """smla_decode_plan picks, over a grid of shapes, the plan plan_fit's copy of its model
+    picks (same features, coefficients, candidate order and tie rule), for this device's
+    compute-unit count."""
+    import torch
+    from sparse_mla_attention_amd import plan_fit
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    diff = []
+    n = 0
+    for T in (1, 2, 3, 5, 7, 12, 16, 33, 64, 100):
+        for H in (16, 48, 64, 128):
+            for W in (1, 64, 100, 320, 640, 1000, 2048, 3000):
+                p = smla.plan_for(T, H, W, 576)
+                got = (p.splits, p.tiles, p.merge if p.splits > 1 else 0, p.heads)
+                want = plan_fit.library_plan(T, H, W, cus)
+                n += 1
+                if got != want:
+                    diff.append(((T, H, W), got, want))
+    log(f"{n} shapes, {len(diff)} differ")
+    assert not diff, diff[:5]
